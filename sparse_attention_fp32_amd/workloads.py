@@ -1,0 +1,234 @@
+"""Seeded synthetic inputs for the DSA decode path.
+
+This module only draws random numbers and lays them out; it computes nothing
+the method computes (no pooling, no geometry beyond buffer capacities, no
+scores).  Both the CPU oracle (through the tests) and the GPU library (through
+the tests and the bench) are fed from here, and from nowhere else.
+
+Five named workloads follow the shapes of the GLM-5.3-Flash DSA layer
+described on the Atlas ``glm5next_dsa`` page (section "Shape of the pipeline"
+and the ``Glm5NextDsaConfig`` fields): an indexer of 16 heads x 128 dims with
+kpool pooling, a 512-wide NoPE latent, 64 MLA heads.
+
+* ``tiny``       one sequence of 128 rows, 5 padding rows, kpool 4, 4 indexer
+                 heads x 32 dims, head-gate [2,256]x[256,4], 8 MLA heads.
+* ``decode32k``  16 requests x 32768 cached rows, one decode query each.
+* ``longctx``    4 ragged requests {131072, 98304, 65537, 40000} rows with
+                 0..63 padding rows each, kpool 8, sharper gate logits.
+* ``prefill4k``  one causal sequence of 4096 rows with 4096 queries.
+* ``mixed64``    64 requests with log-uniform lengths in [1024, 65536], six of
+                 them mostly padding, fp8-e4m3 latent with a per-row scale.
+
+``N(0, v)`` below always names the variance ``v``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+
+@dataclasses.dataclass
+class Spec:
+    name: str
+    lengths: List[int]            # T_r: cache rows per request, padding included
+    pads: List[int]               # leading rows with valid = 0 per request
+    kpool: int
+    index_heads: int              # H
+    index_dim: int                # D
+    hidden: int                   # K of the head-gate product
+    select_k: int
+    out_width: int
+    mla_heads: int                # Hm
+    latent: int = 512             # L
+    q_req: Optional[List[int]] = None   # query -> request (default: one per request)
+    q_pos: Optional[List[int]] = None   # query position (default: last row)
+    gate_var: float = 1.0
+    latent_fp8: bool = False
+    sm_scale: float = 1.0
+    eps: float = 1e-5
+
+    @property
+    def B(self) -> int:
+        return len(self.lengths)
+
+    @property
+    def Q(self) -> int:
+        return len(self.query_req())
+
+    def query_req(self) -> List[int]:
+        return list(self.q_req) if self.q_req is not None else list(range(self.B))
+
+    def query_pos(self) -> List[int]:
+        if self.q_pos is not None:
+            return list(self.q_pos)
+        return [self.lengths[r] - 1 for r in self.query_req()]
+
+    def total_rows(self) -> int:
+        return int(sum(self.lengths))
+
+    def pool_caps(self) -> List[int]:
+        """Pool slots reserved per request: enough for rows // kpool pools."""
+        return [t // self.kpool for t in self.lengths]
+
+    def pstride(self) -> int:
+        return max(1, max(self.pool_caps()))
+
+
+def _log_uniform_lengths(n: int, lo: int, hi: int, seed: int) -> List[int]:
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 101])))
+    u = rng.uniform(math.log(lo), math.log(hi), size=n)
+    return [int(math.floor(math.exp(x))) for x in u]
+
+
+def spec_by_name(name: str, seed: int = 0) -> Spec:
+    if name == "tiny":
+        return Spec(name, lengths=[128], pads=[5], kpool=4, index_heads=4, index_dim=32,
+                    hidden=256, select_k=4, out_width=16, mla_heads=8,
+                    q_req=[0, 0], q_pos=[127, 127])
+    if name == "decode32k":
+        return Spec(name, lengths=[32768] * 16, pads=[0] * 16, kpool=4, index_heads=16,
+                    index_dim=128, hidden=4096, select_k=512, out_width=2048, mla_heads=64)
+    if name == "longctx":
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 102])))
+        pads = [int(x) for x in rng.integers(0, 64, size=4)]
+        return Spec(name, lengths=[131072, 98304, 65537, 40000], pads=pads, kpool=8,
+                    index_heads=16, index_dim=128, hidden=4096, select_k=256,
+                    out_width=2048, mla_heads=64, gate_var=2.0)
+    if name == "prefill4k":
+        return Spec(name, lengths=[4096], pads=[0], kpool=4, index_heads=16, index_dim=128,
+                    hidden=4096, select_k=64, out_width=256, mla_heads=64,
+                    q_req=[0] * 4096, q_pos=list(range(4096)))
+    if name == "mixed64":
+        lengths = _log_uniform_lengths(64, 1024, 65536, seed)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 103])))
+        short = rng.choice(64, size=6, replace=False)
+        pads = [0] * 64
+        for r in short:
+            n_valid = int(rng.integers(1, 512))       # fewer than 512 valid rows
+            pads[int(r)] = lengths[int(r)] - n_valid
+        return Spec(name, lengths=lengths, pads=pads, kpool=4, index_heads=16,
+                    index_dim=128, hidden=4096, select_k=128, out_width=512,
+                    mla_heads=64, latent_fp8=True)
+    raise KeyError(name)
+
+
+WORKLOADS = ("tiny", "decode32k", "longctx", "prefill4k", "mixed64")
+
+
+@dataclasses.dataclass
+class Inputs:
+    """Every tensor one pass of the path reads.  bf16 tensors are carried as
+    int16 bit patterns, fp8 as uint8 codes, so that both sides see the same
+    bytes whatever the device."""
+    spec: Spec
+    hidden: torch.Tensor      # [M, hidden] f32 (M = Q)
+    W: torch.Tensor           # [hidden, H] f32
+    k: torch.Tensor           # [sumT, D] bf16 bits
+    gate: torch.Tensor        # [sumT, D] bf16 bits
+    ape: torch.Tensor         # [kpool, D] bf16 bits
+    valid: torch.Tensor       # [sumT] u8
+    tok_off: torch.Tensor     # [B+1] i32
+    pool_off: torch.Tensor    # [B+1] i32
+    ln_w: torch.Tensor        # [D] f32 (bf16-representable)
+    ln_b: torch.Tensor        # [D] f32 (bf16-representable)
+    qi: torch.Tensor          # [Q, H, D] bf16 bits
+    q_req: torch.Tensor       # [Q] i32
+    q_pos: torch.Tensor       # [Q] i32
+    new_from: torch.Tensor    # [B] i32: first row appended by this decode step
+    q_mla: torch.Tensor       # [Q, Hm, L] bf16 bits
+    ckv: torch.Tensor         # [sumT, L] bf16 bits, or uint8 fp8-e4m3 codes
+    ckv_scale: Optional[torch.Tensor]  # [sumT] f32 for fp8, else None
+    kv_off: torch.Tensor      # [B] i32
+
+    def numpy(self) -> dict:
+        out = {}
+        for f in dataclasses.fields(self):
+            v = getattr(self, f.name)
+            if isinstance(v, torch.Tensor):
+                out[f.name] = v.detach().cpu().numpy()
+            elif f.name != "spec":
+                out[f.name] = v
+        return out
+
+
+class _Streams:
+    """One independently seeded torch generator per tensor name."""
+
+    def __init__(self, seed: int, device: str):
+        self.seed = seed
+        self.device = device
+        self.n = 0
+
+    def gen(self) -> torch.Generator:
+        self.n += 1
+        g = torch.Generator(device=self.device)
+        g.manual_seed(int(np.random.SeedSequence([self.seed, self.n]).generate_state(1)[0]))
+        return g
+
+    def normal(self, shape, std: float = 1.0, mean: float = 0.0) -> torch.Tensor:
+        x = torch.randn(*shape, generator=self.gen(), device=self.device, dtype=torch.float32)
+        if std != 1.0:
+            x.mul_(std)
+        if mean != 0.0:
+            x.add_(mean)
+        return x
+
+
+def _bf16_bits(x: torch.Tensor) -> torch.Tensor:
+    return x.to(torch.bfloat16).view(torch.int16)
+
+
+def _fp8_rows(x: torch.Tensor):
+    """Store rows of x as OCP fp8-e4m3 codes with one f32 scale per row
+    (scale = row amax / 448, the format's largest finite value)."""
+    amax = x.abs().amax(dim=1).clamp_min(1e-30)
+    scale = (amax / 448.0).to(torch.float32)
+    y = (x / scale[:, None]).clamp(-448.0, 448.0)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, scale
+
+
+def make_inputs(spec: Spec, seed: int = 0, device: str = "cpu") -> Inputs:
+    s = _Streams(seed, device)
+    B, Q, T = spec.B, spec.Q, spec.total_rows()
+    H, D, L, Hm, K = spec.index_heads, spec.index_dim, spec.latent, spec.mla_heads, spec.hidden
+    i32 = dict(dtype=torch.int32, device=device)
+
+    hidden = s.normal((Q, K))
+    W = s.normal((K, H), std=1.0 / math.sqrt(K))
+    k = _bf16_bits(s.normal((T, D)))
+    gate = _bf16_bits(s.normal((T, D), std=math.sqrt(spec.gate_var)))
+    ape = _bf16_bits(s.normal((spec.kpool, D)))
+    ln_w = s.normal((D,), std=math.sqrt(0.02), mean=1.0).to(torch.bfloat16).to(torch.float32)
+    ln_b = s.normal((D,), std=math.sqrt(0.02)).to(torch.bfloat16).to(torch.float32)
+
+    offs = np.concatenate([[0], np.cumsum(spec.lengths)]).astype(np.int32)
+    caps = np.concatenate([[0], np.cumsum(spec.pool_caps())]).astype(np.int32)
+    valid = torch.ones(T, dtype=torch.uint8, device=device)
+    for r, p in enumerate(spec.pads):
+        if p:
+            valid[int(offs[r]):int(offs[r]) + p] = 0
+
+    qi = _bf16_bits(s.normal((Q, H, D)))
+    q_mla = _bf16_bits(s.normal((Q, Hm, L)))
+    lat = s.normal((T, L), std=1.0 / math.sqrt(L))
+    if spec.latent_fp8:
+        ckv, ckv_scale = _fp8_rows(lat)
+    else:
+        ckv, ckv_scale = _bf16_bits(lat), None
+    del lat
+
+    return Inputs(
+        spec=spec, hidden=hidden, W=W, k=k, gate=gate, ape=ape, valid=valid,
+        tok_off=torch.tensor(offs, **i32), pool_off=torch.tensor(caps, **i32),
+        ln_w=ln_w, ln_b=ln_b, qi=qi,
+        q_req=torch.tensor(spec.query_req(), **i32),
+        q_pos=torch.tensor(spec.query_pos(), **i32),
+        new_from=torch.tensor([t - 1 for t in spec.lengths], **i32),
+        q_mla=q_mla, ckv=ckv, ckv_scale=ckv_scale,
+        kv_off=torch.tensor(offs[:-1], **i32),
+    )
