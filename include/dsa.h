@@ -1,0 +1,230 @@
+/*
+ * dsa.h -- C ABI of libdsa, the MI355X (gfx950) DeepSeek-Sparse-Attention
+ * decode path of GLM-5.3-Flash.
+ *
+ * The calls follow the pipeline diagram of the Atlas docs page
+ * "spark_model/layers/glm5next_dsa/mod.rs", section "Shape of the pipeline":
+ *
+ *   k,gate,valid,ape -> kpool_compress -> pool keys / starts / validity
+ *                    -> index_scores   -> [Q, P] scores + candidate validity
+ *                    -> topk_pools     -> [Q, select_k] pool ids
+ *                    -> expand_selection -> [Q, out_width] token ids (-1 = none)
+ *                    -> sparse_mla_decode (NoPE MLA over those tokens)
+ *
+ * plus the fp32 indexer head-gate w = hidden @ W of stkernel pull request
+ * #227 ("indexer fp32 head-gate split-K"), whose output weights the heads of
+ * index_scores.
+ *
+ * Conventions shared by every call:
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  Arrays are
+ *    dense, row-major, with the element types named in each comment; bf16
+ *    values travel as uint16_t bit patterns, fp8 as uint8_t codes.
+ *  - The library never allocates, frees, synchronizes, or reads device memory
+ *    on the host.  Each call validates its host arguments first and, if they
+ *    are bad, returns an error before launching anything; otherwise it
+ *    enqueues its kernels on `stream` and returns DSA_OK (or DSA_ERR_LAUNCH if
+ *    the runtime refused a launch).  Calls are safe to capture in a HIP graph.
+ *  - Every per-request length lives in a device array, so a captured graph
+ *    replays correctly over changed lengths.  Host integers only bound sizes.
+ *  - A missing or unsupported path is an error, never a silent fallback onto
+ *    another computation.
+ *  - dsa_last_error() returns a thread-local message for the last failing call
+ *    of the calling thread.
+ *  - Calls on one stream are ordered; two calls that share a workspace must
+ *    not run concurrently.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+typedef int dsa_status;
+#define DSA_OK 0
+#define DSA_ERR_INVALID_ARG 1 /* an argument breaks the documented contract */
+#define DSA_ERR_UNSUPPORTED 2 /* a legal shape this build has no kernel for */
+#define DSA_ERR_LAUNCH 3      /* the HIP runtime refused a launch */
+
+/* latent cache element types for dsa_sparse_mla_decode */
+#define DSA_LATENT_BF16 0
+#define DSA_LATENT_FP8_E4M3 1 /* OCP E4M3FN codes, one f32 scale per row */
+
+/* Largest kpool: the Atlas page's validate() refuses index_kpool above the
+ * 8 pool slots its compression kernel keeps in registers. */
+#define DSA_MAX_KPOOL 8
+/* The latent width: validate() refuses a kv_lora_rank other than 512 (NoPE, so
+ * the cache row is exactly kv_lora_rank wide). */
+#define DSA_KV_LORA 512
+/* Most indexer heads one head-gate row / index_scores call supports. */
+#define DSA_MAX_INDEX_HEADS 16
+/* Longest score row dsa_topk_pools handles. */
+#define DSA_MAX_TOPK_ROW 16384
+
+int dsa_abi_version(void);
+const char* dsa_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * a1. Indexer head-gate   [stkernel PR #227]
+ *
+ *   w[m, n] = sum_k hidden[m, k] * W[k, n]        (fp32 in, fp32 accumulate)
+ *
+ * hidden [M, K] f32, W [K, N] f32, w [M, N] f32.  1 <= N <= 16, K >= 1,
+ * M >= 0 (M = 0 is a no-op).  For M <= 16 (decode) the product is split over
+ * K across many workgroups and the partial sums are added in a fixed order by
+ * the last workgroup to finish, so the result is deterministic and the same
+ * for every row of a batch.  This path needs a workspace of
+ * dsa_head_gate_workspace_size(M, K, N) bytes that is ZERO-FILLED before its
+ * first use; every call leaves it zero-filled again.  For M > 16 one
+ * workgroup per 16 rows runs the whole K loop and the workspace is unused
+ * (the size is 0; ws may be NULL).
+ * Errors: INVALID_ARG for N outside [1,16], K < 1, M < 0, a NULL pointer with
+ * M > 0, or ws_bytes below the size.
+ * ------------------------------------------------------------------------- */
+size_t dsa_head_gate_workspace_size(int M, int K, int N);
+dsa_status dsa_head_gate(const float* hidden, const float* W, float* w, int M, int K, int N,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * a2. Gated pool compression with k_norm   [Atlas page, "Traps carried from
+ *     Slice 8" and the k_norm field of Glm5NextDsaKernels]
+ *
+ * Request r owns rows tok_off[r] .. tok_off[r+1]-1 of k, gate and valid, and
+ * pool slots pool_off[r] .. pool_off[r+1]-1 of keys, pool_start, pool_valid
+ * (its capacity cap_r).  With f_r its first valid row (request-local) and
+ * P_r = floor((T_r - f_r) / kpool) its full pools (0 if no row is valid):
+ *   pool p covers rows f_r + p*kpool + s, s < kpool;
+ *   alpha[s, c] = softmax over s of (gate[row_s, c] + ape[s, c]), per channel;
+ *   x[c] = sum_s alpha[s, c] * k[row_s, c];
+ *   keys[p] = bf16_rne( (x - mean x) / sqrt(var x + eps) * ln_w + ln_b )
+ *             (biased variance; LayerNorm with bias, not an RMSNorm);
+ *   pool_start[p] = f_r + p*kpool;  pool_valid[p] = 1 iff every slot row is
+ *   valid.  Slots p in [P_r, cap_r) get start -1, valid 0, key 0.
+ *   n_pools[r] = P_r.
+ * Left padding is skipped, and a trailing partial pool is not a pool.
+ *
+ * k, gate [sumT, D] bf16; ape [kpool, D] bf16; valid [sumT] u8 (0/1);
+ * tok_off [B+1] i32; pool_off [B+1] i32 with cap_r >= floor(T_r / kpool);
+ * ln_w, ln_b [D] f32; keys [sum cap, D] bf16; pool_start [sum cap] i32;
+ * pool_valid [sum cap] u8; n_pools [B] i32.  max_cap >= every cap_r (host
+ * bound that sizes the grid).
+ *
+ * Incremental mode (a decode step that appended rows): new_from [B] i32 is the
+ * first request-local row that changed in request r, and max_new >= T_r -
+ * new_from[r] for every r.  Then only the pools holding a row at or after
+ * new_from[r] (p in [floor((new_from[r] - f_r)/kpool), P_r)) are written,
+ * with n_pools; all other slots keep their contents (the sentinels and pools
+ * of an earlier full call).  new_from = NULL recomputes every slot.
+ * Errors: INVALID_ARG for kpool outside [1, 8] (never truncated), B < 0, NULL
+ * pointers, max_cap < 0, max_new < 1 with new_from; UNSUPPORTED for D not in
+ * {32, 64, 128, 256}.
+ * ------------------------------------------------------------------------- */
+dsa_status dsa_kpool_compress(const uint16_t* k, const uint16_t* gate, const uint16_t* ape,
+                              const uint8_t* valid, const int32_t* tok_off, const int32_t* pool_off,
+                              const float* ln_w, const float* ln_b, float eps, int B, int D,
+                              int kpool, int max_cap, const int32_t* new_from, int max_new,
+                              uint16_t* keys, int32_t* pool_start, uint8_t* pool_valid,
+                              int32_t* n_pools, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * a3. Index scores   [Atlas page, "Shape of the pipeline": [Q, P] scores +
+ *     candidate validity]
+ *
+ * For query q of request r = q_req[q] and request-local pool p < pstride:
+ *   score[q, p] = sum_h w[q, h] * max(0, <qi[q, h, :], keys[pool_off[r] + p, :]>)
+ * (bf16 products, fp32 accumulation, a -0 result stored as +0) when p is a
+ * candidate: p < n_pools[r], pool_valid, and pool_start + kpool - 1 <=
+ * q_pos[q].  Otherwise score = -inf and cand = 0.  Every element of the
+ * [Q, pstride] rows is written.
+ * qi [Q, H, D] bf16; w [Q, H] f32 (the head-gate output); keys, pool_start,
+ * pool_valid, pool_off, n_pools as written by dsa_kpool_compress; q_req,
+ * q_pos [Q] i32; scores [Q, pstride] f32; cand [Q, pstride] u8.
+ * pstride >= every cap_r.
+ * Errors: INVALID_ARG for H outside [1, 16], kpool outside [1, 8], pstride < 1,
+ * Q < 0, NULL pointers; UNSUPPORTED for D not in {32, 64, 128, 256}.
+ * ------------------------------------------------------------------------- */
+dsa_status dsa_index_scores(const uint16_t* qi, const float* w, const uint16_t* keys,
+                            const int32_t* pool_start, const uint8_t* pool_valid,
+                            const int32_t* pool_off, const int32_t* n_pools, const int32_t* q_req,
+                            const int32_t* q_pos, int Q, int H, int D, int kpool, int pstride,
+                            float* scores, uint8_t* cand, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * a4. Pool top-k   [Atlas page, "Shape of the pipeline": [Q, select_k] pool
+ *     ids; Glm5NextDsaConfig::select_k caps the budget by the pools there are]
+ *
+ * Row q keeps the k_eff = min(select_k, #candidates) candidates with the
+ * largest score, ties to the lower pool id, and lists their ids in ascending
+ * order in sel[q, 0 .. k_eff-1]; sel[q, k_eff ..] = -1.  The ordering is exact
+ * (fp32 keys compared as ordered integers), so the result is a pure function
+ * of the scores.
+ * scores [Q, pstride] f32, cand [Q, pstride] u8, sel [Q, select_k] i32.
+ * No workspace is needed at present (size 0; ws may be NULL).
+ * Errors: INVALID_ARG for select_k < 1, pstride < 1, Q < 0, NULL pointers;
+ * UNSUPPORTED for pstride > DSA_MAX_TOPK_ROW.
+ * ------------------------------------------------------------------------- */
+size_t dsa_topk_pools_workspace_size(int Q, int pstride, int select_k);
+dsa_status dsa_topk_pools(const float* scores, const uint8_t* cand, int Q, int pstride,
+                          int select_k, int32_t* sel, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * a5. Selection expansion   [Atlas page, "Shape of the pipeline" and "Traps":
+ *     the -1 sentinel destination must be fully written]
+ *
+ *   tok[q, j*kpool + s] = pool_start[pool_off[q_req[q]] + sel[q, j]] + s
+ * for sel[q, j] >= 0 and s < kpool; every other element of the [Q, out_width]
+ * row is -1.  Ids are request-local row positions.
+ * sel [Q, select_k] i32; pool_start, pool_off, q_req as above; tok
+ * [Q, out_width] i32.  flags must be 0 (bit 0, always_select_tail, is not
+ * built yet).
+ * Errors: INVALID_ARG for out_width < select_k * kpool (the page's
+ * topk-multiple-of-kpool rule), kpool outside [1, 8], select_k < 1, unknown
+ * flag bits, NULL pointers; UNSUPPORTED for flag bit 0.
+ * ------------------------------------------------------------------------- */
+dsa_status dsa_expand_selection(const int32_t* sel, const int32_t* pool_start,
+                                const int32_t* pool_off, const int32_t* q_req, int Q, int select_k,
+                                int kpool, int out_width, int flags, int32_t* tok,
+                                hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * a6. NoPE sparse MLA decode   [Atlas page, "Traps" (NoPE: the latent is both
+ *     key and value, kv_cache_dim = kv_lora_rank = 512) and the
+ *     MASKED_ATTN_MAX_KEYS note (a per-row gather of the selected ids equals
+ *     the dense set-membership mask; online softmax, no full score row kept)]
+ *
+ * For query q, head h, over the ids j with tok[q, j] >= 0 and latent row
+ * c_j = ckv[kv_off[q_req[q]] + tok[q, j]] (times ckv_scale of that row for
+ * fp8):  l_j = sm_scale * <q[q, h, :], c_j>,  out[q, h] = sum_j softmax(l)_j
+ * c_j (rounded to bf16),  lse[q, h] = log sum_j exp(l_j).  A row with no
+ * selected id gives out = 0, lse = -inf.
+ * q [Q, Hm, L] bf16; ckv [rows, L] bf16 or fp8 codes; ckv_scale [rows] f32
+ * (fp8 only, else NULL); kv_off [B] i32; q_req [Q] i32; tok [Q, out_width]
+ * i32; out [Q, Hm, L] bf16; lse [Q, Hm] f32 or NULL.
+ * The selected ids of a row are split into chunks processed by separate
+ * workgroups and merged in a fixed order; the workspace
+ * dsa_sparse_mla_decode_workspace_size(Q, Hm, L, out_width, latent_dtype)
+ * holds the per-chunk partial results (its contents need no initialisation).
+ * Errors: UNSUPPORTED for L != 512 (the latent width is fixed, as the page's
+ * validate() demands); INVALID_ARG for Hm < 1, out_width < 1, Q < 0, an
+ * unknown latent_dtype, fp8 without ckv_scale, NULL pointers, or ws_bytes
+ * below the size.
+ * ------------------------------------------------------------------------- */
+size_t dsa_sparse_mla_decode_workspace_size(int Q, int Hm, int L, int out_width,
+                                            int latent_dtype);
+dsa_status dsa_sparse_mla_decode(const uint16_t* q, const void* ckv, const float* ckv_scale,
+                                 int latent_dtype, const int32_t* kv_off, const int32_t* q_req,
+                                 const int32_t* tok, int Q, int Hm, int L, int out_width,
+                                 float sm_scale, uint16_t* out, float* lse, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H_ */

@@ -147,10 +147,12 @@ def kpool_compress(k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b, eps, kpoo
     valid.  Slots [P, cap) of the request's pool range are written as
     start -1, valid 0, key 0.
 
-    new_from [B] (optional): only pools holding a row at position >= new_from[r]
-    are recomputed (and the sentinel slots after them); the rest is copied from
-    ``prev``.  ``requests`` limits the work to some requests (the others are
-    left zero), for sampled checks at full size."""
+    new_from [B] (optional, the incremental form used by a decode step that
+    appended rows): only the pools holding a row at position >= new_from[r],
+    p in [floor((new_from[r] - f)/kpool), P), are recomputed; every other slot
+    (sentinels included) is copied from ``prev``.  ``requests`` limits the
+    work to some requests (the others are left as they are), for sampled
+    checks at full size."""
     k = np.asarray(k)
     gate = np.asarray(gate)
     D = k.shape[1]
@@ -174,15 +176,14 @@ def kpool_compress(k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b, eps, kpoo
         P = int(n_pools[r])
         f = int(first[r])
         assert P <= cap, "pool capacity below the number of full pools"
-        p_from = 0
-        if new_from is not None and P > 0 and new_from[r] >= f:
-            p_from = min(cap, (int(new_from[r]) - f) // kpool)
         base = int(pool_off[r])
-        # sentinel slots
-        lo = max(P, p_from)
-        keys[base + lo:base + cap] = 0
-        start[base + lo:base + cap] = -1
-        pvalid[base + lo:base + cap] = 0
+        p_from = 0
+        if new_from is None:
+            keys[base + P:base + cap] = 0          # sentinel slots past the full pools
+            start[base + P:base + cap] = -1
+            pvalid[base + P:base + cap] = 0
+        elif P > 0 and new_from[r] >= f:
+            p_from = min(P, (int(new_from[r]) - f) // kpool)
         if P <= p_from:
             continue
         p = np.arange(p_from, P)
