@@ -1,0 +1,126 @@
+// a3: index scores  s[q,p] = sum_h w[q,h] * relu(<qi[q,h,:], key[p,:]>)  plus
+// candidate validity (Atlas glm5next_dsa page, "Shape of the pipeline").
+//
+// Per query this is a [H x D] x [D x P] contraction (16 heads x 128 dims against
+// every pooled key of the request), 16 FLOP per key byte -- on the fp32 VALU
+// ridge, so it runs on MFMA: v_mfma_f32_16x16x32_bf16 with the heads as M and
+// 16 pools as N.  The query's A operand stays in registers; each lane streams
+// its pools' key rows straight from HBM into the B-operand layout (16 bytes per
+// lane per k-step, a 64-byte run of one key row per lane group), four 16-pool
+// tiles per wave in flight.  The relu, head weighting and head sum happen on
+// the accumulator: each lane holds 4 heads of one pool; two xor shuffles finish
+// the sum in a fixed order.
+#include "dsa_device.hpp"
+#include "dsa_host.hpp"
+
+namespace {
+
+using namespace dsa;
+
+constexpr int kTiles = 4;                  // 16-pool tiles per wave
+constexpr int kPoolsPerWG = 4 * kTiles * 16;  // 4 waves
+
+template <int KS>  // D / 32 k-steps
+__global__ __launch_bounds__(256) void index_scores_kernel(
+    const uint16_t* __restrict__ qi, const float* __restrict__ w,
+    const uint16_t* __restrict__ keys, const int32_t* __restrict__ pool_start,
+    const uint8_t* __restrict__ pool_valid, const int32_t* __restrict__ pool_off,
+    const int32_t* __restrict__ n_pools, const int32_t* __restrict__ q_req,
+    const int32_t* __restrict__ q_pos, int H, int kpool, int pstride, float* __restrict__ scores,
+    uint8_t* __restrict__ cand) {
+  constexpr int D = KS * 32;
+  const int q = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int r = q_req[q];
+  const int P = n_pools[r];
+  const int64_t base = pool_off[r];
+  const int qp = q_pos[q];
+  const int tile0 = blockIdx.x * kPoolsPerWG + wave * (kTiles * 16);
+
+  // Key rows first: they are the long-latency HBM stream.
+  uint4 b[kTiles][KS];
+  int ps[kTiles], pv[kTiles];
+#pragma unroll
+  for (int tt = 0; tt < kTiles; ++tt) {
+    const int p = tile0 + tt * 16 + col;
+    const bool in = p < P;
+    const uint16_t* krow = keys + (base + (in ? p : 0)) * D + grp * 8;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      b[tt][kk] = in ? *(const uint4*)(krow + kk * 32) : make_uint4(0, 0, 0, 0);
+    ps[tt] = in ? pool_start[base + p] : 0;
+    pv[tt] = in ? (int)pool_valid[base + p] : 0;
+  }
+  // A operand: row m = head col, k = kk*32 + grp*8 + j.
+  bf16x8_t a[KS];
+  const uint16_t* qrow = qi + ((int64_t)q * H + (col < H ? col : 0)) * D + grp * 8;
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk)
+    a[kk] = as_bf16x8(col < H ? *(const uint4*)(qrow + kk * 32) : make_uint4(0, 0, 0, 0));
+  float wr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = grp * 4 + i;
+    wr[i] = h < H ? w[(int64_t)q * H + h] : 0.f;
+  }
+
+#pragma unroll
+  for (int tt = 0; tt < kTiles; ++tt) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) acc = mfma16x16x32(a[kk], as_bf16x8(b[tt][kk]), acc);
+    // acc[i] = <qi[head grp*4+i], key[pool col]>
+    float s = fmaxf(acc[0], 0.f) * wr[0];
+    s += fmaxf(acc[1], 0.f) * wr[1];
+    s += fmaxf(acc[2], 0.f) * wr[2];
+    s += fmaxf(acc[3], 0.f) * wr[3];
+    s += __shfl_xor(s, 16, kWave);
+    s += __shfl_xor(s, 32, kWave);
+    if (s == 0.f) s = 0.f;  // store -0 as +0
+    const int p = tile0 + tt * 16 + col;
+    const bool c = p < P && pv[tt] != 0 && ps[tt] + kpool - 1 <= qp;
+    if (p < pstride) {
+      if (grp == 0) scores[(int64_t)q * pstride + p] = c ? s : -INFINITY;
+      if (grp == 1) cand[(int64_t)q * pstride + p] = (uint8_t)c;
+    }
+  }
+}
+
+}  // namespace
+
+DSA_EXPORT dsa_status dsa_index_scores(const uint16_t* qi, const float* w, const uint16_t* keys,
+                                       const int32_t* pool_start, const uint8_t* pool_valid,
+                                       const int32_t* pool_off, const int32_t* n_pools,
+                                       const int32_t* q_req, const int32_t* q_pos, int Q, int H,
+                                       int D, int kpool, int pstride, float* scores,
+                                       uint8_t* cand, hipStream_t stream) {
+  DSA_REQUIRE(H >= 1 && H <= DSA_MAX_INDEX_HEADS, DSA_ERR_INVALID_ARG,
+              "dsa_index_scores: H=%d outside [1,%d]", H, DSA_MAX_INDEX_HEADS);
+  DSA_REQUIRE(kpool >= 1 && kpool <= DSA_MAX_KPOOL, DSA_ERR_INVALID_ARG,
+              "dsa_index_scores: kpool=%d outside [1,%d]", kpool, DSA_MAX_KPOOL);
+  DSA_REQUIRE(D == 32 || D == 64 || D == 128 || D == 256, DSA_ERR_UNSUPPORTED,
+              "dsa_index_scores: D=%d not in {32,64,128,256}", D);
+  DSA_REQUIRE(pstride >= 1, DSA_ERR_INVALID_ARG, "dsa_index_scores: pstride=%d < 1", pstride);
+  DSA_REQUIRE(Q >= 0, DSA_ERR_INVALID_ARG, "dsa_index_scores: Q=%d < 0", Q);
+  if (Q == 0) return DSA_OK;
+  DSA_REQUIRE(qi && w && keys && pool_start && pool_valid && pool_off && n_pools && q_req &&
+                  q_pos && scores && cand,
+              DSA_ERR_INVALID_ARG, "dsa_index_scores: NULL tensor pointer");
+  dim3 grid((pstride + kPoolsPerWG - 1) / kPoolsPerWG, Q);
+  if (dsa::trace_enabled())
+    fprintf(stderr, "[dsa] index_scores Q=%d H=%d D=%d pstride=%d grid=(%d,%d)\n", Q, H, D,
+            pstride, grid.x, grid.y);
+#define DSA_LAUNCH_IS(KS)                                                               \
+  index_scores_kernel<KS><<<grid, 256, 0, stream>>>(qi, w, keys, pool_start, pool_valid, \
+                                                    pool_off, n_pools, q_req, q_pos, H,  \
+                                                    kpool, pstride, scores, cand)
+  switch (D / 32) {
+    case 1: DSA_LAUNCH_IS(1); break;
+    case 2: DSA_LAUNCH_IS(2); break;
+    case 4: DSA_LAUNCH_IS(4); break;
+    default: DSA_LAUNCH_IS(8); break;
+  }
+#undef DSA_LAUNCH_IS
+  return dsa::check_launch("dsa_index_scores");
+}

@@ -1,0 +1,234 @@
+// a2: gated pool compression + k_norm (bias-bearing LayerNorm), fused.
+//
+// Atlas glm5next_dsa page, "Traps carried from Slice 8": the pool softmax runs
+// over the pool-slot axis separately per channel; pooling starts at the first
+// valid row; a pool counts only if all kpool slots are valid (a trailing
+// partial pool is no pool); k_norm is an nn.LayerNorm with a bias.  The page
+// runs compression and an in-place bf16 LayerNorm as two kernels; here the
+// LayerNorm is applied to the fp32 pooled row in registers and the key is
+// rounded to bf16 once.
+//
+// Layout: one pool is handled by D/8 lanes, each owning 8 channels (one 16-byte
+// load per slot row), so a wave streams 64/(D/8) pools at once with fully
+// coalesced row reads.  Per-channel slot softmax is lane-local; the LayerNorm
+// mean and variance are xor-shuffle reductions over the pool's lanes.
+// HBM-bound (2*kpool*D*2 bytes in, D*2 out per pool): no MFMA.
+#include <limits.h>
+
+#include "dsa_device.hpp"
+#include "dsa_host.hpp"
+
+namespace {
+
+using namespace dsa;
+
+// First valid row of a request (request-local), or -1: the whole workgroup
+// scans 4 KiB windows and stops at the first window holding a valid byte.
+__device__ int first_valid_row(const uint8_t* __restrict__ valid, int64_t row0, int T,
+                               int* s_first) {
+  const int t = threadIdx.x;
+  if (t == 0) *s_first = INT_MAX;
+  __syncthreads();
+  for (int base = 0; base < T; base += 256 * 16) {
+    const int lo = base + t * 16;
+    int found = INT_MAX;
+    if (lo < T) {
+      const uint8_t* p = valid + row0 + lo;
+      const int n = min(16, T - lo);
+      for (int i = 0; i < n; ++i)
+        if (p[i]) {
+          found = lo + i;
+          break;
+        }
+    }
+    if (found != INT_MAX) atomicMin(s_first, found);
+    __syncthreads();
+    const int cur = *s_first;
+    __syncthreads();
+    if (cur != INT_MAX) break;
+  }
+  const int f = *s_first;
+  return f == INT_MAX ? -1 : f;
+}
+
+template <int LPP>  // lanes per pool = D / 8
+__global__ __launch_bounds__(256) void kpool_compress_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ gate,
+    const uint16_t* __restrict__ ape, const uint8_t* __restrict__ valid,
+    const int32_t* __restrict__ tok_off, const int32_t* __restrict__ pool_off,
+    const float* __restrict__ ln_w, const float* __restrict__ ln_b, float eps, int kpool,
+    const int32_t* __restrict__ new_from, int pools_per_wg, uint16_t* __restrict__ keys,
+    int32_t* __restrict__ pool_start, uint8_t* __restrict__ pool_valid,
+    int32_t* __restrict__ n_pools) {
+  constexpr int D = LPP * 8;
+  constexpr int kGroups = 256 / LPP;  // pools in flight per workgroup
+  __shared__ int s_first;
+  const int r = blockIdx.y;
+  const int t = threadIdx.x;
+  const int64_t row0 = tok_off[r];
+  const int T = tok_off[r + 1] - (int)row0;
+  const int64_t pbase = pool_off[r];
+  const int cap = pool_off[r + 1] - (int)pbase;
+
+  const int f = first_valid_row(valid, row0, T, &s_first);
+  int P = f < 0 ? 0 : (T - f) / kpool;
+  if (P > cap) P = cap;
+  if (blockIdx.x == 0 && t == 0) n_pools[r] = P;
+
+  int lo, hi;  // slots this launch rewrites
+  if (new_from) {
+    const int nf = new_from[r];
+    lo = (f >= 0 && nf >= f) ? min(P, (nf - f) / kpool) : 0;
+    hi = P;
+  } else {
+    lo = 0;
+    hi = cap;
+  }
+  const int s0 = lo + blockIdx.x * pools_per_wg;
+  const int s1 = min(hi, s0 + pools_per_wg);
+  if (s0 >= s1) return;
+
+  const int li = t % LPP;     // lane within the pool's lane group
+  const int grp = t / LPP;    // pool group within the workgroup
+  const int c0 = li * 8;      // first channel of this lane
+
+  float lw[8], lb[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    lw[c] = ln_w[c0 + c];
+    lb[c] = ln_b[c0 + c];
+  }
+  uint4 ap[DSA_MAX_KPOOL];
+#pragma unroll
+  for (int s = 0; s < DSA_MAX_KPOOL; ++s)
+    ap[s] = s < kpool ? *(const uint4*)(ape + s * D + c0) : make_uint4(0, 0, 0, 0);
+
+  for (int p = s0 + grp; p < s1; p += kGroups) {
+    uint16_t* kout = keys + (pbase + p) * D + c0;
+    if (p >= P) {  // sentinel slot past the full pools
+      *(uint4*)kout = make_uint4(0, 0, 0, 0);
+      if (li == 0) {
+        pool_start[pbase + p] = -1;
+        pool_valid[pbase + p] = 0;
+      }
+      continue;
+    }
+    const int64_t rb = row0 + f + (int64_t)p * kpool;
+    uint4 kr[DSA_MAX_KPOOL], gr[DSA_MAX_KPOOL];
+    int allv = 1;
+#pragma unroll
+    for (int s = 0; s < DSA_MAX_KPOOL; ++s) {
+      if (s < kpool) {
+        kr[s] = *(const uint4*)(k + (rb + s) * D + c0);
+        gr[s] = *(const uint4*)(gate + (rb + s) * D + c0);
+        allv &= valid[rb + s] != 0;
+      }
+    }
+    float x[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int word = c >> 1, sh = (c & 1) * 16;
+      float g[DSA_MAX_KPOOL];
+      float m = -INFINITY;
+#pragma unroll
+      for (int s = 0; s < DSA_MAX_KPOOL; ++s) {
+        if (s < kpool) {
+          const uint32_t gw = u4_word(gr[s], word), aw = u4_word(ap[s], word);
+          g[s] = bf16_to_f32((gw >> sh) & 0xffffu) + bf16_to_f32((aw >> sh) & 0xffffu);
+          m = fmaxf(m, g[s]);
+        }
+      }
+      float z = 0.f, acc = 0.f;
+#pragma unroll
+      for (int s = 0; s < DSA_MAX_KPOOL; ++s) {
+        if (s < kpool) {
+          const float e = expf(g[s] - m);
+          z += e;
+          const uint32_t kw = u4_word(kr[s], word);
+          acc = fmaf(e, bf16_to_f32((kw >> sh) & 0xffffu), acc);
+        }
+      }
+      x[c] = acc / z;
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) sum += x[c];
+    sum = wave_sum_xor(sum, LPP - 1);
+    const float mean = sum / (float)D;
+    float sq = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float d = x[c] - mean;
+      sq = fmaf(d, d, sq);
+    }
+    sq = wave_sum_xor(sq, LPP - 1);
+    const float rstd = 1.0f / sqrtf(sq / (float)D + eps);
+    uint32_t packed[4];
+#pragma unroll
+    for (int c = 0; c < 8; c += 2) {
+      const float y0 = (x[c] - mean) * rstd * lw[c] + lb[c];
+      const float y1 = (x[c + 1] - mean) * rstd * lw[c + 1] + lb[c + 1];
+      packed[c >> 1] = f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16);
+    }
+    *(uint4*)kout = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    if (li == 0) {
+      pool_start[pbase + p] = f + p * kpool;
+      pool_valid[pbase + p] = (uint8_t)allv;
+    }
+  }
+}
+
+}  // namespace
+
+DSA_EXPORT dsa_status dsa_kpool_compress(const uint16_t* k, const uint16_t* gate,
+                                         const uint16_t* ape, const uint8_t* valid,
+                                         const int32_t* tok_off, const int32_t* pool_off,
+                                         const float* ln_w, const float* ln_b, float eps, int B,
+                                         int D, int kpool, int max_cap, const int32_t* new_from,
+                                         int max_new, uint16_t* keys, int32_t* pool_start,
+                                         uint8_t* pool_valid, int32_t* n_pools,
+                                         hipStream_t stream) {
+  DSA_REQUIRE(kpool >= 1 && kpool <= DSA_MAX_KPOOL, DSA_ERR_INVALID_ARG,
+              "dsa_kpool_compress: kpool=%d outside [1,%d] (larger pools are refused, never "
+              "truncated)",
+              kpool, DSA_MAX_KPOOL);
+  DSA_REQUIRE(D == 32 || D == 64 || D == 128 || D == 256, DSA_ERR_UNSUPPORTED,
+              "dsa_kpool_compress: D=%d not in {32,64,128,256}", D);
+  DSA_REQUIRE(B >= 0, DSA_ERR_INVALID_ARG, "dsa_kpool_compress: B=%d < 0", B);
+  DSA_REQUIRE(max_cap >= 0, DSA_ERR_INVALID_ARG, "dsa_kpool_compress: max_cap=%d < 0", max_cap);
+  DSA_REQUIRE(!new_from || max_new >= 1, DSA_ERR_INVALID_ARG,
+              "dsa_kpool_compress: max_new=%d < 1 with new_from", max_new);
+  DSA_REQUIRE(eps >= 0.f, DSA_ERR_INVALID_ARG, "dsa_kpool_compress: eps < 0");
+  if (B == 0) return DSA_OK;
+  DSA_REQUIRE(k && gate && ape && valid && tok_off && pool_off && ln_w && ln_b && keys &&
+                  pool_start && pool_valid && n_pools,
+              DSA_ERR_INVALID_ARG, "dsa_kpool_compress: NULL tensor pointer");
+  const int lpp = D / 8;
+  const int groups = 256 / lpp;
+  int ppw, nx;
+  if (new_from) {
+    const int touch = (max_new + kpool - 1) / kpool;  // pools one request can touch
+    ppw = groups;
+    nx = (touch + ppw - 1) / ppw;
+  } else {
+    ppw = groups * 4;
+    nx = (max_cap + ppw - 1) / ppw;
+  }
+  if (nx < 1) nx = 1;  // n_pools is written even with no slots
+  dim3 grid(nx, B);
+  if (dsa::trace_enabled())
+    fprintf(stderr, "[dsa] kpool_compress B=%d D=%d kpool=%d max_cap=%d inc=%d grid=(%d,%d)\n",
+            B, D, kpool, max_cap, new_from != nullptr, grid.x, grid.y);
+#define DSA_LAUNCH_KP(LPP)                                                                     \
+  kpool_compress_kernel<LPP><<<grid, 256, 0, stream>>>(k, gate, ape, valid, tok_off, pool_off, \
+                                                       ln_w, ln_b, eps, kpool, new_from, ppw,  \
+                                                       keys, pool_start, pool_valid, n_pools)
+  switch (lpp) {
+    case 4: DSA_LAUNCH_KP(4); break;
+    case 8: DSA_LAUNCH_KP(8); break;
+    case 16: DSA_LAUNCH_KP(16); break;
+    default: DSA_LAUNCH_KP(32); break;
+  }
+#undef DSA_LAUNCH_KP
+  return dsa::check_launch("dsa_kpool_compress");
+}

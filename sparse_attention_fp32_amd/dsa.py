@@ -1,0 +1,204 @@
+"""Thin ctypes binding over libdsa.so (see include/dsa.h).
+
+Every function here only marshals arguments: it checks that tensors live on
+the GPU with the dtype and contiguity the C ABI expects, turns them into device
+pointers, and passes torch's current HIP stream.  All arithmetic runs in the
+library's HIP kernels.  There is no CPU fallback: if libdsa.so is missing the
+import of a call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "dsa.h")
+
+DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_LAUNCH = 0, 1, 2, 3
+LATENT_BF16, LATENT_FP8_E4M3 = 0, 1
+MAX_KPOOL, KV_LORA, MAX_INDEX_HEADS, MAX_TOPK_ROW = 8, 512, 16, 16384
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_Z = ctypes.c_size_t
+
+_SIGS = {
+    "dsa_abi_version": (_I, []),
+    "dsa_last_error": (ctypes.c_char_p, []),
+    "dsa_head_gate_workspace_size": (_Z, [_I, _I, _I]),
+    "dsa_head_gate": (_I, [_P, _P, _P, _I, _I, _I, _P, _Z, _P]),
+    "dsa_kpool_compress": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _F, _I, _I, _I, _I, _P, _I,
+                                _P, _P, _P, _P, _P]),
+    "dsa_index_scores": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "dsa_topk_pools_workspace_size": (_Z, [_I, _I, _I]),
+    "dsa_topk_pools": (_I, [_P, _P, _I, _I, _I, _P, _P, _Z, _P]),
+    "dsa_expand_selection": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
+    "dsa_sparse_mla_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
+    "dsa_sparse_mla_decode": (_I, [_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P,
+                                   _Z, _P]),
+}
+
+
+class DsaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libdsa error {code}: {msg}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdsa.so (built in-tree by sparse_attention_fp32_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m sparse_attention_fp32_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/dsa.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def last_error() -> str:
+    return lib().dsa_last_error().decode()
+
+
+def abi_version() -> int:
+    return lib().dsa_abi_version()
+
+
+def _check(code: int):
+    if code != DSA_OK:
+        raise DsaError(code, last_error())
+
+
+def _stream(stream) -> _P:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return _P(s.cuda_stream)
+
+
+def _dev(t: Optional[torch.Tensor], dtype, name: str, allow_none: bool = False) -> _P:
+    if t is None:
+        if allow_none:
+            return _P(None)
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return _P(t.data_ptr())
+
+
+_BF = (torch.int16, torch.uint16, torch.bfloat16)   # bf16 bits in any 16-bit container
+_I32 = torch.int32
+_U8 = (torch.uint8, torch.bool)
+
+
+# --- workspace sizes -------------------------------------------------------
+
+def head_gate_workspace_size(M: int, K: int, N: int) -> int:
+    return lib().dsa_head_gate_workspace_size(M, K, N)
+
+
+def topk_pools_workspace_size(Q: int, pstride: int, select_k: int) -> int:
+    return lib().dsa_topk_pools_workspace_size(Q, pstride, select_k)
+
+
+def sparse_mla_decode_workspace_size(Q: int, Hm: int, L: int, out_width: int, latent_dtype: int) -> int:
+    return lib().dsa_sparse_mla_decode_workspace_size(Q, Hm, L, out_width, latent_dtype)
+
+
+def _ws(ws: Optional[torch.Tensor]):
+    if ws is None:
+        return _P(None), 0
+    if not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return _P(ws.data_ptr()), ws.numel() * ws.element_size()
+
+
+# --- the six calls ---------------------------------------------------------
+
+def dsa_head_gate(hidden, W, w, ws=None, stream=None) -> None:
+    M, K = hidden.shape
+    N = W.shape[1]
+    wp, wb = _ws(ws)
+    _check(lib().dsa_head_gate(_dev(hidden, torch.float32, "hidden"), _dev(W, torch.float32, "W"),
+                               _dev(w, torch.float32, "w"), M, K, N, wp, wb, _stream(stream)))
+
+
+def dsa_kpool_compress(k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b, eps: float, kpool: int,
+                       max_cap: int, keys, pool_start, pool_valid, n_pools, new_from=None,
+                       max_new: int = 0, stream=None) -> None:
+    B = tok_off.numel() - 1
+    D = k.shape[1]
+    _check(lib().dsa_kpool_compress(
+        _dev(k, _BF, "k"), _dev(gate, _BF, "gate"), _dev(ape, _BF, "ape"), _dev(valid, _U8, "valid"),
+        _dev(tok_off, _I32, "tok_off"), _dev(pool_off, _I32, "pool_off"),
+        _dev(ln_w, torch.float32, "ln_w"), _dev(ln_b, torch.float32, "ln_b"), float(eps), B, D,
+        kpool, max_cap, _dev(new_from, _I32, "new_from", allow_none=True), int(max_new),
+        _dev(keys, _BF, "keys"), _dev(pool_start, _I32, "pool_start"),
+        _dev(pool_valid, _U8, "pool_valid"), _dev(n_pools, _I32, "n_pools"), _stream(stream)))
+
+
+def dsa_index_scores(qi, w, keys, pool_start, pool_valid, pool_off, n_pools, q_req, q_pos,
+                     kpool: int, scores, cand, stream=None) -> None:
+    Q, H, D = qi.shape
+    pstride = scores.shape[1]
+    _check(lib().dsa_index_scores(
+        _dev(qi, _BF, "qi"), _dev(w, torch.float32, "w"), _dev(keys, _BF, "keys"),
+        _dev(pool_start, _I32, "pool_start"), _dev(pool_valid, _U8, "pool_valid"),
+        _dev(pool_off, _I32, "pool_off"), _dev(n_pools, _I32, "n_pools"), _dev(q_req, _I32, "q_req"),
+        _dev(q_pos, _I32, "q_pos"), Q, H, D, kpool, pstride, _dev(scores, torch.float32, "scores"),
+        _dev(cand, _U8, "cand"), _stream(stream)))
+
+
+def dsa_topk_pools(scores, cand, sel, ws=None, stream=None) -> None:
+    Q, pstride = scores.shape
+    select_k = sel.shape[1]
+    wp, wb = _ws(ws)
+    _check(lib().dsa_topk_pools(_dev(scores, torch.float32, "scores"), _dev(cand, _U8, "cand"), Q,
+                                pstride, select_k, _dev(sel, _I32, "sel"), wp, wb, _stream(stream)))
+
+
+def dsa_expand_selection(sel, pool_start, pool_off, q_req, kpool: int, tok, flags: int = 0,
+                         stream=None) -> None:
+    Q, select_k = sel.shape
+    out_width = tok.shape[1]
+    _check(lib().dsa_expand_selection(
+        _dev(sel, _I32, "sel"), _dev(pool_start, _I32, "pool_start"), _dev(pool_off, _I32, "pool_off"),
+        _dev(q_req, _I32, "q_req"), Q, select_k, kpool, out_width, flags, _dev(tok, _I32, "tok"),
+        _stream(stream)))
+
+
+def dsa_sparse_mla_decode(q, ckv, ckv_scale, kv_off, q_req, tok, sm_scale: float, out, lse=None,
+                          ws=None, stream=None) -> None:
+    Q, Hm, L = q.shape
+    out_width = tok.shape[1]
+    fp8 = ckv.dtype in (torch.uint8, torch.float8_e4m3fn)
+    dt = LATENT_FP8_E4M3 if fp8 else LATENT_BF16
+    wp, wb = _ws(ws)
+    _check(lib().dsa_sparse_mla_decode(
+        _dev(q, _BF, "q"), _dev(ckv, (torch.uint8, torch.float8_e4m3fn) if fp8 else _BF, "ckv"),
+        _dev(ckv_scale, torch.float32, "ckv_scale", allow_none=not fp8), dt,
+        _dev(kv_off, _I32, "kv_off"), _dev(q_req, _I32, "q_req"), _dev(tok, _I32, "tok"), Q, Hm, L,
+        out_width, float(sm_scale), _dev(out, _BF, "out"), _dev(lse, torch.float32, "lse", allow_none=True),
+        wp, wb, _stream(stream)))

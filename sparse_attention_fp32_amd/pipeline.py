@@ -1,0 +1,83 @@
+"""Device buffers for one DSA decode step and the six library calls in
+pipeline order.  Allocation is torch's; every step of the computation is a
+libdsa call."""
+from __future__ import annotations
+
+import torch
+
+from . import dsa
+from .workloads import Inputs
+
+
+class DsaStep:
+    """Owns the outputs and workspaces of one pass over one resident input set.
+
+    ``run(incremental=True)`` is a decode step over cached pools: the pools
+    that hold the newest row of each request are recompressed and every other
+    stage runs in full."""
+
+    def __init__(self, x: Inputs, stream=None):
+        s = x.spec
+        dev = x.k.device
+        assert dev.type == "cuda", "DsaStep needs inputs resident on the GPU"
+        self.x, self.spec, self.stream = x, s, stream
+        Q, B, H, D = s.Q, s.B, s.index_heads, s.index_dim
+        ncap = int(sum(s.pool_caps()))
+        self.max_cap = max(s.pool_caps()) if s.B else 0
+        self.pstride = s.pstride()
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.w = torch.empty(Q, H, dtype=torch.float32, device=dev)
+        self.ws_gate = torch.zeros(max(1, dsa.head_gate_workspace_size(Q, s.hidden, H)),
+                                   dtype=torch.uint8, device=dev)
+        self.keys = torch.empty(max(1, ncap), D, dtype=torch.int16, device=dev)
+        self.pool_start = torch.empty(max(1, ncap), **i32)
+        self.pool_valid = torch.empty(max(1, ncap), dtype=torch.uint8, device=dev)
+        self.n_pools = torch.empty(B, **i32)
+        self.scores = torch.empty(Q, self.pstride, dtype=torch.float32, device=dev)
+        self.cand = torch.empty(Q, self.pstride, dtype=torch.uint8, device=dev)
+        self.sel = torch.empty(Q, s.select_k, **i32)
+        self.tok = torch.empty(Q, s.out_width, **i32)
+        self.out = torch.empty(Q, s.mla_heads, s.latent, dtype=torch.int16, device=dev)
+        self.lse = torch.empty(Q, s.mla_heads, dtype=torch.float32, device=dev)
+        dt = dsa.LATENT_FP8_E4M3 if s.latent_fp8 else dsa.LATENT_BF16
+        self.ws_mla = torch.empty(max(1, dsa.sparse_mla_decode_workspace_size(
+            Q, s.mla_heads, s.latent, s.out_width, dt)), dtype=torch.uint8, device=dev)
+
+    # -- stages -------------------------------------------------------------
+    def head_gate(self):
+        dsa.dsa_head_gate(self.x.hidden, self.x.W, self.w, self.ws_gate, stream=self.stream)
+
+    def compress(self, incremental: bool = False):
+        x = self.x
+        dsa.dsa_kpool_compress(x.k, x.gate, x.ape, x.valid, x.tok_off, x.pool_off, x.ln_w, x.ln_b,
+                               self.spec.eps, self.spec.kpool, self.max_cap, self.keys,
+                               self.pool_start, self.pool_valid, self.n_pools,
+                               new_from=x.new_from if incremental else None,
+                               max_new=1 if incremental else 0, stream=self.stream)
+
+    def index_scores(self):
+        x = self.x
+        dsa.dsa_index_scores(x.qi, self.w, self.keys, self.pool_start, self.pool_valid, x.pool_off,
+                             self.n_pools, x.q_req, x.q_pos, self.spec.kpool, self.scores,
+                             self.cand, stream=self.stream)
+
+    def topk(self):
+        dsa.dsa_topk_pools(self.scores, self.cand, self.sel, stream=self.stream)
+
+    def expand(self):
+        dsa.dsa_expand_selection(self.sel, self.pool_start, self.x.pool_off, self.x.q_req,
+                                 self.spec.kpool, self.tok, stream=self.stream)
+
+    def mla(self):
+        x = self.x
+        dsa.dsa_sparse_mla_decode(x.q_mla, x.ckv, x.ckv_scale, x.kv_off, x.q_req, self.tok,
+                                  self.spec.sm_scale, self.out, self.lse, self.ws_mla,
+                                  stream=self.stream)
+
+    def run(self, incremental: bool = False):
+        self.head_gate()
+        self.compress(incremental)
+        self.index_scores()
+        self.topk()
+        self.expand()
+        self.mla()

@@ -113,10 +113,21 @@ def spec_by_name(name: str, seed: int = 0) -> Spec:
         return Spec(name, lengths=lengths, pads=pads, kpool=4, index_heads=16,
                     index_dim=128, hidden=4096, select_k=128, out_width=512,
                     mla_heads=64, latent_fp8=True)
+    # Parity shapes: oracle-seconds sizes that still span several tiles and
+    # leave ragged tails in every kernel's grid.
+    if name == "medium":
+        return Spec(name, lengths=[1000, 517, 2053], pads=[3, 0, 61], kpool=4, index_heads=16,
+                    index_dim=128, hidden=1024, select_k=100, out_width=404, mla_heads=64,
+                    q_req=[0, 0, 1, 2, 2], q_pos=[999, 480, 516, 2052, 700])
+    if name == "medium_fp8":
+        return Spec(name, lengths=[777, 1500, 96, 2500], pads=[0, 17, 95, 5], kpool=8,
+                    index_heads=12, index_dim=64, hidden=768, select_k=40, out_width=330,
+                    mla_heads=40, latent_fp8=True, sm_scale=1.0 / math.sqrt(512))
     raise KeyError(name)
 
 
 WORKLOADS = ("tiny", "decode32k", "longctx", "prefill4k", "mixed64")
+PARITY_SHAPES = ("tiny", "medium", "medium_fp8")
 
 
 @dataclasses.dataclass
@@ -143,6 +154,13 @@ class Inputs:
     ckv: torch.Tensor         # [sumT, L] bf16 bits, or uint8 fp8-e4m3 codes
     ckv_scale: Optional[torch.Tensor]  # [sumT] f32 for fp8, else None
     kv_off: torch.Tensor      # [B] i32
+
+    def to(self, device) -> "Inputs":
+        kw = {}
+        for f in dataclasses.fields(self):
+            v = getattr(self, f.name)
+            kw[f.name] = v.to(device) if isinstance(v, torch.Tensor) else v
+        return Inputs(**kw)
 
     def numpy(self) -> dict:
         out = {}

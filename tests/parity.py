@@ -1,0 +1,117 @@
+"""Comparison rules between the HIP path and the oracle.
+
+* integers (pool starts, validity, counts, candidate flags, selections, token
+  ids) must match exactly when the stage is fed the oracle's inputs;
+* head-gate: max |diff| <= 1e-5 (fp32 with another summation order; the split-K
+  head-gate of stkernel PR #227 measured 2.4e-6);
+* pooled keys: at most 1 bf16 ulp apart (fp32 vs fp64 arithmetic before the one
+  rounding to bf16);
+* scores: |diff| <= 1e-5 * max |score| of the row, -inf exactly where the
+  oracle has it;
+* MLA output: per (query, head) row, max |O - O_ref| / max |O_ref| <= 2e-2
+  (bf16 P and bf16 output rounding); lse within 1e-3 absolute;
+* chained top-k: pools in the symmetric difference of the two selections must
+  score (by the oracle) within CHAIN_GAP of the oracle's boundary score b.
+"""
+import numpy as np
+
+import oracle as O
+
+GATE_TOL = 1e-5
+SCORE_REL = 1e-5
+MLA_REL = 2e-2
+LSE_ABS = 1e-3
+GAP_REL = 1e-5     # stage-isolated boundary rule
+# In a chained run the keys come from the GPU and may differ from the oracle's
+# by one bf16 ulp (2^-8 relative) in about 1 element in 2000; one such element
+# moves a score by ~1e-4 of its size.  Chained selections may therefore differ
+# only between pools whose oracle scores are within 1e-3 of the boundary.
+CHAIN_GAP_REL = 1e-3
+
+
+def bf16_ulp_diff(a, b):
+    """Distance in bf16 ulps between two arrays of bf16 bit patterns."""
+    def ordered(x):
+        x = np.asarray(x).astype(np.uint16).astype(np.int32)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x)
+    return np.abs(ordered(a) - ordered(b))
+
+
+def check_gate(w_gpu, w_ref):
+    d = np.max(np.abs(w_gpu.astype(np.float64) - w_ref.astype(np.float64))) if w_ref.size else 0.0
+    assert d <= GATE_TOL, f"head-gate max|diff| {d:.3g} > {GATE_TOL}"
+    return d
+
+
+def check_compress(g, ref, requests=None, pool_off=None):
+    """g, ref: dicts of keys/pool_start/pool_valid/n_pools (numpy)."""
+    if requests is None:
+        sl = slice(None)
+        assert np.array_equal(g["n_pools"], ref["n_pools"]), "n_pools"
+        idx = np.arange(len(ref["pool_start"]))
+    else:
+        assert np.array_equal(g["n_pools"][requests], ref["n_pools"][requests]), "n_pools"
+        idx = np.concatenate([np.arange(pool_off[r], pool_off[r + 1]) for r in requests])
+    assert np.array_equal(g["pool_start"][idx], ref["pool_start"][idx]), "pool_start"
+    assert np.array_equal(g["pool_valid"][idx], ref["pool_valid"][idx]), "pool_valid"
+    u = bf16_ulp_diff(g["keys"][idx], ref["keys"][idx])
+    assert u.max(initial=0) <= 1, f"keys differ by {u.max()} bf16 ulps"
+    return int((u > 0).sum())
+
+
+def check_scores(s_gpu, c_gpu, s_ref, c_ref, rows=None):
+    rows = range(s_ref.shape[0]) if rows is None else rows
+    worst = 0.0
+    for q in rows:
+        assert np.array_equal(c_gpu[q], c_ref[q]), f"cand row {q}"
+        fin = np.isfinite(s_ref[q])
+        assert np.array_equal(np.isfinite(s_gpu[q]), fin), f"-inf pattern row {q}"
+        if fin.any():
+            scale = max(np.abs(s_ref[q][fin]).max(), 1e-30)
+            d = np.abs(s_gpu[q][fin].astype(np.float64) - s_ref[q][fin]).max() / scale
+            worst = max(worst, d)
+            assert d <= SCORE_REL, f"scores row {q}: rel diff {d:.3g}"
+    return worst
+
+
+def boundary_ok(sel_g, sel_r, s_ref, rel):
+    """Selections equal, or every disagreeing pool scores within rel of the
+    oracle's k-th score."""
+    a = set(int(x) for x in sel_g if x >= 0)
+    b = set(int(x) for x in sel_r if x >= 0)
+    if a == b:
+        return True, 0
+    if len(a) != len(b):
+        return False, len(a ^ b)
+    kth = min(float(s_ref[p]) for p in b)
+    finite = s_ref[np.isfinite(s_ref)]
+    tol = rel * max(abs(kth), 1e-6 * np.abs(finite).max())
+    ok = all(abs(float(s_ref[p]) - kth) <= tol for p in a ^ b)
+    return ok, len(a ^ b)
+
+
+def check_sel_exact(sel_g, sel_r, rows=None):
+    rows = range(sel_r.shape[0]) if rows is None else rows
+    for q in rows:
+        assert np.array_equal(sel_g[q], sel_r[q]), f"sel row {q}"
+        v = sel_g[q][sel_g[q] >= 0]
+        assert np.all(np.diff(v) > 0), "selection not strictly ascending"
+
+
+def check_mla(out_g_bits, lse_g, out_ref_f64, lse_ref, rows=None):
+    og = O.bf16_bits_to_f64(out_g_bits)
+    rows = range(out_ref_f64.shape[0]) if rows is None else rows
+    worst = 0.0
+    for q in rows:
+        for h in range(out_ref_f64.shape[1]):
+            ref = out_ref_f64[q, h]
+            m = np.abs(ref).max()
+            if m == 0:
+                assert np.all(og[q, h] == 0), f"empty row q={q} h={h} not zero"
+                assert np.isneginf(lse_g[q, h]) and np.isneginf(lse_ref[q, h])
+                continue
+            d = np.abs(og[q, h] - ref).max() / m
+            worst = max(worst, d)
+            assert d <= MLA_REL, f"MLA q={q} h={h}: rel err {d:.3g}"
+            assert abs(float(lse_g[q, h]) - lse_ref[q, h]) <= LSE_ABS, f"lse q={q} h={h}"
+    return worst

@@ -1,0 +1,123 @@
+"""The C ABI on the CPU: libdsa.so loads, exports every function include/dsa.h
+declares, and refuses bad host arguments with the documented code before it
+touches the GPU (no valid launch is attempted here)."""
+import ctypes
+import os
+
+import pytest
+
+from sparse_attention_fp32_amd import dsa
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dsa.LIB_PATH), reason="libdsa.so not built")
+
+INV, UNS = dsa.DSA_ERR_INVALID_ARG, dsa.DSA_ERR_UNSUPPORTED
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case fails validation first
+NUL = ctypes.c_void_p(None)
+
+
+def test_exports_every_declared_function():
+    names = dsa.header_functions()
+    assert len(names) == 11
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", dsa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for n in names:
+        assert n in exported, n
+        getattr(dsa.lib(), n)
+    assert dsa.abi_version() == 1
+
+
+def _code(fn, *args):
+    return fn(*args)
+
+
+def test_head_gate_errors():
+    L = dsa.lib()
+    assert L.dsa_head_gate(FAKE, FAKE, FAKE, 4, 4096, 0, NUL, 0, NUL) == INV
+    assert L.dsa_head_gate(FAKE, FAKE, FAKE, 4, 4096, 17, NUL, 0, NUL) == INV
+    assert "N=17" in dsa.last_error()
+    assert L.dsa_head_gate(FAKE, FAKE, FAKE, 4, 0, 16, NUL, 0, NUL) == INV
+    assert L.dsa_head_gate(FAKE, FAKE, FAKE, -1, 16, 16, NUL, 0, NUL) == INV
+    assert L.dsa_head_gate(NUL, FAKE, FAKE, 4, 4096, 16, FAKE, 1 << 20, NUL) == INV
+    # workspace too small for the split path
+    need = dsa.head_gate_workspace_size(16, 4096, 16)
+    assert need > 0
+    assert L.dsa_head_gate(FAKE, FAKE, FAKE, 16, 4096, 16, FAKE, need - 1, NUL) == INV
+    assert dsa.head_gate_workspace_size(4096, 4096, 16) == 0
+    assert L.dsa_head_gate(FAKE, FAKE, FAKE, 0, 4096, 16, NUL, 0, NUL) == dsa.DSA_OK  # no-op
+
+
+def _compress(kpool=4, D=128, B=2, max_cap=10, new_from=NUL, max_new=0, k=FAKE):
+    return dsa.lib().dsa_kpool_compress(k, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-5, B, D,
+                                        kpool, max_cap, new_from, max_new, FAKE, FAKE, FAKE, FAKE, NUL)
+
+
+def test_kpool_compress_errors():
+    # the page's validate(): kpool 0 and kpool above the 8-slot bound are refused
+    assert _compress(kpool=0) == INV
+    assert _compress(kpool=9) == INV
+    assert "never truncated" in dsa.last_error()
+    assert _compress(D=96) == UNS
+    assert _compress(D=512) == UNS
+    assert _compress(B=-1) == INV
+    assert _compress(max_cap=-1) == INV
+    assert _compress(new_from=FAKE, max_new=0) == INV
+    assert _compress(k=NUL) == INV
+    assert _compress(B=0) == dsa.DSA_OK
+
+
+def test_index_scores_errors():
+    L = dsa.lib()
+    def call(H=16, D=128, kpool=4, pstride=100, Q=3, qi=FAKE):
+        return L.dsa_index_scores(qi, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, Q, H, D,
+                                  kpool, pstride, FAKE, FAKE, NUL)
+    assert call(H=0) == INV
+    assert call(H=17) == INV
+    assert call(D=100) == UNS
+    assert call(kpool=9) == INV
+    assert call(pstride=0) == INV
+    assert call(Q=-2) == INV
+    assert call(qi=NUL) == INV
+    assert call(Q=0) == dsa.DSA_OK
+
+
+def test_topk_errors():
+    L = dsa.lib()
+    assert L.dsa_topk_pools(FAKE, FAKE, 4, 100, 0, FAKE, NUL, 0, NUL) == INV
+    assert L.dsa_topk_pools(FAKE, FAKE, 4, 0, 8, FAKE, NUL, 0, NUL) == INV
+    assert L.dsa_topk_pools(FAKE, FAKE, 4, dsa.MAX_TOPK_ROW + 1, 8, FAKE, NUL, 0, NUL) == UNS
+    assert L.dsa_topk_pools(NUL, FAKE, 4, 100, 8, FAKE, NUL, 0, NUL) == INV
+    assert dsa.topk_pools_workspace_size(16, 8192, 512) == 0
+
+
+def test_expand_errors():
+    L = dsa.lib()
+    def call(select_k=4, kpool=4, out_width=16, flags=0, sel=FAKE):
+        return L.dsa_expand_selection(sel, FAKE, FAKE, FAKE, 2, select_k, kpool, out_width, flags, FAKE, NUL)
+    # out_width must hold select_k * kpool ids (the page's topk % kpool rule)
+    assert call(out_width=15) == INV
+    assert call(kpool=0) == INV
+    assert call(kpool=9) == INV
+    assert call(select_k=0) == INV
+    assert call(flags=1) == UNS          # always_select_tail: not built
+    assert call(flags=2) == INV
+    assert call(sel=NUL) == INV
+
+
+def test_sparse_mla_errors():
+    L = dsa.lib()
+    def call(L_=512, Hm=64, out_width=2048, dt=0, scale=NUL, Q=16, ws=NUL, wsb=0, q=FAKE):
+        return L.dsa_sparse_mla_decode(q, FAKE, scale, dt, FAKE, FAKE, FAKE, Q, Hm, L_, out_width,
+                                       1.0, FAKE, NUL, ws, wsb, NUL)
+    # the page's validate(): the latent must be exactly 512 wide; zero heads refused
+    assert call(L_=576) == UNS
+    assert "512" in dsa.last_error()
+    assert call(Hm=0) == INV
+    assert call(out_width=0) == INV
+    assert call(dt=7) == INV
+    assert call(dt=1, scale=NUL) == INV           # fp8 without row scales
+    need = dsa.sparse_mla_decode_workspace_size(16, 64, 512, 2048, 0)
+    assert need > 0
+    assert call(ws=FAKE, wsb=need - 1) == INV
+    assert call(q=NUL, ws=FAKE, wsb=need) == INV
+    assert call(Q=0) == dsa.DSA_OK

@@ -1,0 +1,204 @@
+"""GPU parity of every stage against the CPU oracle on parity shapes that span
+several tiles with ragged tails.  Each stage is first fed the ORACLE's
+upstream outputs (stage isolation), then the whole chain runs on the GPU and
+is compared with the chained rules of tests/parity.py."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import parity as PT
+from sparse_attention_fp32_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _say(msg):
+    sys.stdout.write(f"\n[gpu-case] {msg}\n")
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", params=W.PARITY_SHAPES)
+def case(request):
+    _need_gpu()
+    from sparse_attention_fp32_amd.pipeline import DsaStep  # noqa: F401  (loads libdsa)
+    spec = W.spec_by_name(request.param)
+    x = W.make_inputs(spec, seed=0)
+    xn = x.numpy()
+    ref = O.dsa_step(xn, spec.kpool, spec.select_k, spec.out_width, spec.pstride(), spec.eps,
+                     spec.sm_scale)
+    return spec, xn, ref, x.to("cuda")
+
+
+def _step(xg):
+    from sparse_attention_fp32_amd.pipeline import DsaStep
+    return DsaStep(xg)
+
+
+def _poison(t):
+    t.view(torch.uint8).fill_(0xFF)
+
+
+def _np(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def test_head_gate(case):
+    spec, xn, ref, xg = case
+    _say(f"head_gate {spec.name}")
+    st = _step(xg)
+    _poison(st.w)
+    st.head_gate()
+    PT.check_gate(_np(st.w), ref["w"])
+
+
+def test_head_gate_repeat_keeps_workspace_clean(case):
+    spec, xn, ref, xg = case
+    _say(f"head_gate x3 {spec.name}")
+    st = _step(xg)
+    for _ in range(3):
+        st.head_gate()
+    PT.check_gate(_np(st.w), ref["w"])
+    assert int(st.ws_gate[:4].view(torch.int32).item() if st.ws_gate.numel() >= 4 else 0) == 0
+
+
+def test_kpool_compress(case):
+    spec, xn, ref, xg = case
+    _say(f"kpool_compress {spec.name}")
+    st = _step(xg)
+    for t in (st.keys, st.pool_start, st.pool_valid, st.n_pools):
+        _poison(t)
+    st.compress()
+    g = {"keys": _np(st.keys).view(np.uint16), "pool_start": _np(st.pool_start),
+         "pool_valid": _np(st.pool_valid), "n_pools": _np(st.n_pools)}
+    ncap = int(xn["pool_off"][-1])
+    g = {k: (v[:ncap] if k != "n_pools" else v) for k, v in g.items()}
+    flips = PT.check_compress(g, ref)
+    _say(f"keys differing by 1 ulp: {flips} of {ref['keys'].size}")
+
+
+def test_kpool_compress_incremental(case):
+    spec, xn, ref, xg = case
+    _say(f"kpool_compress incremental {spec.name}")
+    st = _step(xg)
+    st.compress()
+    # a decode step appends (here: rewrites) the newest row of every request
+    k2, g2 = xg.k.clone(), xg.gate.clone()
+    offs = xn["tok_off"]
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    for r in range(spec.B):
+        last = int(offs[r + 1]) - 1
+        k2[last] = torch.randn(spec.index_dim, generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+        g2[last] = torch.randn(spec.index_dim, generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+    xg2 = W.Inputs(**{**xg.__dict__, "k": k2, "gate": g2})
+    st.x = xg2
+    st.compress(incremental=True)
+    x2 = dict(xn, k=k2.cpu().numpy(), gate=g2.cpu().numpy())
+    ref2 = O.kpool_compress(x2["k"], x2["gate"], x2["ape"], x2["valid"], x2["tok_off"],
+                            x2["pool_off"], x2["ln_w"], x2["ln_b"], spec.eps, spec.kpool)
+    ncap = int(xn["pool_off"][-1])
+    g = {"keys": _np(st.keys).view(np.uint16)[:ncap], "pool_start": _np(st.pool_start)[:ncap],
+         "pool_valid": _np(st.pool_valid)[:ncap], "n_pools": _np(st.n_pools)}
+    PT.check_compress(g, ref2)
+
+
+def _load_oracle_front(st, ref):
+    ncap = len(ref["pool_start"])
+    st.w.copy_(torch.from_numpy(ref["w"]))
+    st.keys[:ncap].copy_(torch.from_numpy(ref["keys"].view(np.int16)))
+    st.pool_start[:ncap].copy_(torch.from_numpy(ref["pool_start"]))
+    st.pool_valid[:ncap].copy_(torch.from_numpy(ref["pool_valid"]))
+    st.n_pools.copy_(torch.from_numpy(ref["n_pools"]))
+
+
+def test_index_scores_isolated(case):
+    spec, xn, ref, xg = case
+    _say(f"index_scores {spec.name}")
+    st = _step(xg)
+    _load_oracle_front(st, ref)
+    _poison(st.scores)
+    _poison(st.cand)
+    st.index_scores()
+    worst = PT.check_scores(_np(st.scores), _np(st.cand), ref["scores"], ref["cand"])
+    _say(f"scores worst rel diff {worst:.3g}")
+
+
+def test_topk_isolated(case):
+    spec, xn, ref, xg = case
+    _say(f"topk {spec.name}")
+    st = _step(xg)
+    st.scores.copy_(torch.from_numpy(ref["scores"]))
+    st.cand.copy_(torch.from_numpy(ref["cand"]))
+    _poison(st.sel)
+    st.topk()
+    PT.check_sel_exact(_np(st.sel), ref["sel"])
+
+
+def test_expand_isolated(case):
+    spec, xn, ref, xg = case
+    _say(f"expand {spec.name}")
+    st = _step(xg)
+    _load_oracle_front(st, ref)
+    st.sel.copy_(torch.from_numpy(ref["sel"]))
+    _poison(st.tok)
+    st.expand()
+    assert np.array_equal(_np(st.tok), ref["tok"])
+
+
+def test_mla_isolated(case):
+    spec, xn, ref, xg = case
+    _say(f"sparse_mla {spec.name}")
+    st = _step(xg)
+    st.tok.copy_(torch.from_numpy(ref["tok"]))
+    _poison(st.out)
+    _poison(st.lse)
+    st.mla()
+    worst = PT.check_mla(_np(st.out), _np(st.lse), ref["out_f64"], ref["lse"])
+    _say(f"MLA worst rel err {worst:.3g}")
+
+
+def test_chain(case):
+    spec, xn, ref, xg = case
+    _say(f"chain {spec.name}")
+    st = _step(xg)
+    st.run()
+    PT.check_gate(_np(st.w), ref["w"])
+    s_g = _np(st.scores)
+    sel_g, tok_g = _np(st.sel), _np(st.tok)
+    for q in range(spec.Q):
+        ok, nd = PT.boundary_ok(sel_g[q], ref["sel"][q], ref["scores"][q], PT.CHAIN_GAP_REL)
+        assert ok, f"chained selection row {q}: {nd} pools differ away from the boundary"
+        if nd == 0:
+            assert np.array_equal(tok_g[q], ref["tok"][q])
+            PT.check_mla(_np(st.out), _np(st.lse), ref["out_f64"], ref["lse"], rows=[q])
+
+
+def test_determinism_and_duplicate_rows(case):
+    spec, xn, ref, xg = case
+    _say(f"determinism {spec.name}")
+    # make query 1 an exact copy of query 0 (same request, position, vectors)
+    if spec.Q < 2:
+        pytest.skip("needs two queries")
+    d = dict(xg.__dict__)
+    for name in ("hidden", "qi", "q_mla", "q_req", "q_pos"):
+        t = d[name].clone()
+        t[1] = t[0]
+        d[name] = t
+    x2 = W.Inputs(**d)
+    st = _step(x2)
+    st.run()
+    a = [_np(t).copy() for t in (st.w, st.scores, st.sel, st.tok, st.out, st.lse)]
+    st.run()
+    b = [_np(t) for t in (st.w, st.scores, st.sel, st.tok, st.out, st.lse)]
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8)), "run-to-run difference"
+    for u in a:
+        assert np.array_equal(u[0].view(np.uint8), u[1].view(np.uint8)), "duplicate rows split"
