@@ -1,0 +1,263 @@
+"""DSA decode throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode32k]
+
+A step is one pass of the whole path -- head-gate, pool compression (of the
+pools the step's newest row completes; all older pools are cached), index
+scores, pool top-k, selection expansion, sparse MLA -- over one batch of
+resident synthetic input: the 32K-context decode batch (16 requests x 32768
+cached rows, one query each) by default.  Eight input sets (each larger than
+the 256 MB last-level cache together with its outputs) are rotated so that
+every step streams its keys and latent rows from HBM.  Each set's six calls
+are captured once in a HIP graph; the timed region replays K graphs.
+
+The JSON line also carries, for the kernel that takes the most time, its
+algorithmic bytes per launch over its average launch time (HIP events on the
+launch stream), against the 8 TB/s HBM peak; and the CPU oracle's throughput
+on a bounded sample of the same workload (rank 0 only).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from sparse_attention_fp32_amd import dsa  # noqa: E402
+from sparse_attention_fp32_amd import workloads as W  # noqa: E402
+from sparse_attention_fp32_amd.pipeline import DsaStep  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+STAGES = ("head_gate", "kpool_compress", "index_scores", "topk_pools", "expand_selection",
+          "sparse_mla_decode")
+# kernel source behind each stage (a change to it invalidates stored HBM counters)
+STAGE_SOURCE = {"head_gate": "head_gate.hip", "kpool_compress": "kpool_compress.hip",
+                "index_scores": "index_scores.hip", "topk_pools": "topk.hip",
+                "expand_selection": "expand.hip", "sparse_mla_decode": "sparse_mla.hip"}
+
+
+def algorithmic_bytes(spec: W.Spec, xn: dict, n_pools: np.ndarray, tok: np.ndarray) -> dict:
+    """Bytes each call must move at least once (inputs read once, outputs
+    written once), for the cached-pool decode step."""
+    Q, H, D, Hm, L = spec.Q, spec.index_heads, spec.index_dim, spec.mla_heads, spec.latent
+    kp = spec.kpool
+    req = np.asarray(xn["q_req"])
+    P_q = n_pools[req].astype(np.int64)               # pools scanned per query
+    pst = spec.pstride()
+    touched = len(spec.lengths)                        # one pool per request
+    lat_row = L * (1 if spec.latent_fp8 else 2) + (4 if spec.latent_fp8 else 0)
+    n_sel = int((tok >= 0).sum())
+    b = {
+        "head_gate": 4 * (Q * spec.hidden + spec.hidden * H + Q * H),
+        # kpool rows of k and gate per touched pool, ape, LN params, key + meta out,
+        # the valid flags of each pool, offsets
+        "kpool_compress": touched * (2 * kp * D * 2 + kp + D * 2 + 5) + kp * D * 2 + 8 * D
+        + 4 * (2 * (spec.B + 1) + 2 * spec.B),
+        "index_scores": int(P_q.sum()) * (D * 2 + 5) + Q * H * (D * 2 + 4) + Q * pst * 5 + 12 * Q,
+        "topk_pools": Q * pst * 5 + Q * spec.select_k * 4,
+        "expand_selection": Q * spec.select_k * 8 + Q * spec.out_width * 4 + 8 * Q,
+        "sparse_mla_decode": n_sel * lat_row + Q * Hm * L * 2 * 2 + Q * spec.out_width * 4
+        + Q * Hm * 4 + 8 * Q,
+    }
+    return b
+
+
+def source_sha(stage: str) -> str:
+    p = os.path.join(ROOT, "sparse_attention_fp32_amd", "csrc", STAGE_SOURCE[stage])
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(stage: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if a summary for
+    this kernel source and workload is stored in profiles/."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.txt")
+    if not os.path.exists(p):
+        return None
+    kv = {}
+    with open(p) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.strip().split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha") != source_sha(stage):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(spec: W.Spec, x: W.Inputs, budget_s: float = 12.0) -> dict:
+    """The oracle, untuned, on a bounded sample: the cached-pool step for the
+    first four queries, repeated until about budget_s seconds have passed."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    nq = min(4, spec.Q)
+    qs = list(range(nq))
+    reqs = sorted({int(r) for r in x.q_req[:nq].tolist()})
+    # the sample's inputs, copied to host memory (rows of the sampled requests)
+    xn = {}
+    for k_, v in x.__dict__.items():
+        if isinstance(v, torch.Tensor):
+            xn[k_] = v.cpu().numpy()
+    prev = O.kpool_compress(xn["k"], xn["gate"], xn["ape"], xn["valid"], xn["tok_off"],
+                            xn["pool_off"], xn["ln_w"], xn["ln_b"], spec.eps, spec.kpool,
+                            requests=reqs)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.dsa_step(xn, spec.kpool, spec.select_k, spec.out_width, spec.pstride(), spec.eps,
+                   spec.sm_scale, new_from=xn["new_from"], prev=prev, queries=qs)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": round(reps * nq / el, 3), "unit": "queries/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{spec.name}: cached-pool step of queries 0..{nq - 1} (their requests "
+                      f"compressed beforehand), {reps} repetitions in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="decode32k", choices=W.WORKLOADS)
+    ap.add_argument("--sets", type=int, default=8)
+    ap.add_argument("--stage-reps", type=int, default=48)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": a.gpus}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    dsa.lib()
+    spec = W.spec_by_name(a.workload)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    # -- resident input sets and their output buffers ---------------------------
+    sets, steps = [], []
+    for i in range(a.sets):
+        x = W.make_inputs(spec, seed=1000 + i, device=dev)
+        st = DsaStep(x)
+        st.run(incremental=False)       # cache every pool once (set-up, untimed)
+        sets.append(x)
+        steps.append(st)
+    torch.cuda.synchronize()
+    print(f"[bench] {a.sets} input sets of {spec.name} resident", file=sys.stderr, flush=True)
+
+    graphs = []
+    for st in steps:
+        st.run(incremental=True)        # warm the path once before capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            st.run(incremental=True)
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    for i in range(a.warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(a.steps):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1)
+    ms_per_step = ms / a.steps
+    qps = spec.Q * a.steps / (ms / 1e3)
+
+    # -- per-call launch times (HIP events on the launch stream) ---------------
+    stream = torch.cuda.current_stream()
+    fns = {
+        "head_gate": lambda s: s.head_gate(),
+        "kpool_compress": lambda s: s.compress(incremental=True),
+        "index_scores": lambda s: s.index_scores(),
+        "topk_pools": lambda s: s.topk(),
+        "expand_selection": lambda s: s.expand(),
+        "sparse_mla_decode": lambda s: s.mla(),
+    }
+    stage_us = {}
+    for name in STAGES:
+        evs = []
+        for i in range(a.stage_reps):
+            s = steps[i % len(steps)]
+            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ea.record(stream)
+            fns[name](s)
+            eb.record(stream)
+            evs.append((ea, eb))
+        torch.cuda.synchronize()
+        d = [ea.elapsed_time(eb) * 1e3 for ea, eb in evs[4:]]
+        stage_us[name] = float(np.mean(d))
+
+    xn0 = {"q_req": sets[0].q_req.cpu().numpy()}
+    nb = algorithmic_bytes(spec, xn0, steps[0].n_pools.cpu().numpy(), steps[0].tok.cpu().numpy())
+    step_bytes = sum(nb.values())
+    dom = max(STAGES, key=lambda n: stage_us[n])
+    ach = nb[dom] / (stage_us[dom] * 1e-6) / 1e9
+    traffic = stored_traffic(dom, spec.name)
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes": int(nb[dom]), "avg_launch_us": round(stage_us[dom], 2)}
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        cpu = cpu_baseline(spec, sets[0])
+
+    line = {
+        "metric": "DSA decode queries/s (gate+indexer+top-k+sparse MLA) and % of HBM peak",
+        "value": round(qps, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "precision": "bf16 MFMA operands with f32 accumulation; f32 head-gate and pooling",
+        "data": "synthetic, seeded",
+        "config": {"workload": spec.name, "requests": spec.B, "queries": spec.Q,
+                   "context_rows": spec.lengths[0] if len(set(spec.lengths)) == 1 else "ragged",
+                   "kpool": spec.kpool, "select_k": spec.select_k, "out_width": spec.out_width,
+                   "index_heads": spec.index_heads, "index_dim": spec.index_dim,
+                   "mla_heads": spec.mla_heads, "latent": spec.latent,
+                   "latent_dtype": "fp8_e4m3" if spec.latent_fp8 else "bf16",
+                   "pools": "cached; the step recompresses the pool of its newest row",
+                   "input_sets": a.sets, "graph": "one HIP graph per set, six calls"},
+        "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_algorithmic_bytes": int(step_bytes),
+        "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "stage_bytes": {k: int(v) for k, v in nb.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
