@@ -76,16 +76,14 @@ const char* dsa_last_error(void);
  *   w[m, n] = sum_k hidden[m, k] * W[k, n]        (fp32 in, fp32 accumulate)
  *
  * hidden [M, K] f32, W [K, N] f32, w [M, N] f32.  1 <= N <= 16, K >= 1,
- * M >= 0 (M = 0 is a no-op).  For M <= 16 (decode) the product is split over
- * K across many workgroups and the partial sums are added in a fixed order by
- * the last workgroup to finish, so the result is deterministic and the same
- * for every row of a batch.  This path needs a workspace of
- * dsa_head_gate_workspace_size(M, K, N) bytes that is ZERO-FILLED before its
- * first use; every call leaves it zero-filled again.  For M > 16 one
- * workgroup per 16 rows runs the whole K loop and the workspace is unused
- * (the size is 0; ws may be NULL).
- * Errors: INVALID_ARG for N outside [1,16], K < 1, M < 0, a NULL pointer with
- * M > 0, or ws_bytes below the size.
+ * M >= 0 (M = 0 is a no-op).  For M <= 16 (decode) every row gets its own
+ * workgroup that spreads K over 1024 threads and adds the partial sums in a
+ * fixed order, so the result is deterministic and the same bits for a row
+ * whatever the batch.  For M > 16 one workgroup per 16 rows walks K.  No
+ * workspace is needed at present (dsa_head_gate_workspace_size returns 0; ws
+ * may be NULL).
+ * Errors: INVALID_ARG for N outside [1,16], K < 1, M < 0, or a NULL pointer
+ * with M > 0.
  * ------------------------------------------------------------------------- */
 size_t dsa_head_gate_workspace_size(int M, int K, int N);
 dsa_status dsa_head_gate(const float* hidden, const float* W, float* w, int M, int K, int N,

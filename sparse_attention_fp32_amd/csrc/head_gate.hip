@@ -1,106 +1,184 @@
 // a1: fp32 indexer head-gate  w[M,N] = hidden[M,K] @ W[K,N]   (N <= 16)
 //
-// The product of stkernel PR #227 ("indexer fp32 head-gate split-K"): at decode
-// (M <= 16) a plain GEMM leaves almost every compute unit idle, so K is split
-// into 128-row slices, one workgroup per slice.  Unlike the atomic float adds
-// of that PR, the slice partials go to a workspace and the last workgroup to
-// arrive (an integer ticket) adds them in slice order: deterministic, and the
-// same bits for every row of a batch.  Above 16 rows each workgroup owns 16
-// rows and walks all of K itself.
+// The product of stkernel PR #227 ("indexer fp32 head-gate split-K").  At
+// decode (M <= 16) a plain GEMM leaves almost every compute unit idle and the
+// PR splits K over programs that add their partials with float atomics.  Here
+// each of the M rows gets a 1024-thread workgroup that issues all of its loads
+// at once (four 16-float rows of W and four hidden values per thread), keeps 16
+// running sums per thread, and reduces them in a fixed order: a
+// reduce-scatter over the wave (17 shuffles leave lane l with output j(l)),
+// then the 16 waves' sums added in wave order.  Deterministic, and the same
+// bits for a row whatever the batch.  Above 16 rows each workgroup owns 16 rows
+// and walks K through LDS tiles.
 //
-// HBM-bound work (2 FLOP per 4-byte hidden element), so this is plain fp32
-// VALU arithmetic with LDS-staged tiles, not MFMA.
+// HBM-bound work (2 FLOP per 4-byte element of hidden), so this is plain fp32
+// VALU arithmetic, not MFMA.
 #include "dsa_device.hpp"
 #include "dsa_host.hpp"
 
 namespace {
 
-constexpr int kSlice = 128;  // K rows per slice
-constexpr int kRows = 16;    // output rows per workgroup
-constexpr size_t kTicketBytes = 256;
+using namespace dsa;
 
-// Thread t owns output (m = t / 16, n = t % 16) of the workgroup's 16 rows.
-__global__ __launch_bounds__(256) void head_gate_kernel(const float* __restrict__ hidden,
-                                                        const float* __restrict__ W,
-                                                        float* __restrict__ w,
-                                                        float* __restrict__ partial,
-                                                        unsigned* __restrict__ ticket, int M,
-                                                        int K, int N) {
+constexpr int kSlice = 128;  // K rows per LDS tile (rows path)
+constexpr int kRows = 16;    // output rows per workgroup (rows path)
+constexpr int kRowThreads = 1024;
+constexpr int kPerThread = 4;  // K elements per thread per pass (row path)
+
+// One workgroup per output row m (M <= 16).  Thread t takes k = t + 1024*i.
+__global__ __launch_bounds__(kRowThreads) void head_gate_row_kernel(const float* __restrict__ hidden,
+                                                                    const float* __restrict__ W,
+                                                                    float* __restrict__ w, int K,
+                                                                    int N) {
+  __shared__ float s_part[kRowThreads / 64][16];
+  const int m = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const float* hrow = hidden + (size_t)m * K;
+  float acc[16];
+#pragma unroll
+  for (int n = 0; n < 16; ++n) acc[n] = 0.f;
+  for (int k0 = 0; k0 < K; k0 += kRowThreads * kPerThread) {
+    float h[kPerThread];
+    float4 wr[kPerThread][4];
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int k = k0 + t + kRowThreads * i;
+      const int kc = k < K ? k : K - 1;  // clamped: every load is in bounds
+      h[i] = hrow[kc];
+      if (N == 16) {
+        const float4* wp = (const float4*)(W + (size_t)kc * 16);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) wr[i][c] = wp[c];
+      } else {
+        float tmp[16];
+#pragma unroll
+        for (int n = 0; n < 16; ++n) tmp[n] = n < N ? W[(size_t)kc * N + n] : 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          wr[i][c] = make_float4(tmp[4 * c], tmp[4 * c + 1], tmp[4 * c + 2], tmp[4 * c + 3]);
+      }
+      if (k >= K) h[i] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        acc[4 * c + 0] = fmaf(h[i], wr[i][c].x, acc[4 * c + 0]);
+        acc[4 * c + 1] = fmaf(h[i], wr[i][c].y, acc[4 * c + 1]);
+        acc[4 * c + 2] = fmaf(h[i], wr[i][c].z, acc[4 * c + 2]);
+        acc[4 * c + 3] = fmaf(h[i], wr[i][c].w, acc[4 * c + 3]);
+      }
+    }
+  }
+  // Reduce-scatter over the wave: after the xor-32/16/8/4 steps lane l holds
+  // the sum over 16 lanes of output j(l) = 8*b5 + 4*b4 + 2*b3 + b2 (bits of l);
+  // xor 2 and 1 finish the sum over all 64 lanes.
+  float v8[8], v4[4], v2[2];
+  {
+    const bool hi = (lane >> 5) & 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float send = hi ? acc[i] : acc[8 + i];
+      const float keep = hi ? acc[8 + i] : acc[i];
+      v8[i] = keep + __shfl_xor(send, 32, kWave);
+    }
+  }
+  {
+    const bool hi = (lane >> 4) & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float send = hi ? v8[i] : v8[4 + i];
+      const float keep = hi ? v8[4 + i] : v8[i];
+      v4[i] = keep + __shfl_xor(send, 16, kWave);
+    }
+  }
+  {
+    const bool hi = (lane >> 3) & 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float send = hi ? v4[i] : v4[2 + i];
+      const float keep = hi ? v4[2 + i] : v4[i];
+      v2[i] = keep + __shfl_xor(send, 8, kWave);
+    }
+  }
+  float v;
+  {
+    const bool hi = (lane >> 2) & 1;
+    const float send = hi ? v2[0] : v2[1];
+    const float keep = hi ? v2[1] : v2[0];
+    v = keep + __shfl_xor(send, 4, kWave);
+  }
+  v += __shfl_xor(v, 2, kWave);
+  v += __shfl_xor(v, 1, kWave);
+  if ((lane & 3) == 0) {
+    const int j = ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 +
+                  ((lane >> 2) & 1);
+    s_part[wv][j] = v;
+  }
+  __syncthreads();
+  if (t < N) {
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < kRowThreads / 64; ++i) tot += s_part[i][t];
+    w[(size_t)m * N + t] = tot;
+  }
+}
+
+// 16 rows per workgroup, all of K through LDS tiles (M > 16).  Thread t owns
+// output (m = t / 16, n = t % 16).
+__global__ __launch_bounds__(256) void head_gate_rows_kernel(const float* __restrict__ hidden,
+                                                             const float* __restrict__ W,
+                                                             float* __restrict__ w, int M, int K,
+                                                             int N) {
   __shared__ float sh[kRows][kSlice + 1];
   __shared__ float sw[kSlice][16];
-  __shared__ int s_last;
   const int t = threadIdx.x, m = t >> 4, n = t & 15;
-  const int row0 = blockIdx.y * kRows;
-  const int nsplit = gridDim.x;
-  const int nslices = (K + kSlice - 1) / kSlice;
+  const int row0 = blockIdx.x * kRows;
   float acc = 0.f;
-  for (int sl = blockIdx.x; sl < nslices; sl += nsplit) {
-    const int k0 = sl * kSlice;
+  for (int k0 = 0; k0 < K; k0 += kSlice) {
     __syncthreads();
     for (int i = t; i < kRows * kSlice; i += 256) {
       const int mm = i / kSlice, kk = i % kSlice;
       const int gm = row0 + mm, gk = k0 + kk;
-      sh[mm][kk] = (gm < M && gk < K) ? hidden[(size_t)gm * K + gk] : 0.f;
+      const float v = hidden[(size_t)(gm < M ? gm : M - 1) * K + (gk < K ? gk : K - 1)];
+      sh[mm][kk] = (gm < M && gk < K) ? v : 0.f;
     }
     for (int i = t; i < kSlice * 16; i += 256) {
       const int kk = i >> 4, nn = i & 15;
       const int gk = k0 + kk;
-      sw[kk][nn] = (gk < K && nn < N) ? W[(size_t)gk * N + nn] : 0.f;
+      const float v = W[(size_t)(gk < K ? gk : K - 1) * N + (nn < N ? nn : N - 1)];
+      sw[kk][nn] = (gk < K && nn < N) ? v : 0.f;
     }
     __syncthreads();
 #pragma unroll 16
     for (int kk = 0; kk < kSlice; ++kk) acc = fmaf(sh[m][kk], sw[kk][n], acc);
   }
   const int gm = row0 + m;
-  if (nsplit == 1) {
-    if (gm < M && n < N) w[(size_t)gm * N + n] = acc;
-    return;
-  }
-  partial[blockIdx.x * 256 + t] = acc;
-  __threadfence();  // release the partial before taking a ticket
-  __syncthreads();
-  if (t == 0) s_last = (atomicAdd(ticket, 1u) == (unsigned)(nsplit - 1));
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();  // acquire every other workgroup's partial
-  float tot = 0.f;
-  for (int s = 0; s < nsplit; ++s) tot += partial[s * 256 + t];
-  if (gm < M && n < N) w[(size_t)gm * N + n] = tot;
-  if (t == 0) atomicExch(ticket, 0u);  // hand the workspace back zeroed
-}
-
-int split_count(int M, int K) {
-  if (M > kRows) return 1;
-  return (K + kSlice - 1) / kSlice;
+  if (gm < M && n < N) w[(size_t)gm * N + n] = acc;
 }
 
 }  // namespace
 
 DSA_EXPORT size_t dsa_head_gate_workspace_size(int M, int K, int N) {
+  (void)M;
+  (void)K;
   (void)N;
-  if (M <= 0 || K < 1) return 0;
-  const int ns = split_count(M, K);
-  if (ns <= 1) return 0;
-  return kTicketBytes + (size_t)ns * 256 * sizeof(float);
+  return 0;
 }
 
 DSA_EXPORT dsa_status dsa_head_gate(const float* hidden, const float* W, float* w, int M, int K,
                                     int N, void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
   DSA_REQUIRE(N >= 1 && N <= DSA_MAX_INDEX_HEADS, DSA_ERR_INVALID_ARG,
               "dsa_head_gate: N=%d outside [1,%d]", N, DSA_MAX_INDEX_HEADS);
   DSA_REQUIRE(K >= 1, DSA_ERR_INVALID_ARG, "dsa_head_gate: K=%d < 1", K);
   DSA_REQUIRE(M >= 0, DSA_ERR_INVALID_ARG, "dsa_head_gate: M=%d < 0", M);
   if (M == 0) return DSA_OK;
   DSA_REQUIRE(hidden && W && w, DSA_ERR_INVALID_ARG, "dsa_head_gate: NULL tensor pointer");
-  const size_t need = dsa_head_gate_workspace_size(M, K, N);
-  DSA_REQUIRE(ws_bytes >= need && (need == 0 || ws), DSA_ERR_INVALID_ARG,
-              "dsa_head_gate: workspace %zu bytes, need %zu", ws_bytes, need);
-  const int ns = split_count(M, K);
-  dim3 grid(ns, (M + kRows - 1) / kRows);
-  unsigned* ticket = need ? (unsigned*)ws : nullptr;
-  float* partial = need ? (float*)((char*)ws + kTicketBytes) : nullptr;
-  if (dsa::trace_enabled())
-    fprintf(stderr, "[dsa] head_gate M=%d K=%d N=%d grid=(%d,%d)\n", M, K, N, grid.x, grid.y);
-  head_gate_kernel<<<grid, 256, 0, stream>>>(hidden, W, w, partial, ticket, M, K, N);
+  if (dsa::trace_enabled()) fprintf(stderr, "[dsa] head_gate M=%d K=%d N=%d\n", M, K, N);
+  if (M <= kRows)
+    head_gate_row_kernel<<<M, kRowThreads, 0, stream>>>(hidden, W, w, K, N);
+  else
+    head_gate_rows_kernel<<<(M + kRows - 1) / kRows, 256, 0, stream>>>(hidden, W, w, M, K, N);
   return dsa::check_launch("dsa_head_gate");
 }

@@ -38,31 +38,44 @@ __global__ __launch_bounds__(256) void index_scores_kernel(
   const int qp = q_pos[q];
   const int tile0 = blockIdx.x * kPoolsPerWG + wave * (kTiles * 16);
 
-  // Key rows first: they are the long-latency HBM stream.
+  // Key rows first: they are the long-latency HBM stream.  All of the wave's
+  // loads are issued together (indices clamped to the request's last pool, so
+  // no load is conditional); out-of-range pools are masked below.
   uint4 b[kTiles][KS];
   int ps[kTiles], pv[kTiles];
+  if (tile0 < P) {
 #pragma unroll
-  for (int tt = 0; tt < kTiles; ++tt) {
-    const int p = tile0 + tt * 16 + col;
-    const bool in = p < P;
-    const uint16_t* krow = keys + (base + (in ? p : 0)) * D + grp * 8;
+    for (int tt = 0; tt < kTiles; ++tt) {
+      const int p = min(tile0 + tt * 16 + col, P - 1);
+      const uint16_t* krow = keys + (base + p) * D + grp * 8;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-      b[tt][kk] = in ? *(const uint4*)(krow + kk * 32) : make_uint4(0, 0, 0, 0);
-    ps[tt] = in ? pool_start[base + p] : 0;
-    pv[tt] = in ? (int)pool_valid[base + p] : 0;
+      for (int kk = 0; kk < KS; ++kk) b[tt][kk] = *(const uint4*)(krow + kk * 32);
+      ps[tt] = pool_start[base + p];
+      pv[tt] = pool_valid[base + p];
+    }
+  } else {
+#pragma unroll
+    for (int tt = 0; tt < kTiles; ++tt) {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) b[tt][kk] = make_uint4(0, 0, 0, 0);
+      ps[tt] = 0;
+      pv[tt] = 0;
+    }
   }
   // A operand: row m = head col, k = kk*32 + grp*8 + j.
   bf16x8_t a[KS];
-  const uint16_t* qrow = qi + ((int64_t)q * H + (col < H ? col : 0)) * D + grp * 8;
+  const uint16_t* qrow = qi + ((int64_t)q * H + (col < H ? col : H - 1)) * D + grp * 8;
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk)
-    a[kk] = as_bf16x8(col < H ? *(const uint4*)(qrow + kk * 32) : make_uint4(0, 0, 0, 0));
+  for (int kk = 0; kk < KS; ++kk) {
+    const uint4 v = *(const uint4*)(qrow + kk * 32);
+    a[kk] = as_bf16x8(col < H ? v : make_uint4(0, 0, 0, 0));
+  }
   float wr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int h = grp * 4 + i;
-    wr[i] = h < H ? w[(int64_t)q * H + h] : 0.f;
+    const float v = w[(int64_t)q * H + (h < H ? h : H - 1)];
+    wr[i] = h < H ? v : 0.f;
   }
 
 #pragma unroll

@@ -22,8 +22,9 @@ namespace {
 
 using namespace dsa;
 
-// First valid row of a request (request-local), or -1: the whole workgroup
-// scans 4 KiB windows and stops at the first window holding a valid byte.
+// First valid row of a request (request-local), or -1.  The whole workgroup
+// scans 4 KiB windows (16 bytes per thread, all loads issued together with
+// clamped addresses) and stops at the first window holding a valid byte.
 __device__ int first_valid_row(const uint8_t* __restrict__ valid, int64_t row0, int T,
                                int* s_first) {
   const int t = threadIdx.x;
@@ -31,16 +32,13 @@ __device__ int first_valid_row(const uint8_t* __restrict__ valid, int64_t row0, 
   __syncthreads();
   for (int base = 0; base < T; base += 256 * 16) {
     const int lo = base + t * 16;
+    uint8_t b[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) b[i] = valid[row0 + min(lo + i, T - 1)];
     int found = INT_MAX;
-    if (lo < T) {
-      const uint8_t* p = valid + row0 + lo;
-      const int n = min(16, T - lo);
-      for (int i = 0; i < n; ++i)
-        if (p[i]) {
-          found = lo + i;
-          break;
-        }
-    }
+#pragma unroll
+    for (int i = 15; i >= 0; --i)
+      if (lo + i < T && b[i]) found = lo + i;
     if (found != INT_MAX) atomicMin(s_first, found);
     __syncthreads();
     const int cur = *s_first;
@@ -101,7 +99,7 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
   uint4 ap[DSA_MAX_KPOOL];
 #pragma unroll
   for (int s = 0; s < DSA_MAX_KPOOL; ++s)
-    ap[s] = s < kpool ? *(const uint4*)(ape + s * D + c0) : make_uint4(0, 0, 0, 0);
+    ap[s] = *(const uint4*)(ape + (s < kpool ? s : kpool - 1) * D + c0);
 
   for (int p = s0 + grp; p < s1; p += kGroups) {
     uint16_t* kout = keys + (pbase + p) * D + c0;
@@ -114,16 +112,19 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
       continue;
     }
     const int64_t rb = row0 + f + (int64_t)p * kpool;
+    // every slot load is issued at once; slots past kpool re-read the last row
     uint4 kr[DSA_MAX_KPOOL], gr[DSA_MAX_KPOOL];
-    int allv = 1;
+    uint8_t vb[DSA_MAX_KPOOL];
 #pragma unroll
     for (int s = 0; s < DSA_MAX_KPOOL; ++s) {
-      if (s < kpool) {
-        kr[s] = *(const uint4*)(k + (rb + s) * D + c0);
-        gr[s] = *(const uint4*)(gate + (rb + s) * D + c0);
-        allv &= valid[rb + s] != 0;
-      }
+      const int64_t row = rb + (s < kpool ? s : kpool - 1);
+      kr[s] = *(const uint4*)(k + row * D + c0);
+      gr[s] = *(const uint4*)(gate + row * D + c0);
+      vb[s] = valid[row];
     }
+    int allv = 1;
+#pragma unroll
+    for (int s = 0; s < DSA_MAX_KPOOL; ++s) allv &= vb[s] != 0;
     float x[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {

@@ -7,21 +7,28 @@
 //
 // Work split (flash-decoding): workgroup (chunk, head block, query) takes up to
 // 64 heads of one query over one chunk of its selected ids; 4 waves own 16
-// heads each.  The chunk is walked in 32-token sub-chunks: the 32 gathered
-// latent rows (1 KiB each, one coalesced wave load per row) are prefetched into
-// registers one sub-chunk ahead, then staged in LDS and shared by the 4 waves.
+// heads each.  The chunk's ids are staged in LDS first; the chunk is then
+// walked in 32-token sub-chunks whose gathered latent rows (1 KiB each, one
+// coalesced wave load per row, every load unconditional: ids outside the
+// selection are redirected to a selected row and masked) are prefetched into
+// registers two sub-chunks ahead, staged in LDS and shared by the 4 waves.
 // Per sub-chunk and wave, on v_mfma_f32_16x16x32_bf16:
 //   S^T[32 tok x 16 heads] = C[32 x 512] . Q^T   (C from LDS, Q in registers)
 //   online softmax per head (log2 domain), O[16 x 512] rescaled in place
-//   O += P[16 x 32] . C[32 x 512]                (P straight from the S^T
-//        accumulator layout, C read per column from LDS)
+//   O += P[16 x 32] . C[32 x 512]
 // Computing S transposed lets the accumulator of QK^T serve as the A operand
 // of PV with no data movement: K index 8g+j of lane group g maps to token 4g+j
-// (j < 4) or 16+4g+j-4, the same permutation the PV B-operand reads use.
+// (j < 4) or 16+4g+j-4.  The PV B operand needs 8 tokens of one dimension per
+// lane; a lane reads 16 bytes (8 consecutive dims) of each of its 8 token rows
+// and regroups the halves into 8 B operands, so output tile e of dim group G
+// holds dims G*128 + 8c + e at lane column c, and each lane stores 8
+// consecutive dims at once.
 // fp8 latent rows are expanded to bf16 exactly on the way into LDS; the row
 // scale multiplies the logits and the probabilities instead of the data.
 // With more than one chunk, per-chunk (max, sum, unnormalised O) partials go
 // to the workspace and mla_combine_kernel merges them in chunk order.
+#include <limits.h>
+
 #include "dsa_device.hpp"
 #include "dsa_host.hpp"
 
@@ -34,6 +41,7 @@ constexpr int kSub = 32;                 // tokens per sub-chunk
 constexpr int kRowBytes = L * 2 + 16;    // LDS row stride: bf16 row + 16-byte pad
 constexpr int kTargetWG = 256;           // aim for one workgroup per CU
 constexpr int kMinSubPerChunk = 4;       // >= 128 ids per chunk keeps partials small
+constexpr int kMaxTch = 2048;            // ids per chunk staged in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -49,12 +57,21 @@ Chunking mla_chunking(int Q, int Hm, int out_width) {
   long long want = (kTargetWG + base - 1) / base;
   const int max_chunks = nsub / kMinSubPerChunk > 1 ? nsub / kMinSubPerChunk : 1;
   if (want > max_chunks) want = max_chunks;
+  const int min_chunks = (nsub * kSub + kMaxTch - 1) / kMaxTch;
+  if (want < min_chunks) want = min_chunks;
   if (want < 1) want = 1;
   const int spc = (int)((nsub + want - 1) / want);
   return {(nsub + spc - 1) / spc, spc * kSub};
 }
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *(const uint4*)p; }
+
+__device__ __forceinline__ uint32_t lo_pair(uint32_t x, uint32_t y) {
+  return (x & 0xffffu) | (y << 16);
+}
+__device__ __forceinline__ uint32_t hi_pair(uint32_t x, uint32_t y) {
+  return (x >> 16) | (y & 0xffff0000u);
+}
 
 template <bool FP8>
 __global__ __launch_bounds__(256) void sparse_mla_kernel(
@@ -64,9 +81,11 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
     int tch, float sm_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_c[kSub * kRowBytes];
-  __shared__ float s_mul[kSub];  // logit multiplier per token: sm_scale*log2e*row scale
-  __shared__ float s_scl[kSub];  // row scale (1 for bf16)
+  __shared__ int s_id[kMaxTch];      // selected id per chunk position, -1 if none
+  __shared__ float s_mul[kSub];      // logit multiplier per token: sm_scale*log2e*row scale
+  __shared__ float s_scl[kSub];      // row scale (1 for bf16)
   __shared__ int s_ok[kSub];
+  __shared__ int s_safe;             // some selected id of this chunk, or -1
 
   const int chunk = blockIdx.x, nchunks = gridDim.x, hb = blockIdx.y, qx = blockIdx.z;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -79,19 +98,34 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
   const int nsub = j1 > j0 ? (j1 - j0 + kSub - 1) / kSub : 0;
   const int32_t* trow = tok + (int64_t)qx * out_width;
 
-  // Q as the B operand of S^T = C Q^T: lane holds Q[head0+col][kk*32 + grp*8 + j].
+  // Stage the chunk's ids (one round trip) while the Q operand loads.
+  if (t == 0) s_safe = -1;
   const int hq = head0 + col;
   bf16x8_t qb[16];
   {
-    const uint16_t* qrow = q + ((int64_t)qx * Hm + (hq < Hm ? hq : 0)) * L + grp * 8;
+    const uint16_t* qrow = q + ((int64_t)qx * Hm + (hq < Hm ? hq : Hm - 1)) * L + grp * 8;
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk)
-      qb[kk] = as_bf16x8(hq < Hm ? ldg16(qrow + kk * 32) : make_uint4(0, 0, 0, 0));
+    for (int kk = 0; kk < 16; ++kk) {
+      const uint4 v = ldg16(qrow + kk * 32);
+      qb[kk] = as_bf16x8(hq < Hm ? v : make_uint4(0, 0, 0, 0));
+    }
   }
+  __syncthreads();
+  for (int i = t; i < nsub * kSub; i += 256) {
+    const int j = j0 + i;
+    const int id = trow[j < j1 ? j : j1 - 1];
+    const int v = j < j1 ? id : -1;
+    s_id[i] = v;
+    if (v >= 0) atomicMax(&s_safe, v);
+  }
+  __syncthreads();
+  const int safe = s_safe;
 
-  f32x4_t o[32];
+  f32x4_t o[4][8];  // [dim group G][tile e]: O[head grp*4+i][G*128 + 8*col + e]
 #pragma unroll
-  for (int nt = 0; nt < 32; ++nt) o[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int G = 0; G < 4; ++G)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[G][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
   // Gather mapping: bf16 rows are 64 x 16 B (one wave per row, 8 rows per
@@ -100,42 +134,31 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
   constexpr int kColU = FP8 ? 32 : 64;
   const int prow0 = t / kColU, pcu = t % kColU;
   constexpr int kRowStep = 256 / kColU;
-  uint4 pre[NPRE];
-  float pre_scl = 1.f;
-  int pre_ok = 0;
+  uint4 pre0[NPRE], pre1[NPRE];
 
-  auto gather = [&](int s) {
-    const int jb = j0 + s * kSub;
+  auto gather = [&](int s, uint4 (&dst)[NPRE]) {
 #pragma unroll
     for (int i = 0; i < NPRE; ++i) {
-      const int row = prow0 + i * kRowStep;
-      const int j = jb + row;
-      const int id = j < j1 ? trow[j] : -1;
-      if (id >= 0) {
-        const int64_t g = rowbase + id;
-        pre[i] = FP8 ? ldg16((const uint8_t*)ckv_v + g * L + pcu * 16)
-                     : ldg16((const uint16_t*)ckv_v + g * L + pcu * 8);
-      } else {
-        pre[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-    if (t < kSub) {
-      const int j = jb + t;
-      const int id = j < j1 ? trow[j] : -1;
-      pre_ok = id >= 0;
-      pre_scl = (FP8 && id >= 0) ? ckv_scale[rowbase + id] : 1.f;
+      const int id = s_id[s * kSub + prow0 + i * kRowStep];
+      const int64_t g = rowbase + (id >= 0 ? id : safe);
+      dst[i] = FP8 ? ldg16((const uint8_t*)ckv_v + g * L + pcu * 16)
+                   : ldg16((const uint16_t*)ckv_v + g * L + pcu * 8);
     }
   };
 
-  if (nsub > 0) gather(0);
-  for (int s = 0; s < nsub; ++s) {
+  const int nwork = safe >= 0 ? nsub : 0;  // a chunk with no selected id has no work
+  if (nwork > 0) gather(0, pre0);
+  if (nwork > 1) gather(1, pre1);
+
+  // One sub-chunk; `cur` names one of the two prefetch buffers statically.
+  auto step = [&](int s, uint4 (&cur)[NPRE]) {
     __syncthreads();  // every wave is done with the previous sub-chunk
 #pragma unroll
     for (int i = 0; i < NPRE; ++i) {
       const int row = prow0 + i * kRowStep;
       if (FP8) {
-        const uint4 v = pre[i];
-        uint32_t w8[4] = {v.x, v.y, v.z, v.w};
+        const uint4 v = cur[i];
+        const uint32_t w8[4] = {v.x, v.y, v.z, v.w};
         uint32_t o16[8];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -150,26 +173,30 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
         dst[0] = make_uint4(o16[0], o16[1], o16[2], o16[3]);
         dst[1] = make_uint4(o16[4], o16[5], o16[6], o16[7]);
       } else {
-        *(uint4*)(lds_c + row * kRowBytes + pcu * 16) = pre[i];
+        *(uint4*)(lds_c + row * kRowBytes + pcu * 16) = cur[i];
       }
     }
     if (t < kSub) {
-      s_ok[t] = pre_ok;
-      s_scl[t] = pre_scl;
-      s_mul[t] = sm_log2 * pre_scl;
+      const int id = s_id[s * kSub + t];
+      const float scl = FP8 ? ckv_scale[rowbase + (id >= 0 ? id : safe)] : 1.f;
+      s_ok[t] = id >= 0;
+      s_scl[t] = scl;
+      s_mul[t] = sm_log2 * scl;
     }
     __syncthreads();
-    if (s + 1 < nsub) gather(s + 1);  // next rows load while this sub-chunk computes
+    if (s + 2 < nwork) gather(s + 2, cur);  // rows two sub-chunks ahead load meanwhile
 
     // S^T tiles: tokens tt*16 + (0..15) x the wave's 16 heads.
     f32x4_t sacc[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      sacc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const uint8_t* arow = lds_c + (tt * 16 + col) * kRowBytes + grp * 16;
+      uint4 av[16];
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk)
-        sacc[tt] = mfma16x16x32(as_bf16x8(*(const uint4*)(arow + kk * 64)), qb[kk], sacc[tt]);
+      for (int kk = 0; kk < 16; ++kk) av[kk] = *(const uint4*)(arow + kk * 64);
+      sacc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) sacc[tt] = mfma16x16x32(as_bf16x8(av[kk]), qb[kk], sacc[tt]);
     }
     // lane holds S^T[token tt*16 + grp*4 + i][head col]
     float x[8];
@@ -205,9 +232,11 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, grp * 4 + i, kWave);
 #pragma unroll
-    for (int nt = 0; nt < 32; ++nt)
+    for (int G = 0; G < 4; ++G)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[nt][i] *= ai[i];
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[G][e][i] *= ai[i];
 
     // P as the A operand of O = P C: lane holds P[head col][K = grp*8 + k].
     uint32_t pw[4];
@@ -223,41 +252,54 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
     }
     const bf16x8_t pa = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
 
-    // B operand: C[token(K)][dim nt*16 + col], tokens grp*4+0..3 and 16+grp*4+0..3.
-    const uint8_t* r0 = lds_c + (grp * 4) * kRowBytes + col * 2;
-    const uint8_t* r1 = lds_c + (16 + grp * 4) * kRowBytes + col * 2;
+    // B operands: token rows grp*4+0..3 and 16+grp*4+0..3 (K order), 8 dims
+    // G*128 + 8*col .. +7 per 16-byte read.
+    const uint8_t* r0 = lds_c + (grp * 4) * kRowBytes + col * 16;
+    const uint8_t* r1 = lds_c + (16 + grp * 4) * kRowBytes + col * 16;
 #pragma unroll
-    for (int nt = 0; nt < 32; ++nt) {
-      const int cb = nt * 32;
-      const uint32_t v0 = *(const uint16_t*)(r0 + cb);
-      const uint32_t v1 = *(const uint16_t*)(r0 + kRowBytes + cb);
-      const uint32_t v2 = *(const uint16_t*)(r0 + 2 * kRowBytes + cb);
-      const uint32_t v3 = *(const uint16_t*)(r0 + 3 * kRowBytes + cb);
-      const uint32_t v4 = *(const uint16_t*)(r1 + cb);
-      const uint32_t v5 = *(const uint16_t*)(r1 + kRowBytes + cb);
-      const uint32_t v6 = *(const uint16_t*)(r1 + 2 * kRowBytes + cb);
-      const uint32_t v7 = *(const uint16_t*)(r1 + 3 * kRowBytes + cb);
-      const bf16x8_t bv =
-          as_bf16x8(make_uint4(v0 | (v1 << 16), v2 | (v3 << 16), v4 | (v5 << 16), v6 | (v7 << 16)));
-      o[nt] = mfma16x16x32(pa, bv, o[nt]);
+    for (int G = 0; G < 4; ++G) {
+      uint4 u[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u[j] = *(const uint4*)(r0 + j * kRowBytes + G * 256);
+        u[4 + j] = *(const uint4*)(r1 + j * kRowBytes + G * 256);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int wd = e >> 1;
+        uint32_t bw[4];
+#pragma unroll
+        for (int m2 = 0; m2 < 4; ++m2) {
+          const uint32_t a0 = u4_word(u[2 * m2], wd), a1 = u4_word(u[2 * m2 + 1], wd);
+          bw[m2] = (e & 1) ? hi_pair(a0, a1) : lo_pair(a0, a1);
+        }
+        o[G][e] = mfma16x16x32(pa, as_bf16x8(make_uint4(bw[0], bw[1], bw[2], bw[3])), o[G][e]);
+      }
     }
+  };
+  for (int s = 0; s < nwork; s += 2) {
+    step(s, pre0);
+    if (s + 1 < nwork) step(s + 1, pre1);
   }
 
-  float li[4], mi[4];
+  float li[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    li[i] = __shfl(l_run, grp * 4 + i, kWave);
-    mi[i] = __shfl(m_run, grp * 4 + i, kWave);
-  }
+  for (int i = 0; i < 4; ++i) li[i] = __shfl(l_run, grp * 4 + i, kWave);
   if (nchunks == 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = head0 + grp * 4 + i;
       if (h >= Hm) continue;
       const float inv = li[i] > 0.f ? 1.f / li[i] : 0.f;
-      uint16_t* orow = out + ((int64_t)qx * Hm + h) * L + col;
+      uint16_t* orow = out + ((int64_t)qx * Hm + h) * L + col * 8;
 #pragma unroll
-      for (int nt = 0; nt < 32; ++nt) orow[nt * 16] = (uint16_t)f32_to_bf16_rne(o[nt][i] * inv);
+      for (int G = 0; G < 4; ++G) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          pk[e >> 1] = f32_to_bf16_rne(o[G][e][i] * inv) | (f32_to_bf16_rne(o[G][e + 1][i] * inv) << 16);
+        *(uint4*)(orow + G * 128) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      }
     }
     if (lse && grp == 0 && hq < Hm)
       lse[(int64_t)qx * Hm + hq] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
@@ -267,37 +309,43 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
     for (int i = 0; i < 4; ++i) {
       const int h = head0 + grp * 4 + i;
       if (h >= Hm) continue;
-      float* prow = part_o + (pbase + h) * L + col;
+      float* prow = part_o + (pbase + h) * L + col * 8;
 #pragma unroll
-      for (int nt = 0; nt < 32; ++nt) prow[nt * 16] = o[nt][i];
+      for (int G = 0; G < 4; ++G) {
+        float4* d4 = (float4*)(prow + G * 128);
+        d4[0] = make_float4(o[G][0][i], o[G][1][i], o[G][2][i], o[G][3][i]);
+        d4[1] = make_float4(o[G][4][i], o[G][5][i], o[G][6][i], o[G][7][i]);
+      }
     }
     if (grp == 0 && hq < Hm) {
       part_ml[(pbase + hq) * 2] = m_run;
       part_ml[(pbase + hq) * 2 + 1] = l_run;
     }
   }
-  (void)mi;
 }
 
-// Merge the per-chunk partials of one (query, head) in chunk order.
-__global__ __launch_bounds__(64) void mla_combine_kernel(const float* __restrict__ part_o,
-                                                         const float* __restrict__ part_ml,
-                                                         int nchunks, int Hm,
-                                                         uint16_t* __restrict__ out,
-                                                         float* __restrict__ lse) {
-  const int h = blockIdx.x, qx = blockIdx.y, lane = threadIdx.x;
+// Merge the per-chunk partials of one (query, head) in chunk order; a wave per
+// head, 8 dims per lane, four heads per workgroup.
+__global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ part_o,
+                                                          const float* __restrict__ part_ml,
+                                                          int nchunks, int Hm,
+                                                          uint16_t* __restrict__ out,
+                                                          float* __restrict__ lse) {
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 6), qx = blockIdx.y, lane = threadIdx.x & 63;
+  if (h >= Hm) return;
   const int64_t b0 = (int64_t)qx * nchunks * Hm + h;
   float M = -INFINITY;
   for (int c = 0; c < nchunks; ++c) M = fmaxf(M, part_ml[(b0 + (int64_t)c * Hm) * 2]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
+#pragma unroll 4
   for (int c = 0; c < nchunks; ++c) {
     const int64_t pc = b0 + (int64_t)c * Hm;
     const float m = part_ml[pc * 2], l = part_ml[pc * 2 + 1];
-    const float wgt = (M == -INFINITY) ? 0.f : exp2f(m - M);
-    lsum = fmaf(l, wgt, lsum);
     const float4* src = (const float4*)(part_o + pc * L + lane * 8);
     const float4 u = src[0], v = src[1];
+    const float wgt = (M == -INFINITY) ? 0.f : exp2f(m - M);
+    lsum = fmaf(l, wgt, lsum);
     acc[0] = fmaf(wgt, u.x, acc[0]);
     acc[1] = fmaf(wgt, u.y, acc[1]);
     acc[2] = fmaf(wgt, u.z, acc[2]);
@@ -373,6 +421,6 @@ DSA_EXPORT dsa_status dsa_sparse_mla_decode(const uint16_t* q, const void* ckv,
                                                        part_o, part_ml);
   dsa_status st = dsa::check_launch("dsa_sparse_mla_decode");
   if (st != DSA_OK || ch.nchunks == 1) return st;
-  mla_combine_kernel<<<dim3(Hm, Q), 64, 0, stream>>>(part_o, part_ml, ch.nchunks, Hm, out, lse);
+  mla_combine_kernel<<<dim3((Hm + 3) / 4, Q), 256, 0, stream>>>(part_o, part_ml, ch.nchunks, Hm, out, lse);
   return dsa::check_launch("dsa_sparse_mla_decode (combine)");
 }

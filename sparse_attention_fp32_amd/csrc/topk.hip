@@ -61,16 +61,22 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   const uint8_t* crow = cand + (int64_t)q * pstride;
   int32_t* out = sel + (int64_t)q * select_k;
 
+  // all loads issued together (ids clamped into the row), then masked
   uint32_t key[E];
+  float sv[E];
+  uint8_t cv[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int id = min(t * E + e, pstride - 1);
+    sv[e] = srow[id];
+    cv[e] = crow[id];
+  }
   int nc = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int id = t * E + e;
-    key[e] = 0u;
-    if (id < pstride && crow[id]) {
-      key[e] = float_order_key(srow[id]);
-      ++nc;
-    }
+    const bool c = t * E + e < pstride && cv[e] != 0;
+    key[e] = c ? float_order_key(sv[e]) : 0u;
+    nc += c;
   }
   int ncand;
   (void)block_exclusive_scan(nc, s_wave, &ncand);

@@ -5,7 +5,10 @@
 * head-gate: max |diff| <= 1e-5 (fp32 with another summation order; the split-K
   head-gate of stkernel PR #227 measured 2.4e-6);
 * pooled keys: at most 1 bf16 ulp apart (fp32 vs fp64 arithmetic before the one
-  rounding to bf16);
+  rounding to bf16), or, for an output near zero where the LayerNorm's
+  (x - mean) * rstd * w + b cancels, within KEY_ABS_REL of the row's largest
+  |key|: the fp32 evaluation carries an absolute error of a few 2^-24 of the
+  row's scale, which is many ulps of a tiny value;
 * scores: |diff| <= 1e-5 * max |score| of the row, -inf exactly where the
   oracle has it;
 * MLA output: per (query, head) row, max |O - O_ref| / max |O_ref| <= 2e-2
@@ -18,6 +21,7 @@ import numpy as np
 import oracle as O
 
 GATE_TOL = 1e-5
+KEY_ABS_REL = 2.0 ** -18
 SCORE_REL = 1e-5
 MLA_REL = 2e-2
 LSE_ABS = 1e-3
@@ -54,8 +58,16 @@ def check_compress(g, ref, requests=None, pool_off=None):
         idx = np.concatenate([np.arange(pool_off[r], pool_off[r + 1]) for r in requests])
     assert np.array_equal(g["pool_start"][idx], ref["pool_start"][idx]), "pool_start"
     assert np.array_equal(g["pool_valid"][idx], ref["pool_valid"][idx]), "pool_valid"
-    u = bf16_ulp_diff(g["keys"][idx], ref["keys"][idx])
-    assert u.max(initial=0) <= 1, f"keys differ by {u.max()} bf16 ulps"
+    kg, kr = g["keys"][idx], ref["keys"][idx]
+    u = bf16_ulp_diff(kg, kr)
+    if u.max(initial=0) > 1:
+        fg, fr = O.bf16_bits_to_f64(kg), O.bf16_bits_to_f64(kr)
+        scale = np.abs(fr).max(axis=1, keepdims=True)
+        far = (u > 1) & (np.abs(fg - fr) > KEY_ABS_REL * scale)
+        i, j = np.unravel_index(np.argmax(u), u.shape)
+        print(f"[keys] {int((u > 1).sum())} elements > 1 ulp; worst {int(u[i, j])} ulps: "
+              f"gpu {fg[i, j]:.6g} ref {fr[i, j]:.6g} row max {scale[i, 0]:.4g}")
+        assert not far.any(), f"{int(far.sum())} key elements beyond 1 ulp and {KEY_ABS_REL:.2g} of the row"
     return int((u > 0).sum())
 
 

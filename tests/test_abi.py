@@ -39,10 +39,8 @@ def test_head_gate_errors():
     assert L.dsa_head_gate(FAKE, FAKE, FAKE, 4, 0, 16, NUL, 0, NUL) == INV
     assert L.dsa_head_gate(FAKE, FAKE, FAKE, -1, 16, 16, NUL, 0, NUL) == INV
     assert L.dsa_head_gate(NUL, FAKE, FAKE, 4, 4096, 16, FAKE, 1 << 20, NUL) == INV
-    # workspace too small for the split path
-    need = dsa.head_gate_workspace_size(16, 4096, 16)
-    assert need > 0
-    assert L.dsa_head_gate(FAKE, FAKE, FAKE, 16, 4096, 16, FAKE, need - 1, NUL) == INV
+    # no workspace is needed on either path
+    assert dsa.head_gate_workspace_size(16, 4096, 16) == 0
     assert dsa.head_gate_workspace_size(4096, 4096, 16) == 0
     assert L.dsa_head_gate(FAKE, FAKE, FAKE, 0, 4096, 16, NUL, 0, NUL) == dsa.DSA_OK  # no-op
 
