@@ -139,7 +139,19 @@ def main():
     ap.add_argument("--sets", type=int, default=8)
     ap.add_argument("--stage-reps", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     a = ap.parse_args()
+    if a.calibrate_copy:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}))
+        return
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus": a.gpus}))

@@ -26,6 +26,8 @@ constexpr int kRowThreads = 1024;
 constexpr int kPerThread = 4;  // K elements per thread per pass (row path)
 
 // One workgroup per output row m (M <= 16).  Thread t takes k = t + 1024*i.
+// N16: W rows are exactly 16 floats (four 16-byte loads per row).
+template <bool N16>
 __global__ __launch_bounds__(kRowThreads) void head_gate_row_kernel(const float* __restrict__ hidden,
                                                                     const float* __restrict__ W,
                                                                     float* __restrict__ w, int K,
@@ -44,7 +46,7 @@ __global__ __launch_bounds__(kRowThreads) void head_gate_row_kernel(const float*
       const int k = k0 + t + kRowThreads * i;
       const int kc = k < K ? k : K - 1;  // clamped: every load is in bounds
       h[i] = hrow[kc];
-      if (N == 16) {
+      if (N16) {
         const float4* wp = (const float4*)(W + (size_t)kc * 16);
 #pragma unroll
         for (int c = 0; c < 4; ++c) wr[i][c] = wp[c];
@@ -177,7 +179,10 @@ DSA_EXPORT dsa_status dsa_head_gate(const float* hidden, const float* W, float* 
   DSA_REQUIRE(hidden && W && w, DSA_ERR_INVALID_ARG, "dsa_head_gate: NULL tensor pointer");
   if (dsa::trace_enabled()) fprintf(stderr, "[dsa] head_gate M=%d K=%d N=%d\n", M, K, N);
   if (M <= kRows)
-    head_gate_row_kernel<<<M, kRowThreads, 0, stream>>>(hidden, W, w, K, N);
+    if (N == 16)
+      head_gate_row_kernel<true><<<M, kRowThreads, 0, stream>>>(hidden, W, w, K, N);
+    else
+      head_gate_row_kernel<false><<<M, kRowThreads, 0, stream>>>(hidden, W, w, K, N);
   else
     head_gate_rows_kernel<<<(M + kRows - 1) / kRows, 256, 0, stream>>>(hidden, W, w, M, K, N);
   return dsa::check_launch("dsa_head_gate");

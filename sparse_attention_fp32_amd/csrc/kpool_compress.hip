@@ -49,16 +49,17 @@ __device__ int first_valid_row(const uint8_t* __restrict__ valid, int64_t row0, 
   return f == INT_MAX ? -1 : f;
 }
 
-template <int LPP>  // lanes per pool = D / 8
+template <int LPP, int KP>  // lanes per pool = D / 8; pool slots
 __global__ __launch_bounds__(256) void kpool_compress_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ gate,
     const uint16_t* __restrict__ ape, const uint8_t* __restrict__ valid,
     const int32_t* __restrict__ tok_off, const int32_t* __restrict__ pool_off,
-    const float* __restrict__ ln_w, const float* __restrict__ ln_b, float eps, int kpool,
+    const float* __restrict__ ln_w, const float* __restrict__ ln_b, float eps,
     const int32_t* __restrict__ new_from, int pools_per_wg, uint16_t* __restrict__ keys,
     int32_t* __restrict__ pool_start, uint8_t* __restrict__ pool_valid,
     int32_t* __restrict__ n_pools) {
   constexpr int D = LPP * 8;
+  constexpr int kpool = KP;
   constexpr int kGroups = 256 / LPP;  // pools in flight per workgroup
   __shared__ int s_first;
   const int r = blockIdx.y;
@@ -96,10 +97,10 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
     lw[c] = ln_w[c0 + c];
     lb[c] = ln_b[c0 + c];
   }
-  uint4 ap[DSA_MAX_KPOOL];
+  uint4 ap[KP];
 #pragma unroll
-  for (int s = 0; s < DSA_MAX_KPOOL; ++s)
-    ap[s] = *(const uint4*)(ape + (s < kpool ? s : kpool - 1) * D + c0);
+  for (int s = 0; s < KP; ++s)
+    ap[s] = *(const uint4*)(ape + s * D + c0);
 
   for (int p = s0 + grp; p < s1; p += kGroups) {
     uint16_t* kout = keys + (pbase + p) * D + c0;
@@ -112,27 +113,27 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
       continue;
     }
     const int64_t rb = row0 + f + (int64_t)p * kpool;
-    // every slot load is issued at once; slots past kpool re-read the last row
-    uint4 kr[DSA_MAX_KPOOL], gr[DSA_MAX_KPOOL];
-    uint8_t vb[DSA_MAX_KPOOL];
+    // every slot load is issued at once
+    uint4 kr[KP], gr[KP];
+    uint8_t vb[KP];
 #pragma unroll
-    for (int s = 0; s < DSA_MAX_KPOOL; ++s) {
-      const int64_t row = rb + (s < kpool ? s : kpool - 1);
+    for (int s = 0; s < KP; ++s) {
+      const int64_t row = rb + s;
       kr[s] = *(const uint4*)(k + row * D + c0);
       gr[s] = *(const uint4*)(gate + row * D + c0);
       vb[s] = valid[row];
     }
     int allv = 1;
 #pragma unroll
-    for (int s = 0; s < DSA_MAX_KPOOL; ++s) allv &= vb[s] != 0;
+    for (int s = 0; s < KP; ++s) allv &= vb[s] != 0;
     float x[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int word = c >> 1, sh = (c & 1) * 16;
-      float g[DSA_MAX_KPOOL];
+      float g[KP];
       float m = -INFINITY;
 #pragma unroll
-      for (int s = 0; s < DSA_MAX_KPOOL; ++s) {
+      for (int s = 0; s < KP; ++s) {
         if (s < kpool) {
           const uint32_t gw = u4_word(gr[s], word), aw = u4_word(ap[s], word);
           g[s] = bf16_to_f32((gw >> sh) & 0xffffu) + bf16_to_f32((aw >> sh) & 0xffffu);
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
       }
       float z = 0.f, acc = 0.f;
 #pragma unroll
-      for (int s = 0; s < DSA_MAX_KPOOL; ++s) {
+      for (int s = 0; s < KP; ++s) {
         if (s < kpool) {
           const float e = expf(g[s] - m);
           z += e;
@@ -220,16 +221,28 @@ DSA_EXPORT dsa_status dsa_kpool_compress(const uint16_t* k, const uint16_t* gate
   if (dsa::trace_enabled())
     fprintf(stderr, "[dsa] kpool_compress B=%d D=%d kpool=%d max_cap=%d inc=%d grid=(%d,%d)\n",
             B, D, kpool, max_cap, new_from != nullptr, grid.x, grid.y);
-#define DSA_LAUNCH_KP(LPP)                                                                     \
-  kpool_compress_kernel<LPP><<<grid, 256, 0, stream>>>(k, gate, ape, valid, tok_off, pool_off, \
-                                                       ln_w, ln_b, eps, kpool, new_from, ppw,  \
-                                                       keys, pool_start, pool_valid, n_pools)
-  switch (lpp) {
-    case 4: DSA_LAUNCH_KP(4); break;
-    case 8: DSA_LAUNCH_KP(8); break;
-    case 16: DSA_LAUNCH_KP(16); break;
-    default: DSA_LAUNCH_KP(32); break;
+#define DSA_LAUNCH_KP(LPP, KP)                                                            \
+  kpool_compress_kernel<LPP, KP><<<grid, 256, 0, stream>>>(                                \
+      k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b, eps, new_from, ppw, keys, pool_start, \
+      pool_valid, n_pools)
+#define DSA_LAUNCH_KP_D(KP)            \
+  switch (lpp) {                       \
+    case 4: DSA_LAUNCH_KP(4, KP); break;   \
+    case 8: DSA_LAUNCH_KP(8, KP); break;   \
+    case 16: DSA_LAUNCH_KP(16, KP); break; \
+    default: DSA_LAUNCH_KP(32, KP); break; \
   }
+  switch (kpool) {
+    case 1: DSA_LAUNCH_KP_D(1); break;
+    case 2: DSA_LAUNCH_KP_D(2); break;
+    case 3: DSA_LAUNCH_KP_D(3); break;
+    case 4: DSA_LAUNCH_KP_D(4); break;
+    case 5: DSA_LAUNCH_KP_D(5); break;
+    case 6: DSA_LAUNCH_KP_D(6); break;
+    case 7: DSA_LAUNCH_KP_D(7); break;
+    default: DSA_LAUNCH_KP_D(8); break;
+  }
+#undef DSA_LAUNCH_KP_D
 #undef DSA_LAUNCH_KP
   return dsa::check_launch("dsa_kpool_compress");
 }

@@ -11,10 +11,10 @@
 // walked in 32-token sub-chunks whose gathered latent rows (1 KiB each, one
 // coalesced wave load per row, every load unconditional: ids outside the
 // selection are redirected to a selected row and masked) are prefetched into
-// registers two sub-chunks ahead, staged in LDS and shared by the 4 waves.
+// registers one sub-chunk ahead, staged in LDS and shared by the 4 waves.
 // Per sub-chunk and wave, on v_mfma_f32_16x16x32_bf16:
 //   S^T[32 tok x 16 heads] = C[32 x 512] . Q^T   (C from LDS, Q in registers)
-//   online softmax per head (log2 domain), O[16 x 512] rescaled in place
+//   online softmax per head (log2 domain) with a lazily moved reference max
 //   O += P[16 x 32] . C[32 x 512]
 // Computing S transposed lets the accumulator of QK^T serve as the A operand
 // of PV with no data movement: K index 8g+j of lane group g maps to token 4g+j
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
   constexpr int kColU = FP8 ? 32 : 64;
   const int prow0 = t / kColU, pcu = t % kColU;
   constexpr int kRowStep = 256 / kColU;
-  uint4 pre0[NPRE], pre1[NPRE];
+  uint4 pre0[NPRE];
 
   auto gather = [&](int s, uint4 (&dst)[NPRE]) {
 #pragma unroll
@@ -148,9 +148,8 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
 
   const int nwork = safe >= 0 ? nsub : 0;  // a chunk with no selected id has no work
   if (nwork > 0) gather(0, pre0);
-  if (nwork > 1) gather(1, pre1);
 
-  // One sub-chunk; `cur` names one of the two prefetch buffers statically.
+  // One sub-chunk: stage the prefetched rows, start the next gather, compute.
   auto step = [&](int s, uint4 (&cur)[NPRE]) {
     __syncthreads();  // every wave is done with the previous sub-chunk
 #pragma unroll
@@ -184,19 +183,23 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
       s_mul[t] = sm_log2 * scl;
     }
     __syncthreads();
-    if (s + 2 < nwork) gather(s + 2, cur);  // rows two sub-chunks ahead load meanwhile
+    if (s + 1 < nwork) gather(s + 1, cur);  // the next rows load meanwhile
 
     // S^T tiles: tokens tt*16 + (0..15) x the wave's 16 heads.
     f32x4_t sacc[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const uint8_t* arow = lds_c + (tt * 16 + col) * kRowBytes + grp * 16;
-      uint4 av[16];
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk) av[kk] = *(const uint4*)(arow + kk * 64);
       sacc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk) sacc[tt] = mfma16x16x32(as_bf16x8(av[kk]), qb[kk], sacc[tt]);
+      for (int half = 0; half < 2; ++half) {
+        uint4 av[8];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) av[kk] = *(const uint4*)(arow + (half * 8 + kk) * 64);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+          sacc[tt] = mfma16x16x32(as_bf16x8(av[kk]), qb[half * 8 + kk], sacc[tt]);
+      }
     }
     // lane holds S^T[token tt*16 + grp*4 + i][head col]
     float x[8];
@@ -212,31 +215,38 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
       }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-    const float m_new = fmaxf(m_run, mloc);
-    const bool none = m_new == -INFINITY;
-    const float alpha = none ? 1.f : exp2f(m_run - m_new);
+    // Lazy rescaling: a head's reference max m_run moves only when this
+    // sub-chunk's max exceeds it by more than 8 (log2 units), so P stays below
+    // 2^8 and O is rescaled only on the rare step that moves a reference.
+    const bool move = mloc > m_run + 8.f;
+    if (__any(move)) {
+      const float alpha = move ? exp2f(m_run - mloc) : 1.f;  // exp2(-inf) = 0
+      const bool live = __any(move && m_run != -INFINITY);     // O holds data to rescale
+      if (move) m_run = mloc;
+      l_run *= alpha;
+      if (live) {
+        float ai[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, grp * 4 + i, kWave);
+#pragma unroll
+        for (int G = 0; G < 4; ++G)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[G][e][i] *= ai[i];
+      }
+    }
+    const bool none = m_run == -INFINITY;
     float p[8];
     float psum = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      p[k] = none ? 0.f : exp2f(x[k] - m_new);
+      p[k] = none ? 0.f : exp2f(x[k] - m_run);
       psum += p[k];
     }
     psum += __shfl_xor(psum, 16, kWave);
     psum += __shfl_xor(psum, 32, kWave);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-
-    // O rows are heads grp*4+i; their alpha lives in lane grp*4+i.
-    float ai[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, grp * 4 + i, kWave);
-#pragma unroll
-    for (int G = 0; G < 4; ++G)
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[G][e][i] *= ai[i];
+    l_run += psum;
 
     // P as the A operand of O = P C: lane holds P[head col][K = grp*8 + k].
     uint32_t pw[4];
@@ -277,10 +287,7 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
       }
     }
   };
-  for (int s = 0; s < nwork; s += 2) {
-    step(s, pre0);
-    if (s + 1 < nwork) step(s + 1, pre1);
-  }
+  for (int s = 0; s < nwork; ++s) step(s, pre0);
 
   float li[4];
 #pragma unroll
