@@ -51,9 +51,109 @@ __device__ __forceinline__ uint32_t float_order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ float wave_sum_xor(float v, int width_mask) {
-  // butterfly over lanes l ^ 1, 2, 4, ... up to width_mask (a power of two - 1)
-  for (int o = 1; o <= width_mask; o <<= 1) v += __shfl_xor(v, o, kWave);
+// ---- cross-lane primitives at ALU latency (DPP and gfx950 permlane swaps) ----
+// Lane l of v_permlane32_swap(x, x) receives {x[l % 32], x[l % 32 + 32]};
+// lane l of v_permlane16_swap(x, x) receives {x[even row], x[odd row]} of its
+// pair of 16-lane rows.  Combining the two halves in that fixed order gives
+// bit-identical results in both lanes of each pair.
+
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND_ZERO = true>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, BOUND_ZERO);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // i <-> 7-i within 8 lanes
+constexpr int kDppMirror = 0x140;     // i <-> 15-i within 16 lanes
+
+// (x[lo], x[hi]) of the lane pairs l, l^16 and l, l^32.
+__device__ __forceinline__ void pair16(float v, float& lo, float& hi) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  lo = __uint_as_float(p[0]);
+  hi = __uint_as_float(p[1]);
+}
+__device__ __forceinline__ void pair32(float v, float& lo, float& hi) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  lo = __uint_as_float(p[0]);
+  hi = __uint_as_float(p[1]);
+}
+// Value held by lane l ^ 16 / l ^ 32.
+__device__ __forceinline__ float xor16(float v) {
+  float lo, hi;
+  pair16(v, lo, hi);
+  return ((threadIdx.x >> 4) & 1) ? lo : hi;
+}
+__device__ __forceinline__ float xor32(float v) {
+  float lo, hi;
+  pair32(v, lo, hi);
+  return ((threadIdx.x >> 5) & 1) ? lo : hi;
+}
+__device__ __forceinline__ int xor16_i(int v) {
+  const auto p = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  return (int)(((threadIdx.x >> 4) & 1) ? p[0] : p[1]);
+}
+__device__ __forceinline__ int xor32_i(int v) {
+  const auto p = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  return (int)(((threadIdx.x >> 5) & 1) ? p[0] : p[1]);
+}
+// Sum / max over the four 16-lane rows (lanes with the same l % 16).
+__device__ __forceinline__ float rows_sum(float v) {
+  float lo, hi;
+  pair16(v, lo, hi);
+  v = lo + hi;
+  pair32(v, lo, hi);
+  return lo + hi;
+}
+__device__ __forceinline__ float rows_max(float v) {
+  float lo, hi;
+  pair16(v, lo, hi);
+  v = fmaxf(lo, hi);
+  pair32(v, lo, hi);
+  return fmaxf(lo, hi);
+}
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_i<0x111>(x);                 // row_shr:1
+  x += dpp_i<0x112>(x);                 // row_shr:2
+  x += dpp_i<0x114>(x);                 // row_shr:4
+  x += dpp_i<0x118>(x);                 // row_shr:8
+  x += dpp_i<0x142, 0xA, false>(x);     // row_bcast:15 into rows 1 and 3
+  x += dpp_i<0x143, 0xC, false>(x);     // row_bcast:31 into rows 2 and 3
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)dpp_i<kDppXor1>((int)x));
+  x = max(x, (uint32_t)dpp_i<kDppXor2>((int)x));
+  x = max(x, (uint32_t)dpp_i<kDppHalfMirror>((int)x));
+  x = max(x, (uint32_t)dpp_i<kDppMirror>((int)x));
+  const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = max((uint32_t)p[0], (uint32_t)p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max((uint32_t)q[0], (uint32_t)q[1]);
+}
+
+// Sum over aligned groups of W lanes (W a power of two), the same bits in
+// every lane of a group.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  if (W >= 2) v += dpp_f<kDppXor1>(v);
+  if (W >= 4) v += dpp_f<kDppXor2>(v);
+  if (W >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if (W >= 16) v += dpp_f<kDppMirror>(v);
+  if (W >= 32) {
+    float lo, hi;
+    pair16(v, lo, hi);
+    v = lo + hi;
+  }
+  if (W >= 64) {
+    float lo, hi;
+    pair32(v, lo, hi);
+    v = lo + hi;
+  }
   return v;
 }
 

@@ -6,7 +6,8 @@
 // each of the M rows gets a 1024-thread workgroup that issues all of its loads
 // at once (four 16-float rows of W and four hidden values per thread), keeps 16
 // running sums per thread, and reduces them in a fixed order: a
-// reduce-scatter over the wave (17 shuffles leave lane l with output j(l)),
+// reduce-scatter over the wave (17 ALU-latency lane exchanges leave lane l with
+// output j(l)),
 // then the 16 waves' sums added in wave order.  Deterministic, and the same
 // bits for a row whatever the batch.  Above 16 rows each workgroup owns 16 rows
 // and walks K through LDS tiles.
@@ -71,46 +72,35 @@ __global__ __launch_bounds__(kRowThreads) void head_gate_row_kernel(const float*
       }
     }
   }
-  // Reduce-scatter over the wave: after the xor-32/16/8/4 steps lane l holds
-  // the sum over 16 lanes of output j(l) = 8*b5 + 4*b4 + 2*b3 + b2 (bits of l);
-  // xor 2 and 1 finish the sum over all 64 lanes.
+  // Reduce-scatter over the wave: each step keeps half of the running outputs
+  // and adds the partner lane's copy of them (partners: l^32, l^16, then the
+  // row mirror i <-> 15-i and half mirror i <-> 7-i, which also flip bits 3
+  // and 2); lane l ends with output j(l) = 8*b5 + 4*b4 + 2*b3 + b2 summed over
+  // 16 lanes, and the xor-2 and xor-1 steps finish the sum over all 64.
   float v8[8], v4[4], v2[2];
   {
     const bool hi = (lane >> 5) & 1;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float send = hi ? acc[i] : acc[8 + i];
-      const float keep = hi ? acc[8 + i] : acc[i];
-      v8[i] = keep + __shfl_xor(send, 32, kWave);
-    }
+    for (int i = 0; i < 8; ++i) v8[i] = (hi ? acc[8 + i] : acc[i]) + xor32(hi ? acc[i] : acc[8 + i]);
   }
   {
     const bool hi = (lane >> 4) & 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float send = hi ? v8[i] : v8[4 + i];
-      const float keep = hi ? v8[4 + i] : v8[i];
-      v4[i] = keep + __shfl_xor(send, 16, kWave);
-    }
+    for (int i = 0; i < 4; ++i) v4[i] = (hi ? v8[4 + i] : v8[i]) + xor16(hi ? v8[i] : v8[4 + i]);
   }
   {
     const bool hi = (lane >> 3) & 1;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float send = hi ? v4[i] : v4[2 + i];
-      const float keep = hi ? v4[2 + i] : v4[i];
-      v2[i] = keep + __shfl_xor(send, 8, kWave);
-    }
+    for (int i = 0; i < 2; ++i)
+      v2[i] = (hi ? v4[2 + i] : v4[i]) + dpp_f<kDppMirror>(hi ? v4[i] : v4[2 + i]);
   }
   float v;
   {
     const bool hi = (lane >> 2) & 1;
-    const float send = hi ? v2[0] : v2[1];
-    const float keep = hi ? v2[1] : v2[0];
-    v = keep + __shfl_xor(send, 4, kWave);
+    v = (hi ? v2[1] : v2[0]) + dpp_f<kDppHalfMirror>(hi ? v2[0] : v2[1]);
   }
-  v += __shfl_xor(v, 2, kWave);
-  v += __shfl_xor(v, 1, kWave);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppXor1>(v);
   if ((lane & 3) == 0) {
     const int j = ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 +
                   ((lane >> 2) & 1);

@@ -8,7 +8,7 @@
 // its pools' key rows straight from HBM into the B-operand layout (16 bytes per
 // lane per k-step, a 64-byte run of one key row per lane group), four 16-pool
 // tiles per wave in flight.  The relu, head weighting and head sum happen on
-// the accumulator: each lane holds 4 heads of one pool; two xor shuffles finish
+// the accumulator: each lane holds 4 heads of one pool; two permlane swaps finish
 // the sum in a fixed order.
 #include "dsa_device.hpp"
 #include "dsa_host.hpp"
@@ -88,8 +88,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(
     s += fmaxf(acc[1], 0.f) * wr[1];
     s += fmaxf(acc[2], 0.f) * wr[2];
     s += fmaxf(acc[3], 0.f) * wr[3];
-    s += __shfl_xor(s, 16, kWave);
-    s += __shfl_xor(s, 32, kWave);
+    s = rows_sum(s);  // the four lane rows hold four heads each
     if (s == 0.f) s = 0.f;  // store -0 as +0
     const int p = tile0 + tt * 16 + col;
     const bool c = p < P && pv[tt] != 0 && ps[tt] + kpool - 1 <= qp;

@@ -11,7 +11,7 @@
 // Layout: one pool is handled by D/8 lanes, each owning 8 channels (one 16-byte
 // load per slot row), so a wave streams 64/(D/8) pools at once with fully
 // coalesced row reads.  Per-channel slot softmax is lane-local; the LayerNorm
-// mean and variance are xor-shuffle reductions over the pool's lanes.
+// mean and variance are DPP reductions over the pool's lanes.
 // HBM-bound (2*kpool*D*2 bytes in, D*2 out per pool): no MFMA.
 #include <limits.h>
 
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
     float sum = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) sum += x[c];
-    sum = wave_sum_xor(sum, LPP - 1);
+    sum = group_sum<LPP>(sum);
     const float mean = sum / (float)D;
     float sq = 0.f;
 #pragma unroll
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
       const float d = x[c] - mean;
       sq = fmaf(d, d, sq);
     }
-    sq = wave_sum_xor(sq, LPP - 1);
+    sq = group_sum<LPP>(sq);
     const float rstd = 1.0f / sqrtf(sq / (float)D + eps);
     uint32_t packed[4];
 #pragma unroll

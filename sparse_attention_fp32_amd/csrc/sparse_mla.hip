@@ -5,28 +5,26 @@
 // per-row gather of the selected ids is exactly the dense set-membership mask;
 // the serving kernel keeps an online softmax and no full score row).
 //
-// Work split (flash-decoding): workgroup (chunk, head block, query) takes up to
-// 64 heads of one query over one chunk of its selected ids; 4 waves own 16
-// heads each.  The chunk's ids are staged in LDS first; the chunk is then
-// walked in 32-token sub-chunks whose gathered latent rows (1 KiB each, one
-// coalesced wave load per row, every load unconditional: ids outside the
-// selection are redirected to a selected row and masked) are prefetched into
-// registers one sub-chunk ahead, staged in LDS and shared by the 4 waves.
-// Per sub-chunk and wave, on v_mfma_f32_16x16x32_bf16:
-//   S^T[32 tok x 16 heads] = C[32 x 512] . Q^T   (C from LDS, Q in registers)
-//   online softmax per head (log2 domain) with a lazily moved reference max
-//   O += P[16 x 32] . C[32 x 512]
-// Computing S transposed lets the accumulator of QK^T serve as the A operand
-// of PV with no data movement: K index 8g+j of lane group g maps to token 4g+j
-// (j < 4) or 16+4g+j-4.  The PV B operand needs 8 tokens of one dimension per
-// lane; a lane reads 16 bytes (8 consecutive dims) of each of its 8 token rows
-// and regroups the halves into 8 B operands, so output tile e of dim group G
-// holds dims G*128 + 8c + e at lane column c, and each lane stores 8
-// consecutive dims at once.
-// fp8 latent rows are expanded to bf16 exactly on the way into LDS; the row
-// scale multiplies the logits and the probabilities instead of the data.
-// With more than one chunk, per-chunk (max, sum, unnormalised O) partials go
-// to the workspace and mla_combine_kernel merges them in chunk order.
+// Work split (flash-decoding): workgroup (chunk, 64-head block, query) covers
+// one chunk of a query's selected ids for up to 64 heads.  Its 4 waves split
+// the 512 latent dims (128 each), not the heads:
+//  * each wave loads its 128-dim slice of the 32 gathered rows of a sub-chunk
+//    straight from HBM into the MFMA A-operand layout (two sub-chunks in
+//    flight: the next one loads while this one computes);
+//  * QK^T: each wave computes the partial S^T[32 tok x 64 heads] over its dims
+//    (v_mfma_f32_16x16x32_bf16, Q^T in registers); the partials meet in LDS
+//    and wave w adds the four of head tile w in a fixed order, runs the online
+//    softmax (log2 domain, reference max moved only when it grows by > 2^8)
+//    for those 16 heads, and publishes P in the PV A-operand layout -- S^T's
+//    accumulator layout is that operand layout, with K index 8g+j of lane
+//    group g meaning token 4g+j (j < 4) or 16+4g+j-4;
+//  * PV: O[64 heads x its 128 dims] += P . C_slice, the B operand read from
+//    the wave's own slice in LDS (16 bytes = 8 dims per row per lane,
+//    regrouped into 8 operands, so each lane owns 8 consecutive output dims).
+// fp8 rows are widened to bf16 exactly in registers; the row scale multiplies
+// the logits and the probabilities instead of the data.  With more than one
+// chunk, per-chunk (max, sum) pairs and unnormalised O (bf16) go to the
+// workspace and mla_combine_kernel merges them in chunk order.
 #include <limits.h>
 
 #include "dsa_device.hpp"
@@ -37,11 +35,12 @@ namespace {
 using namespace dsa;
 
 constexpr int L = DSA_KV_LORA;
-constexpr int kSub = 32;                 // tokens per sub-chunk
-constexpr int kRowBytes = L * 2 + 16;    // LDS row stride: bf16 row + 16-byte pad
-constexpr int kTargetWG = 256;           // aim for one workgroup per CU
-constexpr int kMinSubPerChunk = 4;       // >= 128 ids per chunk keeps partials small
-constexpr int kMaxTch = 2048;            // ids per chunk staged in LDS
+constexpr int kSub = 32;                  // tokens per sub-chunk
+constexpr int kSlice = 128;               // latent dims per wave
+constexpr int kSliceRow = kSlice * 2 + 16;  // LDS bytes per token row of a slice (+pad)
+constexpr int kTargetWG = 256;            // aim for one workgroup per CU
+constexpr int kMinSubPerChunk = 4;        // >= 128 ids per chunk keeps partials small
+constexpr int kMaxTch = 2048;             // ids per chunk staged in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -64,14 +63,34 @@ Chunking mla_chunking(int Q, int Hm, int out_width) {
   return {(nsub + spc - 1) / spc, spc * kSub};
 }
 
-__device__ __forceinline__ uint4 ldg16(const void* p) { return *(const uint4*)p; }
-
 __device__ __forceinline__ uint32_t lo_pair(uint32_t x, uint32_t y) {
   return (x & 0xffffu) | (y << 16);
 }
 __device__ __forceinline__ uint32_t hi_pair(uint32_t x, uint32_t y) {
   return (x >> 16) | (y & 0xffff0000u);
 }
+// 8 fp8 codes -> 8 bf16 (exact)
+__device__ __forceinline__ uint4 widen_fp8x8(uint2 v) {
+  uint32_t o[4];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t w = k ? v.y : v.x;
+    o[2 * k] = fp8e4m3_to_bf16(w & 0xffu) | (fp8e4m3_to_bf16((w >> 8) & 0xffu) << 16);
+    o[2 * k + 1] = fp8e4m3_to_bf16((w >> 16) & 0xffu) | (fp8e4m3_to_bf16(w >> 24) << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+template <bool FP8>
+struct RowSlice;  // registers holding one lane's share of a sub-chunk's rows
+template <>
+struct RowSlice<false> {
+  uint4 v[2][4];  // [token tile tt][k-step kk]: 8 bf16 dims
+};
+template <>
+struct RowSlice<true> {
+  uint2 v[2][4];  // 8 fp8 codes
+};
 
 template <bool FP8>
 __global__ __launch_bounds__(256) void sparse_mla_kernel(
@@ -79,35 +98,42 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
     const float* __restrict__ ckv_scale, const int32_t* __restrict__ kv_off,
     const int32_t* __restrict__ q_req, const int32_t* __restrict__ tok, int Hm, int out_width,
     int tch, float sm_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_ml) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_c[kSub * kRowBytes];
-  __shared__ int s_id[kMaxTch];      // selected id per chunk position, -1 if none
-  __shared__ float s_mul[kSub];      // logit multiplier per token: sm_scale*log2e*row scale
-  __shared__ float s_scl[kSub];      // row scale (1 for bf16)
-  __shared__ int s_ok[kSub];
-  __shared__ int s_safe;             // some selected id of this chunk, or -1
+    uint16_t* __restrict__ part_o, float* __restrict__ part_ml) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_slice[4][kSub * kSliceRow];
+  __shared__ f32x4_t s_exch[4][4][2][64];  // [source wave][head tile][token tile][lane]
+  __shared__ uint4 s_p[4][64];             // P operands per head tile
+  __shared__ float s_alpha[64];            // O rescale factor per head (when moved)
+  __shared__ int s_moved[4];               // a head tile moved its reference max
+  __shared__ __attribute__((aligned(16))) float s_mul[kSub];   // sm_scale*log2e*row scale
+  __shared__ __attribute__((aligned(16))) float s_bias[kSub];  // 0, or -inf for no token
+  __shared__ __attribute__((aligned(16))) float s_scl[kSub];   // row scale (1 for bf16)
+  __shared__ float s_lrun[64];
+  __shared__ int s_id[kMaxTch];
+  __shared__ int s_safe;
 
   const int chunk = blockIdx.x, nchunks = gridDim.x, hb = blockIdx.y, qx = blockIdx.z;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int head0 = hb * 64 + wave * 16;
   const int r = q_req[qx];
   const int64_t rowbase = kv_off[r];
   const int j0 = chunk * tch;
   const int j1 = min(out_width, j0 + tch);
   const int nsub = j1 > j0 ? (j1 - j0 + kSub - 1) / kSub : 0;
   const int32_t* trow = tok + (int64_t)qx * out_width;
+  const int dim0 = w * kSlice;  // this wave's latent slice
 
-  // Stage the chunk's ids (one round trip) while the Q operand loads.
+  // Stage the chunk's ids while the Q^T operand loads:
+  // qb[ht][kk] = Q[head hb*64 + ht*16 + col][dim0 + kk*32 + grp*8 .. +8].
   if (t == 0) s_safe = -1;
-  const int hq = head0 + col;
-  bf16x8_t qb[16];
-  {
-    const uint16_t* qrow = q + ((int64_t)qx * Hm + (hq < Hm ? hq : Hm - 1)) * L + grp * 8;
+  bf16x8_t qb[4][4];
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      const uint4 v = ldg16(qrow + kk * 32);
-      qb[kk] = as_bf16x8(hq < Hm ? v : make_uint4(0, 0, 0, 0));
+  for (int ht = 0; ht < 4; ++ht) {
+    const int h = hb * 64 + ht * 16 + col;
+    const uint16_t* qrow = q + ((int64_t)qx * Hm + (h < Hm ? h : Hm - 1)) * L + dim0 + grp * 8;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint4 v = *(const uint4*)(qrow + kk * 32);
+      qb[ht][kk] = as_bf16x8(h < Hm ? v : make_uint4(0, 0, 0, 0));
     }
   }
   __syncthreads();
@@ -120,122 +146,96 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
   }
   __syncthreads();
   const int safe = s_safe;
-
-  f32x4_t o[4][8];  // [dim group G][tile e]: O[head grp*4+i][G*128 + 8*col + e]
-#pragma unroll
-  for (int G = 0; G < 4; ++G)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[G][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  // Gather mapping: bf16 rows are 64 x 16 B (one wave per row, 8 rows per
-  // thread); fp8 rows are 32 x 16 B (half a wave per row, 4 rows per thread).
-  constexpr int NPRE = FP8 ? 4 : 8;
-  constexpr int kColU = FP8 ? 32 : 64;
-  const int prow0 = t / kColU, pcu = t % kColU;
-  constexpr int kRowStep = 256 / kColU;
-  uint4 pre0[NPRE];
-
-  auto gather = [&](int s, uint4 (&dst)[NPRE]) {
-#pragma unroll
-    for (int i = 0; i < NPRE; ++i) {
-      const int id = s_id[s * kSub + prow0 + i * kRowStep];
-      const int64_t g = rowbase + (id >= 0 ? id : safe);
-      dst[i] = FP8 ? ldg16((const uint8_t*)ckv_v + g * L + pcu * 16)
-                   : ldg16((const uint16_t*)ckv_v + g * L + pcu * 8);
-    }
-  };
-
   const int nwork = safe >= 0 ? nsub : 0;  // a chunk with no selected id has no work
-  if (nwork > 0) gather(0, pre0);
 
-  // One sub-chunk: stage the prefetched rows, start the next gather, compute.
-  auto step = [&](int s, uint4 (&cur)[NPRE]) {
-    __syncthreads();  // every wave is done with the previous sub-chunk
+  f32x4_t o[4][8];  // [head tile][e]: O[head ht*16 + grp*4 + i][dim0 + 8*col + e]
 #pragma unroll
-    for (int i = 0; i < NPRE; ++i) {
-      const int row = prow0 + i * kRowStep;
-      if (FP8) {
-        const uint4 v = cur[i];
-        const uint32_t w8[4] = {v.x, v.y, v.z, v.w};
-        uint32_t o16[8];
+  for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t b0 = fp8e4m3_to_bf16(w8[k] & 0xffu);
-          const uint32_t b1 = fp8e4m3_to_bf16((w8[k] >> 8) & 0xffu);
-          const uint32_t b2 = fp8e4m3_to_bf16((w8[k] >> 16) & 0xffu);
-          const uint32_t b3 = fp8e4m3_to_bf16(w8[k] >> 24);
-          o16[2 * k] = b0 | (b1 << 16);
-          o16[2 * k + 1] = b2 | (b3 << 16);
-        }
-        uint4* dst = (uint4*)(lds_c + row * kRowBytes + pcu * 32);
-        dst[0] = make_uint4(o16[0], o16[1], o16[2], o16[3]);
-        dst[1] = make_uint4(o16[4], o16[5], o16[6], o16[7]);
-      } else {
-        *(uint4*)(lds_c + row * kRowBytes + pcu * 16) = cur[i];
+    for (int e = 0; e < 8; ++e) o[ht][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;  // head w*16 + col (wave w owns head tile w)
+
+  RowSlice<FP8> cr;
+  float pre_scl = 1.f;
+  auto gather = [&](int s) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int id = s_id[s * kSub + tt * 16 + col];
+      const int64_t g = rowbase + (id >= 0 ? id : safe);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int d = dim0 + kk * 32 + grp * 8;
+        if (FP8)
+          ((uint2*)cr.v[tt])[kk] = *(const uint2*)((const uint8_t*)ckv_v + g * L + d);
+        else
+          ((uint4*)cr.v[tt])[kk] = *(const uint4*)((const uint16_t*)ckv_v + g * L + d);
       }
     }
     if (t < kSub) {
       const int id = s_id[s * kSub + t];
-      const float scl = FP8 ? ckv_scale[rowbase + (id >= 0 ? id : safe)] : 1.f;
-      s_ok[t] = id >= 0;
-      s_scl[t] = scl;
-      s_mul[t] = sm_log2 * scl;
+      pre_scl = FP8 ? ckv_scale[rowbase + (id >= 0 ? id : safe)] : 1.f;
     }
-    __syncthreads();
-    if (s + 1 < nwork) gather(s + 1, cur);  // the next rows load meanwhile
+  };
+  if (nwork > 0) gather(0);
 
-    // S^T tiles: tokens tt*16 + (0..15) x the wave's 16 heads.
-    f32x4_t sacc[2];
+  uint8_t* my_slice = s_slice[w];
+  for (int s = 0; s < nwork; ++s) {
+    // per-token logit multiplier and mask of this sub-chunk
+    if (t < kSub) {
+      const int id = s_id[s * kSub + t];
+      s_mul[t] = sm_log2 * pre_scl;
+      s_bias[t] = id >= 0 ? 0.f : -INFINITY;
+      s_scl[t] = pre_scl;
+    }
+    // partial S^T over this wave's dims, and the slice into LDS for PV
+    f32x4_t sacc[4][2];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) sacc[ht][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const uint8_t* arow = lds_c + (tt * 16 + col) * kRowBytes + grp * 16;
-      sacc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        uint4 av[8];
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint4 a = FP8 ? widen_fp8x8(((const uint2*)cr.v[tt])[kk]) : ((const uint4*)cr.v[tt])[kk];
+        *(uint4*)(my_slice + (tt * 16 + col) * kSliceRow + (kk * 32 + grp * 8) * 2) = a;
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) av[kk] = *(const uint4*)(arow + (half * 8 + kk) * 64);
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-          sacc[tt] = mfma16x16x32(as_bf16x8(av[kk]), qb[half * 8 + kk], sacc[tt]);
+        for (int ht = 0; ht < 4; ++ht) sacc[ht][tt] = mfma16x16x32(as_bf16x8(a), qb[ht][kk], sacc[ht][tt]);
       }
     }
-    // lane holds S^T[token tt*16 + grp*4 + i][head col]
+    if (s + 1 < nwork) gather(s + 1);  // the next rows load while this sub-chunk computes
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) s_exch[w][ht][tt][lane] = sacc[ht][tt];
+    __syncthreads();
+
+    // wave w: full S^T of head tile w, softmax, P
     float x[8];
-    float mloc = -INFINITY;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < 2; ++tt) {
+      const f32x4_t a0 = s_exch[0][w][tt][lane], a1 = s_exch[1][w][tt][lane];
+      const f32x4_t a2 = s_exch[2][w][tt][lane], a3 = s_exch[3][w][tt][lane];
+      const float4 mul = *(const float4*)(s_mul + tt * 16 + grp * 4);
+      const float4 bias = *(const float4*)(s_bias + tt * 16 + grp * 4);
+      const float mu[4] = {mul.x, mul.y, mul.z, mul.w};
+      const float bi[4] = {bias.x, bias.y, bias.z, bias.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tk = tt * 16 + grp * 4 + i;
-        const float v = s_ok[tk] ? sacc[tt][i] * s_mul[tk] : -INFINITY;
-        x[tt * 4 + i] = v;
-        mloc = fmaxf(mloc, v);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-    // Lazy rescaling: a head's reference max m_run moves only when this
-    // sub-chunk's max exceeds it by more than 8 (log2 units), so P stays below
-    // 2^8 and O is rescaled only on the rare step that moves a reference.
+      for (int i = 0; i < 4; ++i) x[tt * 4 + i] = fmaf(((a0[i] + a1[i]) + a2[i]) + a3[i], mu[i], bi[i]);
+    }
+    float mloc = x[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) mloc = fmaxf(mloc, x[k]);
+    mloc = rows_max(mloc);
     const bool move = mloc > m_run + 8.f;
-    if (__any(move)) {
+    const bool any_move = __any(move);
+    if (any_move) {
       const float alpha = move ? exp2f(m_run - mloc) : 1.f;  // exp2(-inf) = 0
-      const bool live = __any(move && m_run != -INFINITY);     // O holds data to rescale
       if (move) m_run = mloc;
       l_run *= alpha;
-      if (live) {
-        float ai[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, grp * 4 + i, kWave);
-#pragma unroll
-        for (int G = 0; G < 4; ++G)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[G][e][i] *= ai[i];
-      }
+      if (grp == 0) s_alpha[w * 16 + col] = alpha;
     }
+    if (lane == 0) s_moved[w] = any_move;
     const bool none = m_run == -INFINITY;
     float p[8];
     float psum = 0.f;
@@ -244,86 +244,100 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
       p[k] = none ? 0.f : exp2f(x[k] - m_run);
       psum += p[k];
     }
-    psum += __shfl_xor(psum, 16, kWave);
-    psum += __shfl_xor(psum, 32, kWave);
-    l_run += psum;
-
-    // P as the A operand of O = P C: lane holds P[head col][K = grp*8 + k].
-    uint32_t pw[4];
-#pragma unroll
-    for (int k = 0; k < 8; k += 2) {
-      float p0 = p[k], p1 = p[k + 1];
+    l_run += rows_sum(psum);
+    {
+      uint32_t pw[4];
+      float sc[8];
       if (FP8) {
-        const int t0 = (k < 4 ? 0 : 16) + grp * 4 + (k & 3);
-        p0 *= s_scl[t0];
-        p1 *= s_scl[t0 + 1];
+        const float4 s0 = *(const float4*)(s_scl + grp * 4);
+        const float4 s1 = *(const float4*)(s_scl + 16 + grp * 4);
+        sc[0] = s0.x; sc[1] = s0.y; sc[2] = s0.z; sc[3] = s0.w;
+        sc[4] = s1.x; sc[5] = s1.y; sc[6] = s1.z; sc[7] = s1.w;
       }
-      pw[k >> 1] = f32_to_bf16_rne(p0) | (f32_to_bf16_rne(p1) << 16);
+#pragma unroll
+      for (int k = 0; k < 8; k += 2) {
+        const float p0 = FP8 ? p[k] * sc[k] : p[k], p1 = FP8 ? p[k + 1] * sc[k + 1] : p[k + 1];
+        pw[k >> 1] = f32_to_bf16_rne(p0) | (f32_to_bf16_rne(p1) << 16);
+      }
+      s_p[w][lane] = make_uint4(pw[0], pw[1], pw[2], pw[3]);
     }
-    const bf16x8_t pa = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    __syncthreads();
 
-    // B operands: token rows grp*4+0..3 and 16+grp*4+0..3 (K order), 8 dims
-    // G*128 + 8*col .. +7 per 16-byte read.
-    const uint8_t* r0 = lds_c + (grp * 4) * kRowBytes + col * 16;
-    const uint8_t* r1 = lds_c + (16 + grp * 4) * kRowBytes + col * 16;
+    // rescale O where a head tile moved its reference max (rare)
+    if (s_moved[0] | s_moved[1] | s_moved[2] | s_moved[3]) {
 #pragma unroll
-    for (int G = 0; G < 4; ++G) {
-      uint4 u[8];
+      for (int ht = 0; ht < 4; ++ht) {
+        if (!s_moved[ht]) continue;
+        float ai[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u[j] = *(const uint4*)(r0 + j * kRowBytes + G * 256);
-        u[4 + j] = *(const uint4*)(r1 + j * kRowBytes + G * 256);
-      }
+        for (int i = 0; i < 4; ++i) ai[i] = s_alpha[ht * 16 + grp * 4 + i];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wd = e >> 1;
-        uint32_t bw[4];
+        for (int e = 0; e < 8; ++e)
 #pragma unroll
-        for (int m2 = 0; m2 < 4; ++m2) {
-          const uint32_t a0 = u4_word(u[2 * m2], wd), a1 = u4_word(u[2 * m2 + 1], wd);
-          bw[m2] = (e & 1) ? hi_pair(a0, a1) : lo_pair(a0, a1);
-        }
-        o[G][e] = mfma16x16x32(pa, as_bf16x8(make_uint4(bw[0], bw[1], bw[2], bw[3])), o[G][e]);
+          for (int i = 0; i < 4; ++i) o[ht][e][i] *= ai[i];
       }
     }
-  };
-  for (int s = 0; s < nwork; ++s) step(s, pre0);
-
-  float li[4];
+    // PV over this wave's slice
+    bf16x8_t pa[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) li[i] = __shfl(l_run, grp * 4 + i, kWave);
+    for (int ht = 0; ht < 4; ++ht) pa[ht] = as_bf16x8(s_p[ht][lane]);
+    uint4 u[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tk = (j < 4 ? 0 : 16) + grp * 4 + (j & 3);
+      u[j] = *(const uint4*)(my_slice + tk * kSliceRow + col * 16);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int wd = e >> 1;
+      uint32_t bw[4];
+#pragma unroll
+      for (int m2 = 0; m2 < 4; ++m2) {
+        const uint32_t a0 = u4_word(u[2 * m2], wd), a1 = u4_word(u[2 * m2 + 1], wd);
+        bw[m2] = (e & 1) ? hi_pair(a0, a1) : lo_pair(a0, a1);
+      }
+      const bf16x8_t bv = as_bf16x8(make_uint4(bw[0], bw[1], bw[2], bw[3]));
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) o[ht][e] = mfma16x16x32(pa[ht], bv, o[ht][e]);
+    }
+  }
+
+  // epilogue: per-head sums to every wave, then this wave's dims of all heads
+  if (grp == 0) s_lrun[w * 16 + col] = l_run;
+  __syncthreads();
   if (nchunks == 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = head0 + grp * 4 + i;
-      if (h >= Hm) continue;
-      const float inv = li[i] > 0.f ? 1.f / li[i] : 0.f;
-      uint16_t* orow = out + ((int64_t)qx * Hm + h) * L + col * 8;
+    for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-      for (int G = 0; G < 4; ++G) {
+      for (int i = 0; i < 4; ++i) {
+        const int h = hb * 64 + ht * 16 + grp * 4 + i;
+        if (h >= Hm) continue;
+        const float lv = s_lrun[ht * 16 + grp * 4 + i];
+        const float inv = lv > 0.f ? 1.f / lv : 0.f;
         uint32_t pk[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2)
-          pk[e >> 1] = f32_to_bf16_rne(o[G][e][i] * inv) | (f32_to_bf16_rne(o[G][e + 1][i] * inv) << 16);
-        *(uint4*)(orow + G * 128) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+          pk[e >> 1] = f32_to_bf16_rne(o[ht][e][i] * inv) | (f32_to_bf16_rne(o[ht][e + 1][i] * inv) << 16);
+        *(uint4*)(out + ((int64_t)qx * Hm + h) * L + dim0 + col * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       }
-    }
+    const int hq = hb * 64 + w * 16 + col;
     if (lse && grp == 0 && hq < Hm)
       lse[(int64_t)qx * Hm + hq] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   } else {
     const int64_t pbase = ((int64_t)qx * nchunks + chunk) * Hm;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = head0 + grp * 4 + i;
-      if (h >= Hm) continue;
-      float* prow = part_o + (pbase + h) * L + col * 8;
+    for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-      for (int G = 0; G < 4; ++G) {
-        float4* d4 = (float4*)(prow + G * 128);
-        d4[0] = make_float4(o[G][0][i], o[G][1][i], o[G][2][i], o[G][3][i]);
-        d4[1] = make_float4(o[G][4][i], o[G][5][i], o[G][6][i], o[G][7][i]);
+      for (int i = 0; i < 4; ++i) {
+        const int h = hb * 64 + ht * 16 + grp * 4 + i;
+        if (h >= Hm) continue;
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          pk[e >> 1] = f32_to_bf16_rne(o[ht][e][i]) | (f32_to_bf16_rne(o[ht][e + 1][i]) << 16);
+        *(uint4*)(part_o + (pbase + h) * L + dim0 + col * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       }
-    }
+    const int hq = hb * 64 + w * 16 + col;
     if (grp == 0 && hq < Hm) {
       part_ml[(pbase + hq) * 2] = m_run;
       part_ml[(pbase + hq) * 2 + 1] = l_run;
@@ -332,12 +346,14 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
 }
 
 // Merge the per-chunk partials of one (query, head) in chunk order; a wave per
-// head, 8 dims per lane, four heads per workgroup.
-__global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ part_o,
+// head, 8 dims per lane, four heads per workgroup.  All chunks' loads of a
+// batch are issued before any is used.
+__global__ __launch_bounds__(256) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
                                                           int nchunks, int Hm,
                                                           uint16_t* __restrict__ out,
                                                           float* __restrict__ lse) {
+  constexpr int kBatch = 16;
   const int h = blockIdx.x * 4 + (threadIdx.x >> 6), qx = blockIdx.y, lane = threadIdx.x & 63;
   if (h >= Hm) return;
   const int64_t b0 = (int64_t)qx * nchunks * Hm + h;
@@ -345,22 +361,26 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
   for (int c = 0; c < nchunks; ++c) M = fmaxf(M, part_ml[(b0 + (int64_t)c * Hm) * 2]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
-#pragma unroll 4
-  for (int c = 0; c < nchunks; ++c) {
-    const int64_t pc = b0 + (int64_t)c * Hm;
-    const float m = part_ml[pc * 2], l = part_ml[pc * 2 + 1];
-    const float4* src = (const float4*)(part_o + pc * L + lane * 8);
-    const float4 u = src[0], v = src[1];
-    const float wgt = (M == -INFINITY) ? 0.f : exp2f(m - M);
-    lsum = fmaf(l, wgt, lsum);
-    acc[0] = fmaf(wgt, u.x, acc[0]);
-    acc[1] = fmaf(wgt, u.y, acc[1]);
-    acc[2] = fmaf(wgt, u.z, acc[2]);
-    acc[3] = fmaf(wgt, u.w, acc[3]);
-    acc[4] = fmaf(wgt, v.x, acc[4]);
-    acc[5] = fmaf(wgt, v.y, acc[5]);
-    acc[6] = fmaf(wgt, v.z, acc[6]);
-    acc[7] = fmaf(wgt, v.w, acc[7]);
+  for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+    uint4 v[kBatch];
+    float2 ml[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int c = min(c0 + k, nchunks - 1);
+      const int64_t pc = b0 + (int64_t)c * Hm;
+      v[k] = *(const uint4*)(part_o + pc * L + lane * 8);
+      ml[k] = *(const float2*)(part_ml + pc * 2);
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float wgt = (M == -INFINITY || c0 + k >= nchunks) ? 0.f : exp2f(ml[k].x - M);
+      lsum = fmaf(ml[k].y, wgt, lsum);
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const uint32_t word = u4_word(v[k], d >> 1);
+        acc[d] = fmaf(wgt, bf16_to_f32((d & 1) ? (word >> 16) : (word & 0xffffu)), acc[d]);
+      }
+    }
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   uint32_t pk[4];
@@ -381,7 +401,8 @@ DSA_EXPORT size_t dsa_sparse_mla_decode_workspace_size(int Q, int Hm, int L_, in
   const Chunking ch = mla_chunking(Q, Hm, out_width);
   if (ch.nchunks <= 1) return 0;
   const size_t rows = (size_t)Q * ch.nchunks * Hm;
-  return rows * L * sizeof(float) + rows * 2 * sizeof(float);
+  // bf16 partial O rows, then (max, sum) f32 pairs (16-byte aligned)
+  return rows * L * sizeof(uint16_t) + rows * 2 * sizeof(float);
 }
 
 DSA_EXPORT dsa_status dsa_sparse_mla_decode(const uint16_t* q, const void* ckv,
@@ -411,8 +432,8 @@ DSA_EXPORT dsa_status dsa_sparse_mla_decode(const uint16_t* q, const void* ckv,
   DSA_REQUIRE(ws_bytes >= need && (need == 0 || ws), DSA_ERR_INVALID_ARG,
               "dsa_sparse_mla_decode: workspace %zu bytes, need %zu", ws_bytes, need);
   const Chunking ch = mla_chunking(Q, Hm, out_width);
-  float* part_o = need ? (float*)ws : nullptr;
-  float* part_ml = need ? (float*)ws + (size_t)Q * ch.nchunks * Hm * L : nullptr;
+  uint16_t* part_o = need ? (uint16_t*)ws : nullptr;
+  float* part_ml = need ? (float*)((uint16_t*)ws + (size_t)Q * ch.nchunks * Hm * L) : nullptr;
   dim3 grid(ch.nchunks, (Hm + 63) / 64, Q);
   const float sm_log2 = sm_scale * kLog2e;
   if (dsa::trace_enabled())

@@ -1,20 +1,22 @@
 // a4: pool top-k with lowest-id tie-breaking, emitted in ascending pool id.
 //
-// One 1024-thread workgroup per score row.  Each thread keeps a contiguous run
-// of E ids as order-preserving integer keys in registers (a finite float maps
-// to an unsigned key that sorts like the float; non-candidates are key 0 and
-// never counted), so no floating-point comparison decides the selection.
-//  1. The row's largest key and the octave of every key below it (difference
-//     of the top 9 key bits = sign and exponent, capped at 15) are found; the
-//     octave counts are kept in registers and summed over the workgroup in a
-//     fixed order -- no atomics, because nearly all scores of a row share
-//     their top key bits.
-//  2. Inside the octave that holds the k_eff-th best key, byte-wise radix
-//     passes over per-wave LDS histograms pin the threshold key T (stopping
-//     early once the threshold bin is taken whole).
-//  3. Every key above T is kept and, among keys equal to T, the lowest ids,
-//     via a block prefix sum in id order; a second prefix sum writes the kept
-//     ids ascending.
+// One 1024-thread workgroup per score row; thread t holds ids t + 1024*e
+// (e < E), so every load instruction is fully coalesced and the order (e, t)
+// is ascending id order.  Scores become order-preserving integer keys (a
+// finite float maps to an unsigned key that sorts like the float; -0 like +0;
+// non-candidates are key 0 and never counted), so no floating-point
+// comparison decides the selection.
+//  1. Candidate count and largest key (wave ballots / DPP max, one barrier).
+//  2. Octave of every key below the largest (difference of the top 9 key bits
+//     = sign and exponent, capped at 15), counted in packed 8-bit register
+//     fields and summed over the workgroup in a fixed order -- no atomics,
+//     because nearly all scores of a row share their top key bits.
+//  3. Inside the octave holding the k_eff-th best key, byte-wise radix passes
+//     over per-wave LDS histograms pin the threshold key T (stopping early
+//     once the threshold bin is taken whole).
+//  4. Keys above T are kept and, among keys equal to T, the lowest ids; kept
+//     ids are compacted in id order with wave ballots and per-(e, wave)
+//     offsets.
 #include "dsa_device.hpp"
 #include "dsa_host.hpp"
 
@@ -25,59 +27,10 @@ using namespace dsa;
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 
-// Exclusive prefix sum over the workgroup in thread order; *total gets the sum.
-__device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) s_wave[wv] = x;
-  __syncthreads();
-  if (wv == 0) {
-    int s = lane < kWaves ? s_wave[lane] : 0;
-    const int own = s;
-#pragma unroll
-    for (int o = 1; o < kWaves; o <<= 1) {
-      const int y = __shfl_up(s, o, kWave);
-      if (lane >= o) s += y;
-    }
-    if (lane < kWaves) s_wave[kWaves + lane] = s - own;  // exclusive wave offsets
-    if (lane == kWaves - 1) s_wave[2 * kWaves] = s;
-  }
-  __syncthreads();
-  const int res = x - v + s_wave[kWaves + wv];
-  *total = s_wave[2 * kWaves];
-  __syncthreads();
-  return res;
-}
-
-// Sum of 16 per-lane counters over the wave, scattered: lane l (l % 4 == 0)
-// returns the total of counter j(l) = 8*b5 + 4*b4 + 2*b3 + b2 of its lane id.
-__device__ int wave_reduce_scatter16(const int (&c)[16], int lane) {
-  int v8[8], v4[4], v2[2];
-  {
-    const bool hi = (lane >> 5) & 1;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v8[i] = (hi ? c[8 + i] : c[i]) + __shfl_xor(hi ? c[i] : c[8 + i], 32, kWave);
-  }
-  {
-    const bool hi = (lane >> 4) & 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v4[i] = (hi ? v8[4 + i] : v8[i]) + __shfl_xor(hi ? v8[i] : v8[4 + i], 16, kWave);
-  }
-  {
-    const bool hi = (lane >> 3) & 1;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) v2[i] = (hi ? v4[2 + i] : v4[i]) + __shfl_xor(hi ? v4[i] : v4[2 + i], 8, kWave);
-  }
-  const bool hi = (lane >> 2) & 1;
-  int v = (hi ? v2[1] : v2[0]) + __shfl_xor(hi ? v2[0] : v2[1], 4, kWave);
-  v += __shfl_xor(v, 2, kWave);
-  v += __shfl_xor(v, 1, kWave);
-  return v;
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+// number of set bits of m below this lane
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 template <int E>
@@ -87,65 +40,102 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
                                                         int32_t* __restrict__ sel) {
   __shared__ int hist[kWaves][256];
   __shared__ int s_tot[256];
-  __shared__ int s_wave[2 * kWaves + 1];
   __shared__ uint32_t s_max[kWaves];
+  __shared__ int s_cnt[kWaves];
   __shared__ int s_oct[kWaves][16];
+  __shared__ int s_ecnt[2][E][kWaves];  // per (e, wave) counts: [0] ties at T, [1] kept
   __shared__ int s_bin, s_above, s_binc;
   const int q = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const float* srow = scores + (int64_t)q * pstride;
   const uint8_t* crow = cand + (int64_t)q * pstride;
   int32_t* out = sel + (int64_t)q * select_k;
 
-  // all loads issued together (ids clamped into the row), then masked
-  uint32_t key[E];
+  // loads (ids clamped into the row), then masked
   float sv[E];
   uint8_t cv[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int id = min(t * E + e, pstride - 1);
+    const int id = min(t + kThreads * e, pstride - 1);
     sv[e] = srow[id];
     cv[e] = crow[id];
   }
-  int nc = 0;
+  uint32_t key[E];
   uint32_t kmx = 0u;
+  int nc = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const bool c = t * E + e < pstride && cv[e] != 0;
+    const bool c = t + kThreads * e < pstride && cv[e] != 0;
     key[e] = c ? float_order_key(sv[e]) : 0u;
-    nc += c;
     kmx = max(kmx, key[e]);
+    nc += __popcll(ballot(c));
   }
+  kmx = wave_max_u32(kmx);
+  if (lane == 0) {
+    s_max[wv] = kmx;
+    s_cnt[wv] = nc;
+  }
+  __syncthreads();
+  int ncand = 0;
+  uint32_t kmax = 0u;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o, kWave));
-  if (lane == 0) s_max[wv] = kmx;
-  int ncand;
-  (void)block_exclusive_scan(nc, s_wave, &ncand);  // its barriers also publish s_max
+  for (int w = 0; w < kWaves; ++w) {
+    ncand += s_cnt[w];
+    kmax = max(kmax, s_max[w]);
+  }
   const int k_eff = min(select_k, ncand);
   if (k_eff == 0) {
     for (int i = t; i < select_k; i += kThreads) out[i] = -1;
     return;
   }
-  uint32_t kmax = 0u;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) kmax = max(kmax, s_max[w]);
   const uint32_t top9 = kmax >> 23;
 
-  // 1. octave counts (register histograms, fixed-order reduction)
-  int cnt[16];
-#pragma unroll
-  for (int b = 0; b < 16; ++b) cnt[b] = 0;
+  // 2. octave counts: 16 bins as four registers of four 8-bit fields (E <= 16)
   uint32_t oct[E];
+  uint32_t c8[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint32_t d = min(top9 - (key[e] >> 23), 15u);
     oct[e] = key[e] ? d : 16u;
-#pragma unroll
-    for (int b = 0; b < 16; ++b) cnt[b] += oct[e] == (uint32_t)b;
+    const uint32_t inc = key[e] ? 1u << ((d & 3u) * 8u) : 0u;
+    const uint32_t r = d >> 2;
+    c8[0] += r == 0u ? inc : 0u;
+    c8[1] += r == 1u ? inc : 0u;
+    c8[2] += r == 2u ? inc : 0u;
+    c8[3] += r == 3u ? inc : 0u;
   }
   {
-    const int v = wave_reduce_scatter16(cnt, lane);
-    if ((lane & 3) == 0)
-      s_oct[wv][((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1)] = v;
+    // widen to 16-bit pairs: p[j] holds bins 2j (low half) and 2j+1 (high half)
+    uint32_t p[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[2 * j] = (c8[j] & 0xffu) | ((c8[j] & 0xff00u) << 8);
+      p[2 * j + 1] = ((c8[j] >> 16) & 0xffu) | ((c8[j] >> 8) & 0xff0000u);
+    }
+    // reduce-scatter the 8 pairs over the wave (fields stay below 2^16)
+    int v4[4], v2[2], v1;
+    {
+      const bool hi = (lane >> 5) & 1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        v4[i] = (int)(hi ? p[4 + i] : p[i]) + xor32_i((int)(hi ? p[i] : p[4 + i]));
+    }
+    {
+      const bool hi = (lane >> 4) & 1;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) v2[i] = (hi ? v4[2 + i] : v4[i]) + xor16_i(hi ? v4[i] : v4[2 + i]);
+    }
+    {
+      const bool hi = (lane >> 3) & 1;
+      v1 = (hi ? v2[1] : v2[0]) + dpp_i<kDppMirror>(hi ? v2[0] : v2[1]);
+    }
+    v1 += dpp_i<kDppHalfMirror>(v1);
+    v1 += dpp_i<kDppXor2>(v1);
+    v1 += dpp_i<kDppXor1>(v1);
+    if ((lane & 7) == 0) {
+      const int j = ((lane >> 5) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
+      s_oct[wv][2 * j] = v1 & 0xffff;
+      s_oct[wv][2 * j + 1] = (int)((uint32_t)v1 >> 16);
+    }
   }
   __syncthreads();
   if (t < 64) {
@@ -153,12 +143,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     if (t < 16)
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) tot += s_oct[w][t];
-    int x = tot;  // inclusive prefix over octaves 0..15 (nearest the max first)
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const int y = __shfl_up(x, o, kWave);
-      if (t >= o) x += y;
-    }
+    const int x = wave_incl_scan(tot);  // octaves 0..15, nearest the max first
     const int before = x - tot;
     if (t < 16 && before < k_eff && k_eff <= x) {
       s_bin = t;
@@ -170,7 +155,6 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   const uint32_t boct = (uint32_t)s_bin;
   int krem = k_eff - s_above;
   const bool whole = s_binc == krem;
-  __syncthreads();
   // the threshold octave; octave 15 also holds everything further down
   uint32_t prefix = boct < 15u ? (top9 - boct) << 23 : 0u;
   uint32_t mask = boct < 15u ? 0xFF800000u : 0u;
@@ -178,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
 #pragma unroll
   for (int e = 0; e < E; ++e) act[e] = boct < 15u ? oct[e] == boct : (oct[e] >= 15u && oct[e] < 16u);
 
-  // 2. byte-wise radix passes inside the threshold octave
+  // 3. byte-wise radix passes inside the threshold octave
   if (!whole) {
     for (int hi = boct < 15u ? 22 : 31; hi >= 0; hi -= 8) {
       const int lo = hi >= 7 ? hi - 7 : 0;
@@ -197,21 +181,17 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
       }
       __syncthreads();
       if (t < 64) {
+        // lane t holds bins 255-4t .. 252-4t (descending): an inclusive prefix
+        // over lanes counts the keys in higher bins
         int h[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) h[j] = s_tot[4 * t + j];
+        for (int j = 0; j < 4; ++j) h[j] = s_tot[255 - 4 * t - j];
         const int sl = h[0] + h[1] + h[2] + h[3];
-        int x = sl;  // inclusive suffix sum over lanes
+        int above = wave_incl_scan(sl) - sl;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_down(x, o, kWave);
-          if (t + o < 64) x += y;
-        }
-        int above = x - sl;
-#pragma unroll
-        for (int j = 3; j >= 0; --j) {
+        for (int j = 0; j < 4; ++j) {
           if (above < krem && krem <= above + h[j]) {
-            s_bin = 4 * t + j;
+            s_bin = 255 - 4 * t - j;
             s_above = above;
             s_binc = h[j];
           }
@@ -223,30 +203,61 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
       krem -= s_above;
       prefix |= (uint32_t)b << lo;
       mask |= dmask << lo;
-      __syncthreads();
       if (bc == krem) break;  // the whole threshold bin is taken
     }
   }
 
-  // 3. keep octaves above the threshold one, keys above T, and the lowest-id ties
-  int n_gt = 0, n_eq = 0;
+  // 4. ties at T in id order, then compaction of every kept id in id order
+  bool gt[E], eq[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint32_t km = key[e] & mask;
-    n_gt += oct[e] < boct || (act[e] && km > prefix);
-    n_eq += act[e] && km == prefix;
+    gt[e] = oct[e] < boct || (act[e] && km > prefix);
+    eq[e] = act[e] && km == prefix;
   }
-  int tot;
-  const int eq_before = block_exclusive_scan(n_eq, s_wave, &tot);
-  const int take_eq = max(0, min(n_eq, krem - eq_before));
-  const int pos0 = block_exclusive_scan(n_gt + take_eq, s_wave, &tot);
-  int pos = pos0, eq_taken = 0;
+  uint64_t beq[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const uint32_t km = key[e] & mask;
-    bool take = oct[e] < boct || (act[e] && km > prefix);
-    if (act[e] && km == prefix) take = eq_taken++ < take_eq;
-    if (take && pos < k_eff) out[pos++] = t * E + e;
+    beq[e] = ballot(eq[e]);
+    if (lane == 0) s_ecnt[0][e][wv] = __popcll(beq[e]);
+  }
+  __syncthreads();
+  bool keep[E];
+  {
+    int base = 0;  // ties in earlier (e, wave) blocks
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      int mine = base;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const int c = s_ecnt[0][e][w];
+        mine += w < wv ? c : 0;
+        base += c;
+      }
+      keep[e] = gt[e] || (eq[e] && mine + lanes_below(beq[e]) < krem);
+    }
+  }
+  uint64_t bk[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    bk[e] = ballot(keep[e]);
+    if (lane == 0) s_ecnt[1][e][wv] = __popcll(bk[e]);
+  }
+  __syncthreads();
+  {
+    int base = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      int mine = base;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const int c = s_ecnt[1][e][w];
+        mine += w < wv ? c : 0;
+        base += c;
+      }
+      const int pos = mine + lanes_below(bk[e]);
+      if (keep[e] && pos < k_eff) out[pos] = t + kThreads * e;
+    }
   }
   for (int i = k_eff + t; i < select_k; i += kThreads) out[i] = -1;
 }
