@@ -4,12 +4,14 @@
 
 A step is one pass of the whole path -- head-gate, pool compression (of the
 pools the step's newest row completes; all older pools are cached), index
-scores, pool top-k, selection expansion, sparse MLA -- over one batch of
+scores, pool top-k, selection expansion, sparse MLA -- through the fused decode
+calls (gate+compress, gated index scores, top-k+expand, sparse MLA) over one batch of
 resident synthetic input: the 32K-context decode batch (16 requests x 32768
 cached rows, one query each) by default.  Eight input sets (each larger than
 the 256 MB last-level cache together with its outputs) are rotated so that
-every step streams its keys and latent rows from HBM.  Each set's six calls
-are captured once in a HIP graph; the timed region replays K graphs.
+every step streams its keys and latent rows from HBM.  Each set's calls are
+captured once in a HIP graph; the timed region replays K graphs.  The same
+step through the six separate calls is timed too, for comparison.
 
 The JSON line also carries, for the kernel that takes the most time, its
 algorithmic bytes per launch over its average launch time (HIP events on the
@@ -36,12 +38,17 @@ from sparse_attention_fp32_amd import workloads as W  # noqa: E402
 from sparse_attention_fp32_amd.pipeline import DsaStep  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-STAGES = ("head_gate", "kpool_compress", "index_scores", "topk_pools", "expand_selection",
-          "sparse_mla_decode")
-# kernel source behind each stage (a change to it invalidates stored HBM counters)
+# the calls of the timed step (the fused decode calls) ...
+STAGES = ("gate_compress", "index_scores_gated", "topk_expand", "sparse_mla_decode")
+# ... and the six separate calls, timed for comparison
+CALLS = ("head_gate", "kpool_compress", "index_scores", "topk_pools", "expand_selection",
+         "sparse_mla_decode")
+# kernel source behind each call (a change to it invalidates stored HBM counters)
 STAGE_SOURCE = {"head_gate": "head_gate.hip", "kpool_compress": "kpool_compress.hip",
                 "index_scores": "index_scores.hip", "topk_pools": "topk.hip",
-                "expand_selection": "expand.hip", "sparse_mla_decode": "sparse_mla.hip"}
+                "expand_selection": "expand.hip", "sparse_mla_decode": "sparse_mla.hip",
+                "gate_compress": "kpool_compress.hip", "index_scores_gated": "index_scores.hip",
+                "topk_expand": "topk.hip"}
 
 
 def algorithmic_bytes(spec: W.Spec, xn: dict, n_pools: np.ndarray, tok: np.ndarray) -> dict:
@@ -67,6 +74,12 @@ def algorithmic_bytes(spec: W.Spec, xn: dict, n_pools: np.ndarray, tok: np.ndarr
         "sparse_mla_decode": n_sel * lat_row + Q * Hm * L * 2 * 2 + Q * spec.out_width * 4
         + Q * Hm * 4 + 8 * Q,
     }
+    # fused calls: the head-gate partials are written once and read once; sel is
+    # written but not read back
+    part = 4 * Q * H * max(1, spec.hidden // 128)
+    b["gate_compress"] = b["head_gate"] - 4 * Q * H + part + b["kpool_compress"]
+    b["index_scores_gated"] = b["index_scores"] - 4 * Q * H + part + 4 * Q * H
+    b["topk_expand"] = b["topk_pools"] + b["expand_selection"] - Q * spec.select_k * 4
     return b
 
 
@@ -175,34 +188,48 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] {a.sets} input sets of {spec.name} resident", file=sys.stderr, flush=True)
 
-    graphs = []
-    for st in steps:
-        st.run(incremental=True)        # warm the path once before capture
+    def capture(fn):
+        graphs = []
+        for st in steps:
+            fn(st)                      # warm the path once before capture
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn(st)
+            graphs.append(g)
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            st.run(incremental=True)
-        graphs.append(g)
-    torch.cuda.synchronize()
+        return graphs
 
-    for i in range(a.warmup):
-        graphs[i % len(graphs)].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(a.steps):
-        graphs[i % len(graphs)].replay()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1)
+    def timed(graphs, n, warm):
+        for i in range(warm):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            graphs[i % len(graphs)].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1), time.perf_counter() - t0
+
+    # the step: the fused decode calls over cached pools
+    graphs = capture(lambda st: st.run_fused(incremental=True))
+    ms, wall = timed(graphs, a.steps, a.warmup)
     ms_per_step = ms / a.steps
     qps = spec.Q * a.steps / (ms / 1e3)
+    # the same step through the six separate calls, for comparison
+    graphs6 = capture(lambda st: st.run(incremental=True))
+    ms6, _ = timed(graphs6, max(1, a.steps // 4), max(1, a.warmup // 4))
+    six_us = ms6 / max(1, a.steps // 4) * 1e3
+    del graphs6
 
     # -- per-call launch times (HIP events on the launch stream) ---------------
     stream = torch.cuda.current_stream()
     fns = {
+        "gate_compress": lambda s: s.gate_compress(incremental=True),
+        "index_scores_gated": lambda s: s.index_scores_gated(),
+        "topk_expand": lambda s: s.topk_expand(),
         "head_gate": lambda s: s.head_gate(),
         "kpool_compress": lambda s: s.compress(incremental=True),
         "index_scores": lambda s: s.index_scores(),
@@ -210,8 +237,8 @@ def main():
         "expand_selection": lambda s: s.expand(),
         "sparse_mla_decode": lambda s: s.mla(),
     }
-    stage_us = {}
-    for name in STAGES:
+    call_us = {}
+    for name in fns:
         evs = []
         for i in range(a.stage_reps):
             s = steps[i % len(steps)]
@@ -222,11 +249,12 @@ def main():
             evs.append((ea, eb))
         torch.cuda.synchronize()
         d = [ea.elapsed_time(eb) * 1e3 for ea, eb in evs[4:]]
-        stage_us[name] = float(np.mean(d))
+        call_us[name] = float(np.mean(d))
+    stage_us = {k: call_us[k] for k in STAGES}
 
     xn0 = {"q_req": sets[0].q_req.cpu().numpy()}
     nb = algorithmic_bytes(spec, xn0, steps[0].n_pools.cpu().numpy(), steps[0].tok.cpu().numpy())
-    step_bytes = sum(nb.values())
+    step_bytes = sum(nb[k] for k in STAGES)
     dom = max(STAGES, key=lambda n: stage_us[n])
     ach = nb[dom] / (stage_us[dom] * 1e-6) / 1e9
     traffic = stored_traffic(dom, spec.name)
@@ -259,11 +287,15 @@ def main():
                    "mla_heads": spec.mla_heads, "latent": spec.latent,
                    "latent_dtype": "fp8_e4m3" if spec.latent_fp8 else "bf16",
                    "pools": "cached; the step recompresses the pool of its newest row",
-                   "input_sets": a.sets, "graph": "one HIP graph per set, six calls"},
+                   "input_sets": a.sets,
+                   "graph": "one HIP graph per set: the fused decode calls (gate+compress, "
+                            "gated index scores, top-k+expand, sparse MLA)"},
         "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": int(step_bytes),
         "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
-        "stage_bytes": {k: int(v) for k, v in nb.items()},
+        "stage_bytes": {k: int(nb[k]) for k in STAGES},
+        "six_call_step_us": round(six_us, 2),
+        "call_us": {k: round(call_us[k], 2) for k in CALLS},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),

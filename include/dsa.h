@@ -222,6 +222,66 @@ dsa_status dsa_sparse_mla_decode(const uint16_t* q, const void* ckv, const float
                                  float sm_scale, uint16_t* out, float* lse, void* ws,
                                  size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Fused decode calls   [stkernel pull request #290 measures what each launch
+ *     of a serving step costs; the Atlas page's pipeline order is kept]
+ *
+ * Three calls that compute a1-a5 with two launches fewer on the critical path;
+ * with dsa_sparse_mla_decode they make one decode step:
+ *
+ *   dsa_gate_compress       a1 (as split-K partials) and a2 in one launch
+ *   dsa_index_scores_gated  a3, adding the a1 partials first (writes w)
+ *   dsa_topk_expand         a4 and a5 in one launch
+ *
+ * Results equal those of the separate calls up to the summation order of the
+ * head-gate (fixed, so deterministic); every output of the separate calls is
+ * still written (w, keys, pool_start, pool_valid, n_pools, scores, cand, sel,
+ * tok).
+ *
+ * dsa_gate_split_count(M, K, N): the number of head-gate partials ns that
+ * dsa_gate_compress writes: K / 128 when 1 <= M <= 64, K is a multiple of 128
+ * and K / 128 <= 64; otherwise 1, and then the "partials" buffer receives w
+ * itself from the dense head-gate.  Returns 0 for N outside [1, 16], M < 0 or
+ * K < 1.
+ * dsa_gate_compress_workspace_size(M, K, N) = ns * M * N * 4 bytes.
+ *
+ * dsa_gate_compress: hidden, W, M, K, N as in dsa_head_gate; gate_part
+ * [ns, M, N] f32, part[s][m][n] = sum over k in slice s of hidden[m][k] W[k][n]
+ * (contents on entry are ignored); every other argument as in
+ * dsa_kpool_compress (B = 0 runs the head-gate alone).  Errors: those of
+ * dsa_kpool_compress and dsa_head_gate, and INVALID_ARG for gate_part_bytes
+ * below the size.
+ *
+ * dsa_index_scores_gated: as dsa_index_scores, with the head weights given as
+ * gate_part and nslices = ns (1 <= ns <= 64): w[q, h] = sum over s of
+ * gate_part[s][q][h], added in a fixed order, and stored to w [Q, H] f32
+ * unless w is NULL.  M of the gate call must equal Q.
+ *
+ * dsa_topk_expand: dsa_topk_pools followed by dsa_expand_selection on the same
+ * rows (arguments as there; sel and tok both written in full).  Errors: the
+ * union of theirs.
+ * ------------------------------------------------------------------------- */
+int dsa_gate_split_count(int M, int K, int N);
+size_t dsa_gate_compress_workspace_size(int M, int K, int N);
+dsa_status dsa_gate_compress(const float* hidden, const float* W, int M, int K, int N,
+                             float* gate_part, size_t gate_part_bytes, const uint16_t* k,
+                             const uint16_t* gate, const uint16_t* ape, const uint8_t* valid,
+                             const int32_t* tok_off, const int32_t* pool_off, const float* ln_w,
+                             const float* ln_b, float eps, int B, int D, int kpool, int max_cap,
+                             const int32_t* new_from, int max_new, uint16_t* keys,
+                             int32_t* pool_start, uint8_t* pool_valid, int32_t* n_pools,
+                             hipStream_t stream);
+dsa_status dsa_index_scores_gated(const uint16_t* qi, const float* gate_part, int nslices,
+                                  float* w, const uint16_t* keys, const int32_t* pool_start,
+                                  const uint8_t* pool_valid, const int32_t* pool_off,
+                                  const int32_t* n_pools, const int32_t* q_req,
+                                  const int32_t* q_pos, int Q, int H, int D, int kpool,
+                                  int pstride, float* scores, uint8_t* cand, hipStream_t stream);
+dsa_status dsa_topk_expand(const float* scores, const uint8_t* cand, int Q, int pstride,
+                           int select_k, const int32_t* pool_start, const int32_t* pool_off,
+                           const int32_t* q_req, int kpool, int out_width, int flags,
+                           int32_t* sel, int32_t* tok, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,6 +21,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// Two floats to packed bf16 (low half = lo), round to nearest even: one
+// v_cvt_pk_bf16_f32.  Matches f32_to_bf16_rne on every non-NaN input.
+typedef __bf16 bf16x2_vec __attribute__((ext_vector_type(2)));
+typedef float f32x2_vec __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_vec v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_vec));
+}
+
 // Word i of a uint4 (i a compile-time constant after unrolling).
 __device__ __forceinline__ uint32_t u4_word(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));

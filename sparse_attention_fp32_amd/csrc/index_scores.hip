@@ -10,6 +10,11 @@
 // tiles per wave in flight.  The relu, head weighting and head sum happen on
 // the accumulator: each lane holds 4 heads of one pool; two permlane swaps finish
 // the sum in a fixed order.
+//
+// Gated variant (dsa_index_scores_gated, fused decode path): the head weights
+// arrive as split-K partials of the head-gate (one per 128-wide K slice); each
+// workgroup adds them in slice order while its key rows load, and the first
+// workgroup of each query stores the sum as w.
 #include "dsa_device.hpp"
 #include "dsa_host.hpp"
 
@@ -20,14 +25,16 @@ using namespace dsa;
 constexpr int kTiles = 4;                  // 16-pool tiles per wave
 constexpr int kPoolsPerWG = 4 * kTiles * 16;  // 4 waves
 
-template <int KS>  // D / 32 k-steps
+constexpr int kMaxGateSlices = 64;  // 16 slice groups x 4 per thread
+
+template <int KS, bool GATED>  // D / 32 k-steps; w given as head-gate partials
 __global__ __launch_bounds__(256) void index_scores_kernel(
     const uint16_t* __restrict__ qi, const float* __restrict__ w,
     const uint16_t* __restrict__ keys, const int32_t* __restrict__ pool_start,
     const uint8_t* __restrict__ pool_valid, const int32_t* __restrict__ pool_off,
     const int32_t* __restrict__ n_pools, const int32_t* __restrict__ q_req,
     const int32_t* __restrict__ q_pos, int H, int kpool, int pstride, float* __restrict__ scores,
-    uint8_t* __restrict__ cand) {
+    uint8_t* __restrict__ cand, int nslices, float* __restrict__ w_out) {
   constexpr int D = KS * 32;
   const int q = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -71,11 +78,41 @@ __global__ __launch_bounds__(256) void index_scores_kernel(
     a[kk] = as_bf16x8(col < H ? v : make_uint4(0, 0, 0, 0));
   }
   float wr[4];
+  if (GATED) {
+    // w[q, h] = sum over slices of part[sl][q][h]: thread (group g, head h)
+    // adds slices g, g+16, g+32, g+48; the 16 group sums go in group order.
+    __shared__ float s_red[16][16];
+    __shared__ float s_w[16];
+    const int Q = gridDim.y;
+    const int t = threadIdx.x, h = t & 15, g = t >> 4;
+    float pv[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = grp * 4 + i;
-    const float v = w[(int64_t)q * H + (h < H ? h : H - 1)];
-    wr[i] = h < H ? v : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const int sl = min(g + 16 * i, nslices - 1);
+      pv[i] = w[((int64_t)sl * Q + q) * H + min(h, H - 1)];
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc += g + 16 * i < nslices ? pv[i] : 0.f;
+    s_red[g][h] = acc;
+    __syncthreads();
+    if (t < 16) {
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sum += s_red[j][t];
+      s_w[t] = sum;
+      if (w_out && blockIdx.x == 0 && t < H) w_out[(int64_t)q * H + t] = sum;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wr[i] = grp * 4 + i < H ? s_w[grp * 4 + i] : 0.f;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = grp * 4 + i;
+      const float v = w[(int64_t)q * H + (h < H ? h : H - 1)];
+      wr[i] = h < H ? v : 0.f;
+    }
   }
 
 #pragma unroll
@@ -101,38 +138,77 @@ __global__ __launch_bounds__(256) void index_scores_kernel(
 
 }  // namespace
 
+namespace {
+
+dsa_status launch_scores(const uint16_t* qi, const float* w, int nslices, float* w_out,
+                         const uint16_t* keys, const int32_t* pool_start,
+                         const uint8_t* pool_valid, const int32_t* pool_off,
+                         const int32_t* n_pools, const int32_t* q_req, const int32_t* q_pos,
+                         int Q, int H, int D, int kpool, int pstride, float* scores,
+                         uint8_t* cand, hipStream_t stream, const char* who) {
+  DSA_REQUIRE(H >= 1 && H <= DSA_MAX_INDEX_HEADS, DSA_ERR_INVALID_ARG, "%s: H=%d outside [1,%d]",
+              who, H, DSA_MAX_INDEX_HEADS);
+  DSA_REQUIRE(kpool >= 1 && kpool <= DSA_MAX_KPOOL, DSA_ERR_INVALID_ARG,
+              "%s: kpool=%d outside [1,%d]", who, kpool, DSA_MAX_KPOOL);
+  DSA_REQUIRE(D == 32 || D == 64 || D == 128 || D == 256, DSA_ERR_UNSUPPORTED,
+              "%s: D=%d not in {32,64,128,256}", who, D);
+  DSA_REQUIRE(pstride >= 1, DSA_ERR_INVALID_ARG, "%s: pstride=%d < 1", who, pstride);
+  DSA_REQUIRE(Q >= 0, DSA_ERR_INVALID_ARG, "%s: Q=%d < 0", who, Q);
+  DSA_REQUIRE(nslices >= 0 && nslices <= kMaxGateSlices, DSA_ERR_INVALID_ARG,
+              "%s: %d head-gate slices outside [1,%d]", who, nslices, kMaxGateSlices);
+  if (Q == 0) return DSA_OK;
+  DSA_REQUIRE(qi && w && keys && pool_start && pool_valid && pool_off && n_pools && q_req &&
+                  q_pos && scores && cand,
+              DSA_ERR_INVALID_ARG, "%s: NULL tensor pointer", who);
+  dim3 grid((pstride + kPoolsPerWG - 1) / kPoolsPerWG, Q);
+  DSA_REQUIRE(grid.y <= 65535u, DSA_ERR_UNSUPPORTED, "%s: Q=%d above 65535", who, Q);
+  if (dsa::trace_enabled())
+    fprintf(stderr, "[dsa] %s Q=%d H=%d D=%d pstride=%d slices=%d grid=(%d,%d)\n", who, Q, H, D,
+            pstride, nslices, grid.x, grid.y);
+#define DSA_LAUNCH_IS(KS, G)                                                               \
+  index_scores_kernel<KS, G><<<grid, 256, 0, stream>>>(qi, w, keys, pool_start, pool_valid, \
+                                                       pool_off, n_pools, q_req, q_pos, H,  \
+                                                       kpool, pstride, scores, cand, nslices, w_out)
+#define DSA_LAUNCH_IS_D(G)             \
+  switch (D / 32) {                    \
+    case 1: DSA_LAUNCH_IS(1, G); break; \
+    case 2: DSA_LAUNCH_IS(2, G); break; \
+    case 4: DSA_LAUNCH_IS(4, G); break; \
+    default: DSA_LAUNCH_IS(8, G); break; \
+  }
+  if (nslices > 0) {
+    DSA_LAUNCH_IS_D(true);
+  } else {
+    DSA_LAUNCH_IS_D(false);
+  }
+#undef DSA_LAUNCH_IS_D
+#undef DSA_LAUNCH_IS
+  return dsa::check_launch(who);
+}
+
+}  // namespace
+
 DSA_EXPORT dsa_status dsa_index_scores(const uint16_t* qi, const float* w, const uint16_t* keys,
                                        const int32_t* pool_start, const uint8_t* pool_valid,
                                        const int32_t* pool_off, const int32_t* n_pools,
                                        const int32_t* q_req, const int32_t* q_pos, int Q, int H,
                                        int D, int kpool, int pstride, float* scores,
                                        uint8_t* cand, hipStream_t stream) {
-  DSA_REQUIRE(H >= 1 && H <= DSA_MAX_INDEX_HEADS, DSA_ERR_INVALID_ARG,
-              "dsa_index_scores: H=%d outside [1,%d]", H, DSA_MAX_INDEX_HEADS);
-  DSA_REQUIRE(kpool >= 1 && kpool <= DSA_MAX_KPOOL, DSA_ERR_INVALID_ARG,
-              "dsa_index_scores: kpool=%d outside [1,%d]", kpool, DSA_MAX_KPOOL);
-  DSA_REQUIRE(D == 32 || D == 64 || D == 128 || D == 256, DSA_ERR_UNSUPPORTED,
-              "dsa_index_scores: D=%d not in {32,64,128,256}", D);
-  DSA_REQUIRE(pstride >= 1, DSA_ERR_INVALID_ARG, "dsa_index_scores: pstride=%d < 1", pstride);
-  DSA_REQUIRE(Q >= 0, DSA_ERR_INVALID_ARG, "dsa_index_scores: Q=%d < 0", Q);
-  if (Q == 0) return DSA_OK;
-  DSA_REQUIRE(qi && w && keys && pool_start && pool_valid && pool_off && n_pools && q_req &&
-                  q_pos && scores && cand,
-              DSA_ERR_INVALID_ARG, "dsa_index_scores: NULL tensor pointer");
-  dim3 grid((pstride + kPoolsPerWG - 1) / kPoolsPerWG, Q);
-  if (dsa::trace_enabled())
-    fprintf(stderr, "[dsa] index_scores Q=%d H=%d D=%d pstride=%d grid=(%d,%d)\n", Q, H, D,
-            pstride, grid.x, grid.y);
-#define DSA_LAUNCH_IS(KS)                                                               \
-  index_scores_kernel<KS><<<grid, 256, 0, stream>>>(qi, w, keys, pool_start, pool_valid, \
-                                                    pool_off, n_pools, q_req, q_pos, H,  \
-                                                    kpool, pstride, scores, cand)
-  switch (D / 32) {
-    case 1: DSA_LAUNCH_IS(1); break;
-    case 2: DSA_LAUNCH_IS(2); break;
-    case 4: DSA_LAUNCH_IS(4); break;
-    default: DSA_LAUNCH_IS(8); break;
-  }
-#undef DSA_LAUNCH_IS
-  return dsa::check_launch("dsa_index_scores");
+  return launch_scores(qi, w, 0, nullptr, keys, pool_start, pool_valid, pool_off, n_pools, q_req,
+                       q_pos, Q, H, D, kpool, pstride, scores, cand, stream, "dsa_index_scores");
+}
+
+DSA_EXPORT dsa_status dsa_index_scores_gated(const uint16_t* qi, const float* gate_part,
+                                             int nslices, float* w, const uint16_t* keys,
+                                             const int32_t* pool_start,
+                                             const uint8_t* pool_valid, const int32_t* pool_off,
+                                             const int32_t* n_pools, const int32_t* q_req,
+                                             const int32_t* q_pos, int Q, int H, int D,
+                                             int kpool, int pstride, float* scores,
+                                             uint8_t* cand, hipStream_t stream) {
+  DSA_REQUIRE(nslices >= 1, DSA_ERR_INVALID_ARG, "dsa_index_scores_gated: nslices=%d < 1",
+              nslices);
+  return launch_scores(qi, gate_part, nslices, w, keys, pool_start, pool_valid, pool_off, n_pools,
+                       q_req, q_pos, Q, H, D, kpool, pstride, scores, cand, stream,
+                       "dsa_index_scores_gated");
 }

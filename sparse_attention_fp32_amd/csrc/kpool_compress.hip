@@ -13,6 +13,13 @@
 // coalesced row reads.  Per-channel slot softmax is lane-local; the LayerNorm
 // mean and variance are DPP reductions over the pool's lanes.
 // HBM-bound (2*kpool*D*2 bytes in, D*2 out per pool): no MFMA.
+//
+// Fused decode variant (dsa_gate_compress): the head-gate of the same step is
+// independent of the compression, so the same launch also runs it, split over
+// K (stkernel PR #227's split-K) in workgroups placed after the compression
+// ones.  Each writes the partial products of one 128-wide K slice for 16 rows;
+// the index-score kernel adds the slices in a fixed order, so the gate leaves
+// the launch chain and stays deterministic.
 #include <limits.h>
 
 #include "dsa_device.hpp"
@@ -49,6 +56,67 @@ __device__ int first_valid_row(const uint8_t* __restrict__ valid, int64_t row0, 
   return f == INT_MAX ? -1 : f;
 }
 
+constexpr int kGateSlice = 128;  // K per gate partial
+constexpr int kGateRows = 16;    // gate rows per partial workgroup
+
+// Split-K head-gate work riding in a compression launch.
+struct GateArgs {
+  const float* hidden;  // [M, K] f32
+  const float* W;       // [K, N] f32
+  float* part;          // [nslices, M, N] f32: part[s] = hidden[:, slice s] @ W[slice s, :]
+  int M, K, N, nslices, nwg;  // nwg = nslices * ceil(M / 16); 0 = no gate work
+};
+
+// part[sl][m][n] for the 16 rows of tile mt, K slice sl; k added in order.
+__device__ void gate_partial(const GateArgs& ga, int g) {
+  __shared__ __attribute__((aligned(16))) float s_h[kGateRows][kGateSlice + 4];
+  __shared__ __attribute__((aligned(16))) float s_w[kGateSlice][16];
+  const int t = threadIdx.x;
+  const int sl = g % ga.nslices, m0 = (g / ga.nslices) * kGateRows;
+  const int k0 = sl * kGateSlice;
+  const int M = ga.M, K = ga.K, N = ga.N;
+  // hidden tile: row t/16, eight columns from 8*(t%16); rows past M clamped
+  {
+    const int hr = t >> 4, hc = (t & 15) * 8;
+    const float* hp = ga.hidden + (int64_t)min(m0 + hr, M - 1) * K + k0 + hc;
+    const float4 a = *(const float4*)hp, b = *(const float4*)(hp + 4);
+    float4* dst = (float4*)&s_h[hr][hc];
+    dst[0] = a;
+    dst[1] = b;
+  }
+  // W tile: k row t/2, eight outputs from 8*(t%2); outputs past N are zero
+  {
+    const int kr = t >> 1, n0 = (t & 1) * 8;
+    const float* wp = ga.W + (int64_t)(k0 + kr) * N;
+    float v[8];
+    if (N == 16) {
+      const float4 a = *(const float4*)(wp + n0), b = *(const float4*)(wp + n0 + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = wp[min(n0 + j, N - 1)];
+        v[j] = n0 + j < N ? x : 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s_w[kr][n0 + j] = v[j];
+  }
+  __syncthreads();
+  const int m = t >> 4, n = t & 15;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int k = 0; k < kGateSlice; k += 4) {
+    const float4 h = *(const float4*)&s_h[m][k];
+    acc = fmaf(h.x, s_w[k][n], acc);
+    acc = fmaf(h.y, s_w[k + 1][n], acc);
+    acc = fmaf(h.z, s_w[k + 2][n], acc);
+    acc = fmaf(h.w, s_w[k + 3][n], acc);
+  }
+  if (m0 + m < M && n < N) ga.part[((int64_t)sl * M + m0 + m) * N + n] = acc;
+}
+
 template <int LPP, int KP>  // lanes per pool = D / 8; pool slots
 __global__ __launch_bounds__(256) void kpool_compress_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ gate,
@@ -57,11 +125,16 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
     const float* __restrict__ ln_w, const float* __restrict__ ln_b, float eps,
     const int32_t* __restrict__ new_from, int pools_per_wg, uint16_t* __restrict__ keys,
     int32_t* __restrict__ pool_start, uint8_t* __restrict__ pool_valid,
-    int32_t* __restrict__ n_pools) {
+    int32_t* __restrict__ n_pools, int B, GateArgs ga) {
   constexpr int D = LPP * 8;
   constexpr int kpool = KP;
   constexpr int kGroups = 256 / LPP;  // pools in flight per workgroup
   __shared__ int s_first;
+  if ((int)blockIdx.y >= B) {  // head-gate workgroups of the fused launch
+    const int g = (blockIdx.y - B) * gridDim.x + blockIdx.x;
+    if (g < ga.nwg) gate_partial(ga, g);
+    return;
+  }
   const int r = blockIdx.y;
   const int t = threadIdx.x;
   const int64_t row0 = tok_off[r];
@@ -170,7 +243,7 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
     for (int c = 0; c < 8; c += 2) {
       const float y0 = (x[c] - mean) * rstd * lw[c] + lb[c];
       const float y1 = (x[c + 1] - mean) * rstd * lw[c + 1] + lb[c + 1];
-      packed[c >> 1] = f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16);
+      packed[c >> 1] = pack_bf16x2(y0, y1);
     }
     *(uint4*)kout = make_uint4(packed[0], packed[1], packed[2], packed[3]);
     if (li == 0) {
@@ -182,14 +255,10 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
 
 }  // namespace
 
-DSA_EXPORT dsa_status dsa_kpool_compress(const uint16_t* k, const uint16_t* gate,
-                                         const uint16_t* ape, const uint8_t* valid,
-                                         const int32_t* tok_off, const int32_t* pool_off,
-                                         const float* ln_w, const float* ln_b, float eps, int B,
-                                         int D, int kpool, int max_cap, const int32_t* new_from,
-                                         int max_new, uint16_t* keys, int32_t* pool_start,
-                                         uint8_t* pool_valid, int32_t* n_pools,
-                                         hipStream_t stream) {
+namespace {
+
+dsa_status check_compress_args(int B, int D, int kpool, int max_cap, const int32_t* new_from,
+                               int max_new, float eps) {
   DSA_REQUIRE(kpool >= 1 && kpool <= DSA_MAX_KPOOL, DSA_ERR_INVALID_ARG,
               "dsa_kpool_compress: kpool=%d outside [1,%d] (larger pools are refused, never "
               "truncated)",
@@ -201,10 +270,17 @@ DSA_EXPORT dsa_status dsa_kpool_compress(const uint16_t* k, const uint16_t* gate
   DSA_REQUIRE(!new_from || max_new >= 1, DSA_ERR_INVALID_ARG,
               "dsa_kpool_compress: max_new=%d < 1 with new_from", max_new);
   DSA_REQUIRE(eps >= 0.f, DSA_ERR_INVALID_ARG, "dsa_kpool_compress: eps < 0");
-  if (B == 0) return DSA_OK;
-  DSA_REQUIRE(k && gate && ape && valid && tok_off && pool_off && ln_w && ln_b && keys &&
-                  pool_start && pool_valid && n_pools,
-              DSA_ERR_INVALID_ARG, "dsa_kpool_compress: NULL tensor pointer");
+  return DSA_OK;
+}
+
+// One launch: B rows of compression workgroups, then ga.nwg gate workgroups.
+dsa_status launch_compress(const uint16_t* k, const uint16_t* gate, const uint16_t* ape,
+                           const uint8_t* valid, const int32_t* tok_off, const int32_t* pool_off,
+                           const float* ln_w, const float* ln_b, float eps, int B, int D,
+                           int kpool, int max_cap, const int32_t* new_from, int max_new,
+                           uint16_t* keys, int32_t* pool_start, uint8_t* pool_valid,
+                           int32_t* n_pools, const GateArgs& ga, hipStream_t stream,
+                           const char* who) {
   const int lpp = D / 8;
   const int groups = 256 / lpp;
   int ppw, nx;
@@ -217,14 +293,16 @@ DSA_EXPORT dsa_status dsa_kpool_compress(const uint16_t* k, const uint16_t* gate
     nx = (max_cap + ppw - 1) / ppw;
   }
   if (nx < 1) nx = 1;  // n_pools is written even with no slots
-  dim3 grid(nx, B);
+  const int gate_rows = (ga.nwg + nx - 1) / nx;
+  dim3 grid(nx, B + gate_rows);
   if (dsa::trace_enabled())
-    fprintf(stderr, "[dsa] kpool_compress B=%d D=%d kpool=%d max_cap=%d inc=%d grid=(%d,%d)\n",
-            B, D, kpool, max_cap, new_from != nullptr, grid.x, grid.y);
-#define DSA_LAUNCH_KP(LPP, KP)                                                            \
-  kpool_compress_kernel<LPP, KP><<<grid, 256, 0, stream>>>(                                \
+    fprintf(stderr,
+            "[dsa] %s B=%d D=%d kpool=%d max_cap=%d inc=%d gate_wg=%d grid=(%d,%d)\n", who, B,
+            D, kpool, max_cap, new_from != nullptr, ga.nwg, grid.x, grid.y);
+#define DSA_LAUNCH_KP(LPP, KP)                                                                 \
+  kpool_compress_kernel<LPP, KP><<<grid, 256, 0, stream>>>(                                     \
       k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b, eps, new_from, ppw, keys, pool_start, \
-      pool_valid, n_pools)
+      pool_valid, n_pools, B, ga)
 #define DSA_LAUNCH_KP_D(KP)            \
   switch (lpp) {                       \
     case 4: DSA_LAUNCH_KP(4, KP); break;   \
@@ -244,5 +322,86 @@ DSA_EXPORT dsa_status dsa_kpool_compress(const uint16_t* k, const uint16_t* gate
   }
 #undef DSA_LAUNCH_KP_D
 #undef DSA_LAUNCH_KP
-  return dsa::check_launch("dsa_kpool_compress");
+  return dsa::check_launch(who);
+}
+
+// K slices of the split head-gate, or 1 when the dense head-gate call serves
+// (then the "partials" buffer holds w itself).
+int gate_slices(int M, int K) {
+  if (M >= 1 && M <= 64 && K >= kGateSlice && K % kGateSlice == 0 && K / kGateSlice <= 64)
+    return K / kGateSlice;
+  return 1;
+}
+
+}  // namespace
+
+DSA_EXPORT dsa_status dsa_kpool_compress(const uint16_t* k, const uint16_t* gate,
+                                         const uint16_t* ape, const uint8_t* valid,
+                                         const int32_t* tok_off, const int32_t* pool_off,
+                                         const float* ln_w, const float* ln_b, float eps, int B,
+                                         int D, int kpool, int max_cap, const int32_t* new_from,
+                                         int max_new, uint16_t* keys, int32_t* pool_start,
+                                         uint8_t* pool_valid, int32_t* n_pools,
+                                         hipStream_t stream) {
+  const dsa_status st = check_compress_args(B, D, kpool, max_cap, new_from, max_new, eps);
+  if (st != DSA_OK) return st;
+  if (B == 0) return DSA_OK;
+  DSA_REQUIRE(k && gate && ape && valid && tok_off && pool_off && ln_w && ln_b && keys &&
+                  pool_start && pool_valid && n_pools,
+              DSA_ERR_INVALID_ARG, "dsa_kpool_compress: NULL tensor pointer");
+  return launch_compress(k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b, eps, B, D, kpool,
+                         max_cap, new_from, max_new, keys, pool_start, pool_valid, n_pools,
+                         GateArgs{}, stream, "dsa_kpool_compress");
+}
+
+DSA_EXPORT int dsa_gate_split_count(int M, int K, int N) {
+  if (M < 0 || K < 1 || N < 1 || N > DSA_MAX_INDEX_HEADS) return 0;
+  return gate_slices(M, K);
+}
+
+DSA_EXPORT size_t dsa_gate_compress_workspace_size(int M, int K, int N) {
+  const int ns = dsa_gate_split_count(M, K, N);
+  if (ns < 1 || M < 1) return 0;
+  return (size_t)ns * M * N * sizeof(float);
+}
+
+DSA_EXPORT dsa_status dsa_gate_compress(const float* hidden, const float* W, int M, int K, int N,
+                                        float* gate_part, size_t gate_part_bytes,
+                                        const uint16_t* k, const uint16_t* gate,
+                                        const uint16_t* ape, const uint8_t* valid,
+                                        const int32_t* tok_off, const int32_t* pool_off,
+                                        const float* ln_w, const float* ln_b, float eps, int B,
+                                        int D, int kpool, int max_cap, const int32_t* new_from,
+                                        int max_new, uint16_t* keys, int32_t* pool_start,
+                                        uint8_t* pool_valid, int32_t* n_pools,
+                                        hipStream_t stream) {
+  DSA_REQUIRE(N >= 1 && N <= DSA_MAX_INDEX_HEADS, DSA_ERR_INVALID_ARG,
+              "dsa_gate_compress: N=%d outside [1,%d]", N, DSA_MAX_INDEX_HEADS);
+  DSA_REQUIRE(M >= 0 && K >= 1, DSA_ERR_INVALID_ARG, "dsa_gate_compress: M=%d K=%d", M, K);
+  const dsa_status st = check_compress_args(B, D, kpool, max_cap, new_from, max_new, eps);
+  if (st != DSA_OK) return st;
+  const size_t need = dsa_gate_compress_workspace_size(M, K, N);
+  DSA_REQUIRE(M == 0 || (gate_part && gate_part_bytes >= need), DSA_ERR_INVALID_ARG,
+              "dsa_gate_compress: gate partials %zu bytes, need %zu", gate_part_bytes, need);
+  DSA_REQUIRE(M == 0 || (hidden && W), DSA_ERR_INVALID_ARG,
+              "dsa_gate_compress: NULL tensor pointer");
+  DSA_REQUIRE(B == 0 || (k && gate && ape && valid && tok_off && pool_off && ln_w && ln_b &&
+                         keys && pool_start && pool_valid && n_pools),
+              DSA_ERR_INVALID_ARG, "dsa_gate_compress: NULL tensor pointer");
+  const int ns = gate_slices(M, K);
+  if (M > 0 && ns == 1) {  // dense head-gate: the partials buffer receives w
+    const dsa_status g = dsa_head_gate(hidden, W, gate_part, M, K, N, nullptr, 0, stream);
+    if (g != DSA_OK) return g;
+    if (B == 0) return DSA_OK;
+    return launch_compress(k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b, eps, B, D, kpool,
+                           max_cap, new_from, max_new, keys, pool_start, pool_valid, n_pools,
+                           GateArgs{}, stream, "dsa_gate_compress");
+  }
+  GateArgs ga{hidden, W, gate_part, M, K, N, ns, M > 0 ? ns * ((M + kGateRows - 1) / kGateRows) : 0};
+  if (B == 0 && ga.nwg == 0) return DSA_OK;
+  // with B == 0 the launch holds only gate workgroups (its compression
+  // arguments are never read)
+  return launch_compress(k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b, eps, B, D, kpool,
+                         max_cap, new_from, max_new, keys, pool_start, pool_valid, n_pools, ga,
+                         stream, "dsa_gate_compress");
 }

@@ -40,7 +40,7 @@ constexpr int kSlice = 128;               // latent dims per wave
 constexpr int kSliceRow = kSlice * 2 + 16;  // LDS bytes per token row of a slice (+pad)
 constexpr int kTargetWG = 256;            // aim for one workgroup per CU
 constexpr int kMinSubPerChunk = 4;        // >= 128 ids per chunk keeps partials small
-constexpr int kMaxTch = 2048;             // ids per chunk staged in LDS
+constexpr int kMaxTch = 2048;             // most ids per chunk
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -108,23 +108,37 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
   __shared__ __attribute__((aligned(16))) float s_bias[kSub];  // 0, or -inf for no token
   __shared__ __attribute__((aligned(16))) float s_scl[kSub];   // row scale (1 for bf16)
   __shared__ float s_lrun[64];
-  __shared__ int s_id[kMaxTch];
-  __shared__ int s_safe;
 
   const int chunk = blockIdx.x, nchunks = gridDim.x, hb = blockIdx.y, qx = blockIdx.z;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int r = q_req[qx];
-  const int64_t rowbase = kv_off[r];
   const int j0 = chunk * tch;
   const int j1 = min(out_width, j0 + tch);
   const int nsub = j1 > j0 ? (j1 - j0 + kSub - 1) / kSub : 0;
   const int32_t* trow = tok + (int64_t)qx * out_width;
   const int dim0 = w * kSlice;  // this wave's latent slice
+  constexpr int kRowBytes = FP8 ? L : 2 * L;
+  // Source of the loads for a token slot with no id: this query's own Q row
+  // (always readable, at least one latent row long); the data is zeroed.
+  const uint8_t* dummy = (const uint8_t*)(q + (int64_t)qx * Hm * L);
 
-  // Stage the chunk's ids while the Q^T operand loads:
-  // qb[ht][kk] = Q[head hb*64 + ht*16 + col][dim0 + kk*32 + grp*8 .. +8].
-  if (t == 0) s_safe = -1;
+  // Ids of sub-chunk s for this lane's two rows (tokens tt*16 + col), -1 past
+  // the chunk.  Every wave and lane group holds the same ids, so any decision
+  // taken on them is uniform over the workgroup.
+  auto load_ids = [&](int s, int (&id)[2]) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int j = j0 + s * kSub + tt * 16 + col;
+      const int v = trow[min(j, max(j1 - 1, 0))];
+      id[tt] = j < j1 ? v : -1;
+    }
+  };
+  int idA[2], idB[2];  // ids of the sub-chunk in registers, and of the next one
+  load_ids(0, idA);
+  load_ids(1, idB);
+  const int r = q_req[qx];
+
+  // Q^T operand: qb[ht][kk] = Q[head hb*64 + ht*16 + col][dim0 + kk*32 + grp*8 .. +8]
   bf16x8_t qb[4][4];
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) {
@@ -136,17 +150,7 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
       qb[ht][kk] = as_bf16x8(h < Hm ? v : make_uint4(0, 0, 0, 0));
     }
   }
-  __syncthreads();
-  for (int i = t; i < nsub * kSub; i += 256) {
-    const int j = j0 + i;
-    const int id = trow[j < j1 ? j : j1 - 1];
-    const int v = j < j1 ? id : -1;
-    s_id[i] = v;
-    if (v >= 0) atomicMax(&s_safe, v);
-  }
-  __syncthreads();
-  const int safe = s_safe;
-  const int nwork = safe >= 0 ? nsub : 0;  // a chunk with no selected id has no work
+  const int64_t rowbase = kv_off[r];
 
   f32x4_t o[4][8];  // [head tile][e]: O[head ht*16 + grp*4 + i][dim0 + 8*col + e]
 #pragma unroll
@@ -156,150 +160,171 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
   float m_run = -INFINITY, l_run = 0.f;  // head w*16 + col (wave w owns head tile w)
 
   RowSlice<FP8> cr;
-  float pre_scl = 1.f;
-  auto gather = [&](int s) {
+  float scl[2] = {1.f, 1.f};  // row scales of tokens col, 16 + col (wave 0, lanes < 16)
+  auto gather = [&](const int (&id)[2]) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const int id = s_id[s * kSub + tt * 16 + col];
-      const int64_t g = rowbase + (id >= 0 ? id : safe);
+      const uint8_t* src = id[tt] >= 0 ? (const uint8_t*)ckv_v + (rowbase + id[tt]) * kRowBytes : dummy;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int d = dim0 + kk * 32 + grp * 8;
         if (FP8)
-          ((uint2*)cr.v[tt])[kk] = *(const uint2*)((const uint8_t*)ckv_v + g * L + d);
+          ((uint2*)cr.v[tt])[kk] = *(const uint2*)(src + d);
         else
-          ((uint4*)cr.v[tt])[kk] = *(const uint4*)((const uint16_t*)ckv_v + g * L + d);
+          ((uint4*)cr.v[tt])[kk] = *(const uint4*)(src + 2 * d);
       }
-    }
-    if (t < kSub) {
-      const int id = s_id[s * kSub + t];
-      pre_scl = FP8 ? ckv_scale[rowbase + (id >= 0 ? id : safe)] : 1.f;
+      if (FP8 && t < 16) {
+        const float* sp = id[tt] >= 0 ? ckv_scale + rowbase + id[tt] : (const float*)dummy;
+        const float v = *sp;
+        scl[tt] = id[tt] >= 0 ? v : 0.f;
+      }
     }
   };
-  if (nwork > 0) gather(0);
+  gather(idA);
 
   uint8_t* my_slice = s_slice[w];
-  for (int s = 0; s < nwork; ++s) {
-    // per-token logit multiplier and mask of this sub-chunk
-    if (t < kSub) {
-      const int id = s_id[s * kSub + t];
-      s_mul[t] = sm_log2 * pre_scl;
-      s_bias[t] = id >= 0 ? 0.f : -INFINITY;
-      s_scl[t] = pre_scl;
-    }
-    // partial S^T over this wave's dims, and the slice into LDS for PV
+  for (int s = 0; s < nsub; ++s) {
+    int idC[2];
+    load_ids(s + 2, idC);
+    const bool live = __any(idA[0] >= 0 || idA[1] >= 0);  // uniform over the workgroup
     f32x4_t sacc[4][2];
+    if (live) {
+      // per-token logit multiplier and mask of this sub-chunk
+      if (t < 16) {
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht)
+        for (int tt = 0; tt < 2; ++tt) {
+          s_mul[tt * 16 + t] = sm_log2 * scl[tt];
+          s_bias[tt * 16 + t] = idA[tt] >= 0 ? 0.f : -INFINITY;
+          s_scl[tt * 16 + t] = scl[tt];
+        }
+      }
+      // partial S^T over this wave's dims, and the slice into LDS for PV
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) sacc[ht][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+        for (int tt = 0; tt < 2; ++tt) sacc[ht][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint4 a = FP8 ? widen_fp8x8(((const uint2*)cr.v[tt])[kk]) : ((const uint4*)cr.v[tt])[kk];
-        *(uint4*)(my_slice + (tt * 16 + col) * kSliceRow + (kk * 32 + grp * 8) * 2) = a;
+      for (int tt = 0; tt < 2; ++tt) {
+        const bool ok = idA[tt] >= 0;
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) sacc[ht][tt] = mfma16x16x32(as_bf16x8(a), qb[ht][kk], sacc[ht][tt]);
+        for (int kk = 0; kk < 4; ++kk) {
+          uint4 a;
+          if (FP8) {
+            const uint2 raw = ((const uint2*)cr.v[tt])[kk];
+            a = widen_fp8x8(ok ? raw : make_uint2(0, 0));
+          } else {
+            const uint4 raw = ((const uint4*)cr.v[tt])[kk];
+            a = ok ? raw : make_uint4(0, 0, 0, 0);
+          }
+          *(uint4*)(my_slice + (tt * 16 + col) * kSliceRow + (kk * 32 + grp * 8) * 2) = a;
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht) sacc[ht][tt] = mfma16x16x32(as_bf16x8(a), qb[ht][kk], sacc[ht][tt]);
+        }
       }
     }
-    if (s + 1 < nwork) gather(s + 1);  // the next rows load while this sub-chunk computes
+    if (s + 1 < nsub) gather(idB);  // the next rows load while this sub-chunk computes
+    if (live) {
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht)
+      for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) s_exch[w][ht][tt][lane] = sacc[ht][tt];
-    __syncthreads();
+        for (int tt = 0; tt < 2; ++tt) s_exch[w][ht][tt][lane] = sacc[ht][tt];
+      __syncthreads();
 
-    // wave w: full S^T of head tile w, softmax, P
-    float x[8];
+      // wave w: full S^T of head tile w, softmax, P
+      float x[8];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const f32x4_t a0 = s_exch[0][w][tt][lane], a1 = s_exch[1][w][tt][lane];
-      const f32x4_t a2 = s_exch[2][w][tt][lane], a3 = s_exch[3][w][tt][lane];
-      const float4 mul = *(const float4*)(s_mul + tt * 16 + grp * 4);
-      const float4 bias = *(const float4*)(s_bias + tt * 16 + grp * 4);
-      const float mu[4] = {mul.x, mul.y, mul.z, mul.w};
-      const float bi[4] = {bias.x, bias.y, bias.z, bias.w};
+      for (int tt = 0; tt < 2; ++tt) {
+        const f32x4_t a0 = s_exch[0][w][tt][lane], a1 = s_exch[1][w][tt][lane];
+        const f32x4_t a2 = s_exch[2][w][tt][lane], a3 = s_exch[3][w][tt][lane];
+        const float4 mul = *(const float4*)(s_mul + tt * 16 + grp * 4);
+        const float4 bias = *(const float4*)(s_bias + tt * 16 + grp * 4);
+        const float mu[4] = {mul.x, mul.y, mul.z, mul.w};
+        const float bi[4] = {bias.x, bias.y, bias.z, bias.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[tt * 4 + i] = fmaf(((a0[i] + a1[i]) + a2[i]) + a3[i], mu[i], bi[i]);
-    }
-    float mloc = x[0];
-#pragma unroll
-    for (int k = 1; k < 8; ++k) mloc = fmaxf(mloc, x[k]);
-    mloc = rows_max(mloc);
-    const bool move = mloc > m_run + 8.f;
-    const bool any_move = __any(move);
-    if (any_move) {
-      const float alpha = move ? exp2f(m_run - mloc) : 1.f;  // exp2(-inf) = 0
-      if (move) m_run = mloc;
-      l_run *= alpha;
-      if (grp == 0) s_alpha[w * 16 + col] = alpha;
-    }
-    if (lane == 0) s_moved[w] = any_move;
-    const bool none = m_run == -INFINITY;
-    float p[8];
-    float psum = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      p[k] = none ? 0.f : exp2f(x[k] - m_run);
-      psum += p[k];
-    }
-    l_run += rows_sum(psum);
-    {
-      uint32_t pw[4];
-      float sc[8];
-      if (FP8) {
-        const float4 s0 = *(const float4*)(s_scl + grp * 4);
-        const float4 s1 = *(const float4*)(s_scl + 16 + grp * 4);
-        sc[0] = s0.x; sc[1] = s0.y; sc[2] = s0.z; sc[3] = s0.w;
-        sc[4] = s1.x; sc[5] = s1.y; sc[6] = s1.z; sc[7] = s1.w;
+        for (int i = 0; i < 4; ++i) x[tt * 4 + i] = fmaf(((a0[i] + a1[i]) + a2[i]) + a3[i], mu[i], bi[i]);
       }
+      float mloc = x[0];
 #pragma unroll
-      for (int k = 0; k < 8; k += 2) {
-        const float p0 = FP8 ? p[k] * sc[k] : p[k], p1 = FP8 ? p[k + 1] * sc[k + 1] : p[k + 1];
-        pw[k >> 1] = f32_to_bf16_rne(p0) | (f32_to_bf16_rne(p1) << 16);
+      for (int k = 1; k < 8; ++k) mloc = fmaxf(mloc, x[k]);
+      mloc = rows_max(mloc);
+      const bool move = mloc > m_run + 8.f;
+      const bool any_move = __any(move);
+      if (any_move) {
+        const float alpha = move ? exp2f(m_run - mloc) : 1.f;  // exp2(-inf) = 0
+        if (move) m_run = mloc;
+        l_run *= alpha;
+        if (grp == 0) s_alpha[w * 16 + col] = alpha;
       }
-      s_p[w][lane] = make_uint4(pw[0], pw[1], pw[2], pw[3]);
-    }
-    __syncthreads();
+      if (lane == 0) s_moved[w] = any_move;
+      const bool none = m_run == -INFINITY;
+      float p[8];
+      float psum = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        p[k] = none ? 0.f : exp2f(x[k] - m_run);
+        psum += p[k];
+      }
+      l_run += rows_sum(psum);
+      {
+        uint32_t pw[4];
+        float sc[8];
+        if (FP8) {
+          const float4 s0 = *(const float4*)(s_scl + grp * 4);
+          const float4 s1 = *(const float4*)(s_scl + 16 + grp * 4);
+          sc[0] = s0.x; sc[1] = s0.y; sc[2] = s0.z; sc[3] = s0.w;
+          sc[4] = s1.x; sc[5] = s1.y; sc[6] = s1.z; sc[7] = s1.w;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; k += 2) {
+          const float p0 = FP8 ? p[k] * sc[k] : p[k], p1 = FP8 ? p[k + 1] * sc[k + 1] : p[k + 1];
+          pw[k >> 1] = pack_bf16x2(p0, p1);
+        }
+        s_p[w][lane] = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+      }
+      __syncthreads();
 
-    // rescale O where a head tile moved its reference max (rare)
-    if (s_moved[0] | s_moved[1] | s_moved[2] | s_moved[3]) {
+      // rescale O where a head tile moved its reference max (rare)
+      if (s_moved[0] | s_moved[1] | s_moved[2] | s_moved[3]) {
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
-        if (!s_moved[ht]) continue;
-        float ai[4];
+        for (int ht = 0; ht < 4; ++ht) {
+          if (!s_moved[ht]) continue;
+          float ai[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ai[i] = s_alpha[ht * 16 + grp * 4 + i];
+          for (int i = 0; i < 4; ++i) ai[i] = s_alpha[ht * 16 + grp * 4 + i];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+          for (int e = 0; e < 8; ++e)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o[ht][e][i] *= ai[i];
+            for (int i = 0; i < 4; ++i) o[ht][e][i] *= ai[i];
+        }
+      }
+      // PV over this wave's slice
+      bf16x8_t pa[4];
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) pa[ht] = as_bf16x8(s_p[ht][lane]);
+      uint4 u[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int tk = (j < 4 ? 0 : 16) + grp * 4 + (j & 3);
+        u[j] = *(const uint4*)(my_slice + tk * kSliceRow + col * 16);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int wd = e >> 1;
+        uint32_t bw[4];
+#pragma unroll
+        for (int m2 = 0; m2 < 4; ++m2) {
+          const uint32_t a0 = u4_word(u[2 * m2], wd), a1 = u4_word(u[2 * m2 + 1], wd);
+          bw[m2] = (e & 1) ? hi_pair(a0, a1) : lo_pair(a0, a1);
+        }
+        const bf16x8_t bv = as_bf16x8(make_uint4(bw[0], bw[1], bw[2], bw[3]));
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) o[ht][e] = mfma16x16x32(pa[ht], bv, o[ht][e]);
       }
     }
-    // PV over this wave's slice
-    bf16x8_t pa[4];
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht) pa[ht] = as_bf16x8(s_p[ht][lane]);
-    uint4 u[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int tk = (j < 4 ? 0 : 16) + grp * 4 + (j & 3);
-      u[j] = *(const uint4*)(my_slice + tk * kSliceRow + col * 16);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int wd = e >> 1;
-      uint32_t bw[4];
-#pragma unroll
-      for (int m2 = 0; m2 < 4; ++m2) {
-        const uint32_t a0 = u4_word(u[2 * m2], wd), a1 = u4_word(u[2 * m2 + 1], wd);
-        bw[m2] = (e & 1) ? hi_pair(a0, a1) : lo_pair(a0, a1);
-      }
-      const bf16x8_t bv = as_bf16x8(make_uint4(bw[0], bw[1], bw[2], bw[3]));
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht) o[ht][e] = mfma16x16x32(pa[ht], bv, o[ht][e]);
-    }
+    idA[0] = idB[0];
+    idA[1] = idB[1];
+    idB[0] = idC[0];
+    idB[1] = idC[1];
   }
 
   // epilogue: per-head sums to every wave, then this wave's dims of all heads
@@ -316,8 +341,7 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
         const float inv = lv > 0.f ? 1.f / lv : 0.f;
         uint32_t pk[4];
 #pragma unroll
-        for (int e = 0; e < 8; e += 2)
-          pk[e >> 1] = f32_to_bf16_rne(o[ht][e][i] * inv) | (f32_to_bf16_rne(o[ht][e + 1][i] * inv) << 16);
+        for (int e = 0; e < 8; e += 2) pk[e >> 1] = pack_bf16x2(o[ht][e][i] * inv, o[ht][e + 1][i] * inv);
         *(uint4*)(out + ((int64_t)qx * Hm + h) * L + dim0 + col * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       }
     const int hq = hb * 64 + w * 16 + col;
@@ -333,8 +357,7 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
         if (h >= Hm) continue;
         uint32_t pk[4];
 #pragma unroll
-        for (int e = 0; e < 8; e += 2)
-          pk[e >> 1] = f32_to_bf16_rne(o[ht][e][i]) | (f32_to_bf16_rne(o[ht][e + 1][i]) << 16);
+        for (int e = 0; e < 8; e += 2) pk[e >> 1] = pack_bf16x2(o[ht][e][i], o[ht][e + 1][i]);
         *(uint4*)(part_o + (pbase + h) * L + dim0 + col * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       }
     const int hq = hb * 64 + w * 16 + col;
@@ -357,8 +380,8 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const uint16_t* __rest
   const int h = blockIdx.x * 4 + (threadIdx.x >> 6), qx = blockIdx.y, lane = threadIdx.x & 63;
   if (h >= Hm) return;
   const int64_t b0 = (int64_t)qx * nchunks * Hm + h;
+  // the running reference max M only grows: each batch rescales what came before
   float M = -INFINITY;
-  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, part_ml[(b0 + (int64_t)c * Hm) * 2]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
   for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
@@ -370,6 +393,16 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const uint16_t* __rest
       const int64_t pc = b0 + (int64_t)c * Hm;
       v[k] = *(const uint4*)(part_o + pc * L + lane * 8);
       ml[k] = *(const float2*)(part_ml + pc * 2);
+    }
+    float Mb = M;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) Mb = c0 + k < nchunks ? fmaxf(Mb, ml[k].x) : Mb;
+    if (Mb != M) {  // exp2(-inf) = 0 clears the (empty) history
+      const float a = M == -INFINITY ? 0.f : exp2f(M - Mb);
+      lsum *= a;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[d] *= a;
+      M = Mb;
     }
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
@@ -385,8 +418,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const uint16_t* __rest
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   uint32_t pk[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
-    pk[k] = f32_to_bf16_rne(acc[2 * k] * inv) | (f32_to_bf16_rne(acc[2 * k + 1] * inv) << 16);
+  for (int k = 0; k < 4; ++k) pk[k] = pack_bf16x2(acc[2 * k] * inv, acc[2 * k + 1] * inv);
   *(uint4*)(out + ((int64_t)qx * Hm + h) * L + lane * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
   if (lse && lane == 0)
     lse[(int64_t)qx * Hm + h] = lsum > 0.f ? (M + log2f(lsum)) * kLn2 : -INFINITY;

@@ -17,6 +17,9 @@
 //  4. Keys above T are kept and, among keys equal to T, the lowest ids; kept
 //     ids are compacted in id order with wave ballots and per-(e, wave)
 //     offsets.
+// The fused variant (dsa_topk_expand) also writes the expanded token ids of
+// each kept pool (a5): the pools' start rows are loaded beside the scores, so
+// the expansion adds no dependent load and no launch.
 #include "dsa_device.hpp"
 #include "dsa_host.hpp"
 
@@ -33,11 +36,20 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-template <int E>
+// Expansion arguments of the fused variant (a5): token row of each kept pool.
+struct ExpandArgs {
+  const int32_t* pool_start;
+  const int32_t* pool_off;
+  const int32_t* q_req;
+  int kpool, out_width;
+  int32_t* tok;
+};
+
+template <int E, bool EXPAND>
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores,
                                                         const uint8_t* __restrict__ cand,
                                                         int pstride, int select_k,
-                                                        int32_t* __restrict__ sel) {
+                                                        int32_t* __restrict__ sel, ExpandArgs ex) {
   __shared__ int hist[kWaves][256];
   __shared__ int s_tot[256];
   __shared__ uint32_t s_max[kWaves];
@@ -58,6 +70,22 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     const int id = min(t + kThreads * e, pstride - 1);
     sv[e] = srow[id];
     cv[e] = crow[id];
+  }
+  // fused expansion: start rows of this request's pool slots (ids clamped to
+  // the request's slots; a candidate is always one of them)
+  int32_t ps[EXPAND ? E : 1];
+  int32_t* trow = nullptr;
+  if (EXPAND) {
+    const int r = ex.q_req[q];
+    const int pb = ex.pool_off[r], cap = ex.pool_off[r + 1] - pb;
+    trow = ex.tok + (int64_t)q * ex.out_width;
+    if (cap > 0) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) ps[e] = ex.pool_start[pb + min(t + kThreads * e, cap - 1)];
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) ps[e] = -1;
+    }
   }
   uint32_t key[E];
   uint32_t kmx = 0u;
@@ -85,6 +113,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   const int k_eff = min(select_k, ncand);
   if (k_eff == 0) {
     for (int i = t; i < select_k; i += kThreads) out[i] = -1;
+    if (EXPAND)
+      for (int i = t; i < ex.out_width; i += kThreads) trow[i] = -1;
     return;
   }
   const uint32_t top9 = kmax >> 23;
@@ -256,10 +286,34 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
         base += c;
       }
       const int pos = mine + lanes_below(bk[e]);
-      if (keep[e] && pos < k_eff) out[pos] = t + kThreads * e;
+      if (keep[e] && pos < k_eff) {
+        out[pos] = t + kThreads * e;
+        if (EXPAND)
+          for (int s = 0; s < ex.kpool; ++s) trow[pos * ex.kpool + s] = ps[e] + s;
+      }
     }
   }
   for (int i = k_eff + t; i < select_k; i += kThreads) out[i] = -1;
+  if (EXPAND)
+    for (int i = k_eff * ex.kpool + t; i < ex.out_width; i += kThreads) trow[i] = -1;
+}
+
+template <bool EXPAND>
+dsa_status launch_topk(const float* scores, const uint8_t* cand, int Q, int pstride, int select_k,
+                       int32_t* sel, const ExpandArgs& ex, hipStream_t stream) {
+  const int need = (pstride + kThreads - 1) / kThreads;
+  if (dsa::trace_enabled())
+    fprintf(stderr, "[dsa] topk_pools Q=%d pstride=%d select_k=%d E=%d expand=%d\n", Q, pstride,
+            select_k, need, (int)EXPAND);
+#define DSA_LAUNCH_TK(E) \
+  topk_kernel<E, EXPAND><<<Q, kThreads, 0, stream>>>(scores, cand, pstride, select_k, sel, ex)
+  if (need <= 1) DSA_LAUNCH_TK(1);
+  else if (need <= 2) DSA_LAUNCH_TK(2);
+  else if (need <= 4) DSA_LAUNCH_TK(4);
+  else if (need <= 8) DSA_LAUNCH_TK(8);
+  else DSA_LAUNCH_TK(16);
+#undef DSA_LAUNCH_TK
+  return dsa::check_launch(EXPAND ? "dsa_topk_expand" : "dsa_topk_pools");
 }
 
 }  // namespace
@@ -283,17 +337,31 @@ DSA_EXPORT dsa_status dsa_topk_pools(const float* scores, const uint8_t* cand, i
               "dsa_topk_pools: pstride=%d above %d", pstride, DSA_MAX_TOPK_ROW);
   if (Q == 0) return DSA_OK;
   DSA_REQUIRE(scores && cand && sel, DSA_ERR_INVALID_ARG, "dsa_topk_pools: NULL tensor pointer");
-  const int need = (pstride + kThreads - 1) / kThreads;
-  if (dsa::trace_enabled())
-    fprintf(stderr, "[dsa] topk_pools Q=%d pstride=%d select_k=%d E=%d\n", Q, pstride, select_k,
-            need);
-#define DSA_LAUNCH_TK(E) \
-  topk_kernel<E><<<Q, kThreads, 0, stream>>>(scores, cand, pstride, select_k, sel)
-  if (need <= 1) DSA_LAUNCH_TK(1);
-  else if (need <= 2) DSA_LAUNCH_TK(2);
-  else if (need <= 4) DSA_LAUNCH_TK(4);
-  else if (need <= 8) DSA_LAUNCH_TK(8);
-  else DSA_LAUNCH_TK(16);
-#undef DSA_LAUNCH_TK
-  return dsa::check_launch("dsa_topk_pools");
+  return launch_topk<false>(scores, cand, Q, pstride, select_k, sel, ExpandArgs{}, stream);
+}
+
+DSA_EXPORT dsa_status dsa_topk_expand(const float* scores, const uint8_t* cand, int Q,
+                                      int pstride, int select_k, const int32_t* pool_start,
+                                      const int32_t* pool_off, const int32_t* q_req, int kpool,
+                                      int out_width, int flags, int32_t* sel, int32_t* tok,
+                                      hipStream_t stream) {
+  DSA_REQUIRE(select_k >= 1, DSA_ERR_INVALID_ARG, "dsa_topk_expand: select_k=%d < 1", select_k);
+  DSA_REQUIRE(pstride >= 1, DSA_ERR_INVALID_ARG, "dsa_topk_expand: pstride=%d < 1", pstride);
+  DSA_REQUIRE(Q >= 0, DSA_ERR_INVALID_ARG, "dsa_topk_expand: Q=%d < 0", Q);
+  DSA_REQUIRE(pstride <= DSA_MAX_TOPK_ROW, DSA_ERR_UNSUPPORTED,
+              "dsa_topk_expand: pstride=%d above %d", pstride, DSA_MAX_TOPK_ROW);
+  DSA_REQUIRE((flags & ~1) == 0, DSA_ERR_INVALID_ARG, "dsa_topk_expand: unknown flags 0x%x",
+              flags);
+  DSA_REQUIRE((flags & 1) == 0, DSA_ERR_UNSUPPORTED,
+              "dsa_topk_expand: always_select_tail is not built");
+  DSA_REQUIRE(kpool >= 1 && kpool <= DSA_MAX_KPOOL, DSA_ERR_INVALID_ARG,
+              "dsa_topk_expand: kpool=%d outside [1,%d]", kpool, DSA_MAX_KPOOL);
+  DSA_REQUIRE((long long)out_width >= (long long)select_k * kpool, DSA_ERR_INVALID_ARG,
+              "dsa_topk_expand: out_width=%d < select_k*kpool=%lld", out_width,
+              (long long)select_k * kpool);
+  if (Q == 0) return DSA_OK;
+  DSA_REQUIRE(scores && cand && sel && pool_start && pool_off && q_req && tok,
+              DSA_ERR_INVALID_ARG, "dsa_topk_expand: NULL tensor pointer");
+  return launch_topk<true>(scores, cand, Q, pstride, select_k, sel,
+                           ExpandArgs{pool_start, pool_off, q_req, kpool, out_width, tok}, stream);
 }

@@ -44,6 +44,13 @@ _SIGS = {
     "dsa_sparse_mla_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "dsa_sparse_mla_decode": (_I, [_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P,
                                    _Z, _P]),
+    "dsa_gate_split_count": (_I, [_I, _I, _I]),
+    "dsa_gate_compress_workspace_size": (_Z, [_I, _I, _I]),
+    "dsa_gate_compress": (_I, [_P, _P, _I, _I, _I, _P, _Z, _P, _P, _P, _P, _P, _P, _P, _P, _F,
+                               _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P]),
+    "dsa_index_scores_gated": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                    _I, _P, _P, _P]),
+    "dsa_topk_expand": (_I, [_P, _P, _I, _I, _I, _P, _P, _P, _I, _I, _I, _P, _P, _P]),
 }
 
 
@@ -202,3 +209,58 @@ def dsa_sparse_mla_decode(q, ckv, ckv_scale, kv_off, q_req, tok, sm_scale: float
         _dev(kv_off, _I32, "kv_off"), _dev(q_req, _I32, "q_req"), _dev(tok, _I32, "tok"), Q, Hm, L,
         out_width, float(sm_scale), _dev(out, _BF, "out"), _dev(lse, torch.float32, "lse", allow_none=True),
         wp, wb, _stream(stream)))
+
+
+# --- fused decode calls ----------------------------------------------------
+
+def gate_split_count(M: int, K: int, N: int) -> int:
+    return lib().dsa_gate_split_count(M, K, N)
+
+
+def gate_compress_workspace_size(M: int, K: int, N: int) -> int:
+    return lib().dsa_gate_compress_workspace_size(M, K, N)
+
+
+def dsa_gate_compress(hidden, W, gate_part, k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b,
+                      eps: float, kpool: int, max_cap: int, keys, pool_start, pool_valid, n_pools,
+                      new_from=None, max_new: int = 0, stream=None) -> None:
+    M, K = hidden.shape
+    N = W.shape[1]
+    B = tok_off.numel() - 1
+    D = k.shape[1]
+    gp, gb = _ws(gate_part)
+    if gate_part is not None and gate_part.dtype != torch.float32:
+        raise ValueError("gate_part must be float32")
+    _check(lib().dsa_gate_compress(
+        _dev(hidden, torch.float32, "hidden"), _dev(W, torch.float32, "W"), M, K, N, gp, gb,
+        _dev(k, _BF, "k"), _dev(gate, _BF, "gate"), _dev(ape, _BF, "ape"), _dev(valid, _U8, "valid"),
+        _dev(tok_off, _I32, "tok_off"), _dev(pool_off, _I32, "pool_off"),
+        _dev(ln_w, torch.float32, "ln_w"), _dev(ln_b, torch.float32, "ln_b"), float(eps), B, D,
+        kpool, max_cap, _dev(new_from, _I32, "new_from", allow_none=True), int(max_new),
+        _dev(keys, _BF, "keys"), _dev(pool_start, _I32, "pool_start"),
+        _dev(pool_valid, _U8, "pool_valid"), _dev(n_pools, _I32, "n_pools"), _stream(stream)))
+
+
+def dsa_index_scores_gated(qi, gate_part, nslices: int, w, keys, pool_start, pool_valid, pool_off,
+                           n_pools, q_req, q_pos, kpool: int, scores, cand, stream=None) -> None:
+    Q, H, D = qi.shape
+    pstride = scores.shape[1]
+    _check(lib().dsa_index_scores_gated(
+        _dev(qi, _BF, "qi"), _dev(gate_part, torch.float32, "gate_part"), int(nslices),
+        _dev(w, torch.float32, "w", allow_none=True), _dev(keys, _BF, "keys"),
+        _dev(pool_start, _I32, "pool_start"), _dev(pool_valid, _U8, "pool_valid"),
+        _dev(pool_off, _I32, "pool_off"), _dev(n_pools, _I32, "n_pools"), _dev(q_req, _I32, "q_req"),
+        _dev(q_pos, _I32, "q_pos"), Q, H, D, kpool, pstride, _dev(scores, torch.float32, "scores"),
+        _dev(cand, _U8, "cand"), _stream(stream)))
+
+
+def dsa_topk_expand(scores, cand, pool_start, pool_off, q_req, kpool: int, sel, tok, flags: int = 0,
+                    stream=None) -> None:
+    Q, pstride = scores.shape
+    select_k = sel.shape[1]
+    out_width = tok.shape[1]
+    _check(lib().dsa_topk_expand(
+        _dev(scores, torch.float32, "scores"), _dev(cand, _U8, "cand"), Q, pstride, select_k,
+        _dev(pool_start, _I32, "pool_start"), _dev(pool_off, _I32, "pool_off"),
+        _dev(q_req, _I32, "q_req"), kpool, out_width, flags, _dev(sel, _I32, "sel"),
+        _dev(tok, _I32, "tok"), _stream(stream)))

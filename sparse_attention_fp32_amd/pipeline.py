@@ -39,6 +39,10 @@ class DsaStep:
         self.tok = torch.empty(Q, s.out_width, **i32)
         self.out = torch.empty(Q, s.mla_heads, s.latent, dtype=torch.int16, device=dev)
         self.lse = torch.empty(Q, s.mla_heads, dtype=torch.float32, device=dev)
+        # fused path: head-gate partials (or w itself when the split does not apply)
+        self.nslices = dsa.gate_split_count(Q, s.hidden, H)
+        self.gate_part = torch.empty(max(1, dsa.gate_compress_workspace_size(Q, s.hidden, H) // 4),
+                                     dtype=torch.float32, device=dev)
         dt = dsa.LATENT_FP8_E4M3 if s.latent_fp8 else dsa.LATENT_BF16
         self.ws_mla = torch.empty(max(1, dsa.sparse_mla_decode_workspace_size(
             Q, s.mla_heads, s.latent, s.out_width, dt)), dtype=torch.uint8, device=dev)
@@ -73,6 +77,33 @@ class DsaStep:
         dsa.dsa_sparse_mla_decode(x.q_mla, x.ckv, x.ckv_scale, x.kv_off, x.q_req, self.tok,
                                   self.spec.sm_scale, self.out, self.lse, self.ws_mla,
                                   stream=self.stream)
+
+    # -- fused decode calls (same outputs, fewer launches) ---------------------
+    def gate_compress(self, incremental: bool = False):
+        x = self.x
+        dsa.dsa_gate_compress(x.hidden, x.W, self.gate_part, x.k, x.gate, x.ape, x.valid, x.tok_off,
+                              x.pool_off, x.ln_w, x.ln_b, self.spec.eps, self.spec.kpool,
+                              self.max_cap, self.keys, self.pool_start, self.pool_valid,
+                              self.n_pools, new_from=x.new_from if incremental else None,
+                              max_new=1 if incremental else 0, stream=self.stream)
+
+    def index_scores_gated(self):
+        x = self.x
+        dsa.dsa_index_scores_gated(x.qi, self.gate_part, self.nslices, self.w, self.keys,
+                                   self.pool_start, self.pool_valid, x.pool_off, self.n_pools,
+                                   x.q_req, x.q_pos, self.spec.kpool, self.scores, self.cand,
+                                   stream=self.stream)
+
+    def topk_expand(self):
+        dsa.dsa_topk_expand(self.scores, self.cand, self.pool_start, self.x.pool_off, self.x.q_req,
+                            self.spec.kpool, self.sel, self.tok, stream=self.stream)
+
+    def run_fused(self, incremental: bool = False):
+        """The decode step through the fused calls: four calls, five launches."""
+        self.gate_compress(incremental)
+        self.index_scores_gated()
+        self.topk_expand()
+        self.mla()
 
     def run(self, incremental: bool = False):
         self.head_gate()

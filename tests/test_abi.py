@@ -17,7 +17,7 @@ NUL = ctypes.c_void_p(None)
 
 def test_exports_every_declared_function():
     names = dsa.header_functions()
-    assert len(names) == 11
+    assert len(names) == 16
     import subprocess
     out = subprocess.run(["nm", "-D", "--defined-only", dsa.LIB_PATH], capture_output=True, text=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
@@ -119,3 +119,44 @@ def test_sparse_mla_errors():
     assert call(ws=FAKE, wsb=need - 1) == INV
     assert call(q=NUL, ws=FAKE, wsb=need) == INV
     assert call(Q=0) == dsa.DSA_OK
+
+
+def test_fused_call_errors():
+    L = dsa.lib()
+    # split rule: K/128 partials for 1 <= M <= 64 and K a multiple of 128 (<= 64 slices)
+    assert dsa.gate_split_count(16, 4096, 16) == 32
+    assert dsa.gate_split_count(2, 256, 4) == 2
+    assert dsa.gate_split_count(4096, 4096, 16) == 1      # dense head-gate writes w
+    assert dsa.gate_split_count(16, 4000, 16) == 1
+    assert dsa.gate_split_count(16, 128 * 65, 16) == 1
+    assert dsa.gate_split_count(16, 4096, 17) == 0
+    assert dsa.gate_compress_workspace_size(16, 4096, 16) == 32 * 16 * 16 * 4
+    assert dsa.gate_compress_workspace_size(4096, 4096, 16) == 4096 * 16 * 4
+
+    def gc(M=16, K=4096, N=16, part_bytes=32 * 16 * 16 * 4, kpool=4, B=2, hidden=FAKE):
+        return L.dsa_gate_compress(hidden, FAKE, M, K, N, FAKE, part_bytes, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, FAKE, FAKE, FAKE, 1e-5, B, 128, kpool, 10, NUL, 0, FAKE,
+                                   FAKE, FAKE, FAKE, NUL)
+    assert gc(N=17) == INV
+    assert gc(part_bytes=32 * 16 * 16 * 4 - 1) == INV
+    assert "need" in dsa.last_error()
+    assert gc(kpool=9) == INV
+    assert gc(hidden=NUL) == INV
+    assert gc(M=0, B=0) == dsa.DSA_OK
+
+    def sg(nslices=32, H=16, Q=3):
+        return L.dsa_index_scores_gated(FAKE, FAKE, nslices, NUL, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        FAKE, Q, H, 128, 4, 100, FAKE, FAKE, NUL)
+    assert sg(nslices=0) == INV
+    assert sg(nslices=65) == INV
+    assert sg(H=17) == INV
+    assert sg(Q=0) == dsa.DSA_OK
+
+    def te(select_k=4, kpool=4, out_width=16, flags=0, tok=FAKE):
+        return L.dsa_topk_expand(FAKE, FAKE, 2, 100, select_k, FAKE, FAKE, FAKE, kpool, out_width,
+                                 flags, FAKE, tok, NUL)
+    assert te(out_width=15) == INV
+    assert te(select_k=0) == INV
+    assert te(kpool=9) == INV
+    assert te(flags=1) == UNS
+    assert te(tok=NUL) == INV

@@ -53,27 +53,37 @@ def test_fullsize(name):
     ref = O.dsa_step(xn, spec.kpool, spec.select_k, spec.out_width, spec.pstride(), spec.eps,
                      spec.sm_scale, queries=sample)
 
-    _say(f"fullsize {name}: GPU chain (full compression, then the cached-pool step)")
+    ncap = int(xn["pool_off"][-1])
+
+    def check_chained(st, label):
+        PT.check_gate(_np(st.w), ref["w"])
+        g = {"keys": _np(st.keys).view(np.uint16)[:ncap], "pool_start": _np(st.pool_start)[:ncap],
+             "pool_valid": _np(st.pool_valid)[:ncap], "n_pools": _np(st.n_pools)}
+        flips = PT.check_compress(g, ref, requests=reqs, pool_off=xn["pool_off"])
+        sel_g, tok_g, out_g, lse_g = _np(st.sel), _np(st.tok), _np(st.out), _np(st.lse)
+        ndiff = 0
+        for q in sample:
+            ok, nd = PT.boundary_ok(sel_g[q], ref["sel"][q], ref["scores"][q], PT.CHAIN_GAP_REL)
+            assert ok, f"{label} selection q={q}: {nd} pools differ away from the boundary"
+            ndiff += nd
+            if nd == 0:
+                assert np.array_equal(tok_g[q], ref["tok"][q])
+                PT.check_mla(out_g, lse_g, ref["out_f64"], ref["lse"], rows=[q])
+        _say(f"fullsize {name}: {label} ok; key ulp flips in sample {flips}, boundary swaps {ndiff}")
+
+    # the fused decode calls the bench times: full compression, then the cached-pool step
+    _say(f"fullsize {name}: fused GPU chain")
+    stf = DsaStep(xg)
+    stf.run_fused(incremental=False)
+    stf.run_fused(incremental=True)
+    check_chained(stf, "fused chain")
+    del stf
+
+    _say(f"fullsize {name}: GPU chain of the six calls (full compression, then the cached-pool step)")
     st = DsaStep(xg)
     st.run(incremental=False)
     st.run(incremental=True)
-    torch.cuda.synchronize()
-
-    PT.check_gate(_np(st.w), ref["w"])
-    ncap = int(xn["pool_off"][-1])
-    g = {"keys": _np(st.keys).view(np.uint16)[:ncap], "pool_start": _np(st.pool_start)[:ncap],
-         "pool_valid": _np(st.pool_valid)[:ncap], "n_pools": _np(st.n_pools)}
-    flips = PT.check_compress(g, ref, requests=reqs, pool_off=xn["pool_off"])
-    sel_g, tok_g, out_g, lse_g = _np(st.sel), _np(st.tok), _np(st.out), _np(st.lse)
-    ndiff = 0
-    for q in sample:
-        ok, nd = PT.boundary_ok(sel_g[q], ref["sel"][q], ref["scores"][q], PT.CHAIN_GAP_REL)
-        assert ok, f"chained selection q={q}: {nd} pools differ away from the boundary"
-        ndiff += nd
-        if nd == 0:
-            assert np.array_equal(tok_g[q], ref["tok"][q])
-            PT.check_mla(out_g, lse_g, ref["out_f64"], ref["lse"], rows=[q])
-    _say(f"fullsize {name}: chained ok; key ulp flips in sample {flips}, boundary swaps {ndiff}")
+    check_chained(st, "chain")
 
     # stage isolation on the sampled queries: oracle inputs into the GPU buffers
     idx = np.concatenate([np.arange(xn["pool_off"][r], xn["pool_off"][r + 1]) for r in reqs])

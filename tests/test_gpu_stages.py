@@ -202,3 +202,86 @@ def test_determinism_and_duplicate_rows(case):
         assert np.array_equal(u.view(np.uint8), v.view(np.uint8)), "run-to-run difference"
     for u in a:
         assert np.array_equal(u[0].view(np.uint8), u[1].view(np.uint8)), "duplicate rows split"
+
+
+# --- fused decode calls -------------------------------------------------------
+
+def _oracle_gate_partials(xn, ns):
+    """Head-gate partials of ns equal K slices, each from the oracle's head-gate
+    on that slice (so their sum is the oracle's w up to fp32 rounding)."""
+    K = xn["hidden"].shape[1]
+    if ns == 1:
+        return O.head_gate(xn["hidden"], xn["W"])[None]
+    s = K // ns
+    return np.stack([O.head_gate(xn["hidden"][:, i * s:(i + 1) * s], xn["W"][i * s:(i + 1) * s])
+                     for i in range(ns)])
+
+
+def test_fused_gate_compress(case):
+    spec, xn, ref, xg = case
+    _say(f"gate_compress {spec.name}")
+    st = _step(xg)
+    for t in (st.keys, st.pool_start, st.pool_valid, st.n_pools, st.gate_part):
+        _poison(t)
+    st.gate_compress()
+    ns = st.nslices
+    part = _np(st.gate_part)[:ns * spec.Q * spec.index_heads].reshape(ns, spec.Q, spec.index_heads)
+    if ns > 1:
+        PT.check_gate(part, _oracle_gate_partials(xn, ns))
+    PT.check_gate(part.astype(np.float64).sum(axis=0), ref["w"])
+    ncap = int(xn["pool_off"][-1])
+    g = {"keys": _np(st.keys).view(np.uint16)[:ncap], "pool_start": _np(st.pool_start)[:ncap],
+         "pool_valid": _np(st.pool_valid)[:ncap], "n_pools": _np(st.n_pools)}
+    PT.check_compress(g, ref)
+
+
+def test_fused_index_scores_isolated(case):
+    spec, xn, ref, xg = case
+    _say(f"index_scores_gated {spec.name}")
+    st = _step(xg)
+    _load_oracle_front(st, ref)
+    part = _oracle_gate_partials(xn, st.nslices)
+    st.gate_part[:part.size].copy_(torch.from_numpy(part.reshape(-1)))
+    for t in (st.scores, st.cand, st.w):
+        _poison(t)
+    st.index_scores_gated()
+    PT.check_gate(_np(st.w), ref["w"])
+    worst = PT.check_scores(_np(st.scores), _np(st.cand), ref["scores"], ref["cand"])
+    _say(f"gated scores worst rel diff {worst:.3g}")
+
+
+def test_fused_topk_expand_isolated(case):
+    spec, xn, ref, xg = case
+    _say(f"topk_expand {spec.name}")
+    st = _step(xg)
+    _load_oracle_front(st, ref)
+    st.scores.copy_(torch.from_numpy(ref["scores"]))
+    st.cand.copy_(torch.from_numpy(ref["cand"]))
+    _poison(st.sel)
+    _poison(st.tok)
+    st.topk_expand()
+    PT.check_sel_exact(_np(st.sel), ref["sel"])
+    assert np.array_equal(_np(st.tok), ref["tok"])
+
+
+def test_fused_chain(case):
+    spec, xn, ref, xg = case
+    _say(f"fused chain {spec.name}")
+    st = _step(xg)
+    for t in (st.w, st.scores, st.cand, st.sel, st.tok, st.out, st.lse):
+        _poison(t)
+    st.run_fused()
+    PT.check_gate(_np(st.w), ref["w"])
+    sel_g, tok_g = _np(st.sel), _np(st.tok)
+    for q in range(spec.Q):
+        ok, nd = PT.boundary_ok(sel_g[q], ref["sel"][q], ref["scores"][q], PT.CHAIN_GAP_REL)
+        assert ok, f"fused selection row {q}: {nd} pools differ away from the boundary"
+        if nd == 0:
+            assert np.array_equal(tok_g[q], ref["tok"][q])
+            PT.check_mla(_np(st.out), _np(st.lse), ref["out_f64"], ref["lse"], rows=[q])
+    # the cached-pool step after it gives the same outputs (nothing changed)
+    a = [_np(t).copy() for t in (st.w, st.scores, st.sel, st.tok, st.out, st.lse)]
+    st.run_fused(incremental=True)
+    b = [_np(t) for t in (st.w, st.scores, st.sel, st.tok, st.out, st.lse)]
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8)), "incremental fused step differs"
