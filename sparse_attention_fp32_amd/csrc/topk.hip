@@ -14,9 +14,10 @@
 //  3. Inside the octave holding the k_eff-th best key, byte-wise radix passes
 //     over per-wave LDS histograms pin the threshold key T (stopping early
 //     once the threshold bin is taken whole).
-//  4. Keys above T are kept and, among keys equal to T, the lowest ids; kept
-//     ids are compacted in id order with wave ballots and per-(e, wave)
-//     offsets.
+//  4. Keys above T are kept and, among keys equal to T, the lowest ids (a
+//     rank pass only when the budget splits one key value); kept ids are
+//     compacted in id order with wave ballots and per-(e, wave) offsets that
+//     one wave scans.
 // The fused variant (dsa_topk_expand) also writes the expanded token ids of
 // each kept pool (a5): the pools' start rows are loaded beside the scores, so
 // the expansion adds no dependent load and no launch.
@@ -45,6 +46,30 @@ struct ExpandArgs {
   int32_t* tok;
 };
 
+// Exclusive prefix, in (e, wave) order, of the per-(e, wave) counts in cnt
+// (E * kWaves entries), written to off; run by wave 0 alone.
+template <int E>
+__device__ __forceinline__ void wave0_offsets(const int* __restrict__ cnt, int* __restrict__ off,
+                                              int lane) {
+  constexpr int kN = E * kWaves;
+  constexpr int kPer = (kN + 63) / 64;
+  int c[kPer];
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int ix = lane * kPer + i;
+    c[i] = ix < kN ? cnt[ix] : 0;
+    sum += c[i];
+  }
+  int base = wave_incl_scan(sum) - sum;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int ix = lane * kPer + i;
+    if (ix < kN) off[ix] = base;
+    base += c[i];
+  }
+}
+
 template <int E, bool EXPAND>
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores,
                                                         const uint8_t* __restrict__ cand,
@@ -55,7 +80,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   __shared__ uint32_t s_max[kWaves];
   __shared__ int s_cnt[kWaves];
   __shared__ int s_oct[kWaves][16];
-  __shared__ int s_ecnt[2][E][kWaves];  // per (e, wave) counts: [0] ties at T, [1] kept
+  __shared__ int s_ecnt[E * kWaves];  // per (e, wave) counts
+  __shared__ int s_eoff[E * kWaves];  // their exclusive prefix in (e, wave) order
   __shared__ int s_bin, s_above, s_binc;
   const int q = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const float* srow = scores + (int64_t)q * pstride;
@@ -71,29 +97,32 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     sv[e] = srow[id];
     cv[e] = crow[id];
   }
-  // fused expansion: start rows of this request's pool slots (ids clamped to
-  // the request's slots; a candidate is always one of them)
+  // fused expansion: start rows of this request's pool slots, loaded without a
+  // branch (ids clamped to the request's slots; a request with no slot reads
+  // q_req instead, and none of its pools can be selected)
   int32_t ps[EXPAND ? E : 1];
   int32_t* trow = nullptr;
   if (EXPAND) {
     const int r = ex.q_req[q];
     const int pb = ex.pool_off[r], cap = ex.pool_off[r + 1] - pb;
     trow = ex.tok + (int64_t)q * ex.out_width;
-    if (cap > 0) {
+    const int32_t* src = cap > 0 ? ex.pool_start + pb : ex.q_req;
+    const int last = max(cap - 1, 0);
 #pragma unroll
-      for (int e = 0; e < E; ++e) ps[e] = ex.pool_start[pb + min(t + kThreads * e, cap - 1)];
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) ps[e] = -1;
-    }
+    for (int e = 0; e < E; ++e) ps[e] = src[min(t + kThreads * e, last)];
   }
   uint32_t key[E];
   uint32_t kmx = 0u;
   int nc = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const bool c = t + kThreads * e < pstride && cv[e] != 0;
-    key[e] = c ? float_order_key(sv[e]) : 0u;
+    // the empty asm hands the loaded values over as opaque registers, so the
+    // compiler cannot turn the masking below into a branch around a load
+    // (which would end in a wait for every outstanding load)
+    uint32_t u = __float_as_uint(sv[e]), cb = cv[e];
+    asm volatile("" : "+v"(u), "+v"(cb));
+    const bool c = (t + kThreads * e < pstride) & (cb != 0u);
+    key[e] = c ? float_order_key(__uint_as_float(u)) : 0u;
     kmx = max(kmx, key[e]);
     nc += __popcll(ballot(c));
   }
@@ -119,29 +148,28 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   }
   const uint32_t top9 = kmax >> 23;
 
-  // 2. octave counts: 16 bins as four registers of four 8-bit fields (E <= 16)
+  // 2. octave counts: 16 four-bit counters per 64-bit word, one word per 8
+  // keys (so no counter exceeds 8), widened to 16-bit pairs
   uint32_t oct[E];
-  uint32_t c8[4] = {0u, 0u, 0u, 0u};
+  uint32_t p[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const uint32_t d = min(top9 - (key[e] >> 23), 15u);
-    oct[e] = key[e] ? d : 16u;
-    const uint32_t inc = key[e] ? 1u << ((d & 3u) * 8u) : 0u;
-    const uint32_t r = d >> 2;
-    c8[0] += r == 0u ? inc : 0u;
-    c8[1] += r == 1u ? inc : 0u;
-    c8[2] += r == 2u ? inc : 0u;
-    c8[3] += r == 3u ? inc : 0u;
-  }
-  {
-    // widen to 16-bit pairs: p[j] holds bins 2j (low half) and 2j+1 (high half)
-    uint32_t p[8];
+  for (int e0 = 0; e0 < E; e0 += 8) {
+    uint64_t c4 = 0ull;
+#pragma unroll
+    for (int e = e0; e < e0 + 8 && e < E; ++e) {
+      const uint32_t d = min(top9 - (key[e] >> 23), 15u);
+      oct[e] = key[e] ? d : 16u;
+      c4 += key[e] ? (1ull << (4u * d)) : 0ull;
+    }
+    const uint32_t lo = (uint32_t)c4, hi = (uint32_t)(c4 >> 32);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      p[2 * j] = (c8[j] & 0xffu) | ((c8[j] & 0xff00u) << 8);
-      p[2 * j + 1] = ((c8[j] >> 16) & 0xffu) | ((c8[j] >> 8) & 0xff0000u);
+      p[j] += ((lo >> (8 * j)) & 0xFu) | (((lo >> (8 * j + 4)) & 0xFu) << 16);
+      p[4 + j] += ((hi >> (8 * j)) & 0xFu) | (((hi >> (8 * j + 4)) & 0xFu) << 16);
     }
-    // reduce-scatter the 8 pairs over the wave (fields stay below 2^16)
+  }
+  {
+    // reduce-scatter the 8 pairs (bins 2j, 2j+1) over the wave (fields stay below 2^16)
     int v4[4], v2[2], v1;
     {
       const bool hi = (lane >> 5) & 1;
@@ -184,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   __syncthreads();
   const uint32_t boct = (uint32_t)s_bin;
   int krem = k_eff - s_above;
-  const bool whole = s_binc == krem;
+  int binc = s_binc;
   // the threshold octave; octave 15 also holds everything further down
   uint32_t prefix = boct < 15u ? (top9 - boct) << 23 : 0u;
   uint32_t mask = boct < 15u ? 0xFF800000u : 0u;
@@ -193,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   for (int e = 0; e < E; ++e) act[e] = boct < 15u ? oct[e] == boct : (oct[e] >= 15u && oct[e] < 16u);
 
   // 3. byte-wise radix passes inside the threshold octave
-  if (!whole) {
+  if (binc != krem) {
     for (int hi = boct < 15u ? 22 : 31; hi >= 0; hi -= 8) {
       const int lo = hi >= 7 ? hi - 7 : 0;
       const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
@@ -229,67 +257,65 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
         }
       }
       __syncthreads();
-      const int b = s_bin, bc = s_binc;
+      const int b = s_bin;
+      binc = s_binc;
       krem -= s_above;
       prefix |= (uint32_t)b << lo;
       mask |= dmask << lo;
-      if (bc == krem) break;  // the whole threshold bin is taken
+      if (binc == krem) break;  // the whole threshold bin is taken
     }
   }
 
-  // 4. ties at T in id order, then compaction of every kept id in id order
-  bool gt[E], eq[E];
+  if (EXPAND) {
+    // take delivery of the start rows here, before the stores, so that no
+    // wait inside the store phase covers the stores themselves
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const uint32_t km = key[e] & mask;
-    gt[e] = oct[e] < boct || (act[e] && km > prefix);
-    eq[e] = act[e] && km == prefix;
+    for (int e = 0; e < E; ++e) asm volatile("" ::"v"(ps[e]));
   }
-  uint64_t beq[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    beq[e] = ballot(eq[e]);
-    if (lane == 0) s_ecnt[0][e][wv] = __popcll(beq[e]);
-  }
-  __syncthreads();
+  // 4. keys above the threshold bin are kept, and from the bin either all of
+  // it or, when its keys are one value split by the budget, the lowest ids
   bool keep[E];
-  {
-    int base = 0;  // ties in earlier (e, wave) blocks
+  if (binc == krem) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) keep[e] = oct[e] < boct || (act[e] && (key[e] & mask) >= prefix);
+  } else {
+    bool gt[E], eq[E];
+    uint64_t beq[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      int mine = base;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const int c = s_ecnt[0][e][w];
-        mine += w < wv ? c : 0;
-        base += c;
-      }
-      keep[e] = gt[e] || (eq[e] && mine + lanes_below(beq[e]) < krem);
+      const uint32_t km = key[e] & mask;
+      gt[e] = oct[e] < boct || (act[e] && km > prefix);
+      eq[e] = act[e] && km == prefix;
+      beq[e] = ballot(eq[e]);
+      if (lane == 0) s_ecnt[e * kWaves + wv] = __popcll(beq[e]);
     }
+    __syncthreads();
+    if (wv == 0) wave0_offsets<E>(s_ecnt, s_eoff, lane);
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      keep[e] = gt[e] || (eq[e] && s_eoff[e * kWaves + wv] + lanes_below(beq[e]) < krem);
+    __syncthreads();  // s_ecnt / s_eoff are reused below
   }
+  // compaction of the kept ids in id order: (e, wave, lane) is ascending id
   uint64_t bk[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     bk[e] = ballot(keep[e]);
-    if (lane == 0) s_ecnt[1][e][wv] = __popcll(bk[e]);
+    if (lane == 0) s_ecnt[e * kWaves + wv] = __popcll(bk[e]);
   }
   __syncthreads();
-  {
-    int base = 0;
+  if (wv == 0) wave0_offsets<E>(s_ecnt, s_eoff, lane);
+  __syncthreads();
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      int mine = base;
+  for (int e = 0; e < E; ++e) {
+    const int pos = s_eoff[e * kWaves + wv] + lanes_below(bk[e]);
+    if (keep[e] && pos < k_eff) {
+      out[pos] = t + kThreads * e;
+      if (EXPAND) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const int c = s_ecnt[1][e][w];
-        mine += w < wv ? c : 0;
-        base += c;
-      }
-      const int pos = mine + lanes_below(bk[e]);
-      if (keep[e] && pos < k_eff) {
-        out[pos] = t + kThreads * e;
-        if (EXPAND)
-          for (int s = 0; s < ex.kpool; ++s) trow[pos * ex.kpool + s] = ps[e] + s;
+        for (int s = 0; s < DSA_MAX_KPOOL; ++s)
+          if (s < ex.kpool) trow[pos * ex.kpool + s] = ps[e] + s;
       }
     }
   }
