@@ -39,61 +39,59 @@ __global__ __launch_bounds__(256) void index_scores_kernel(
   const int q = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
+  // Head-gate partials first (gated variant): the oldest loads, so the
+  // reduction below waits for them alone while the key rows stream in.
+  float gp[4];
+  if (GATED) {
+    const int Q = gridDim.y;
+    const int h = threadIdx.x & 15, g = threadIdx.x >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sl = min(g + 16 * i, nslices - 1);
+      gp[i] = w[((int64_t)sl * Q + q) * H + min(h, H - 1)];
+    }
+  }
   const int r = q_req[q];
   const int P = n_pools[r];
   const int64_t base = pool_off[r];
   const int qp = q_pos[q];
   const int tile0 = blockIdx.x * kPoolsPerWG + wave * (kTiles * 16);
 
-  // Key rows first: they are the long-latency HBM stream.  All of the wave's
-  // loads are issued together (indices clamped to the request's last pool, so
-  // no load is conditional); out-of-range pools are masked below.
+  // Key rows: the long-latency HBM stream.  Every load is issued, unconditional
+  // and together: pool indices are clamped to the request's last pool (a
+  // request without pools reads this query's qi row instead), and pools past
+  // the end are masked below.
+  const uint16_t* kb = P > 0 ? keys + base * D : qi + (int64_t)q * H * D;
+  const int32_t* sb = P > 0 ? pool_start + base : q_pos;
+  const uint8_t* vb = P > 0 ? pool_valid + base : (const uint8_t*)q_pos;
+  const int plast = max(P - 1, 0);
   uint4 b[kTiles][KS];
   int ps[kTiles], pv[kTiles];
-  if (tile0 < P) {
 #pragma unroll
-    for (int tt = 0; tt < kTiles; ++tt) {
-      const int p = min(tile0 + tt * 16 + col, P - 1);
-      const uint16_t* krow = keys + (base + p) * D + grp * 8;
+  for (int tt = 0; tt < kTiles; ++tt) {
+    const int p = min(tile0 + tt * 16 + col, plast);
+    const uint16_t* krow = kb + (int64_t)p * D + grp * 8;
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) b[tt][kk] = *(const uint4*)(krow + kk * 32);
-      ps[tt] = pool_start[base + p];
-      pv[tt] = pool_valid[base + p];
-    }
-  } else {
-#pragma unroll
-    for (int tt = 0; tt < kTiles; ++tt) {
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) b[tt][kk] = make_uint4(0, 0, 0, 0);
-      ps[tt] = 0;
-      pv[tt] = 0;
-    }
+    for (int kk = 0; kk < KS; ++kk) b[tt][kk] = *(const uint4*)(krow + kk * 32);
+    ps[tt] = sb[p];
+    pv[tt] = vb[p];
   }
-  // A operand: row m = head col, k = kk*32 + grp*8 + j.
+  // A operand: row m = head col, k = kk*32 + grp*8 + j.  Rows past H repeat
+  // head H-1; their weight is zero below.
   bf16x8_t a[KS];
-  const uint16_t* qrow = qi + ((int64_t)q * H + (col < H ? col : H - 1)) * D + grp * 8;
+  const uint16_t* qrow = qi + ((int64_t)q * H + min(col, H - 1)) * D + grp * 8;
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    const uint4 v = *(const uint4*)(qrow + kk * 32);
-    a[kk] = as_bf16x8(col < H ? v : make_uint4(0, 0, 0, 0));
-  }
+  for (int kk = 0; kk < KS; ++kk) a[kk] = as_bf16x8(*(const uint4*)(qrow + kk * 32));
   float wr[4];
   if (GATED) {
     // w[q, h] = sum over slices of part[sl][q][h]: thread (group g, head h)
     // adds slices g, g+16, g+32, g+48; the 16 group sums go in group order.
     __shared__ float s_red[16][16];
     __shared__ float s_w[16];
-    const int Q = gridDim.y;
     const int t = threadIdx.x, h = t & 15, g = t >> 4;
-    float pv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sl = min(g + 16 * i, nslices - 1);
-      pv[i] = w[((int64_t)sl * Q + q) * H + min(h, H - 1)];
-    }
     float acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc += g + 16 * i < nslices ? pv[i] : 0.f;
+    for (int i = 0; i < 4; ++i) acc += g + 16 * i < nslices ? gp[i] : 0.f;
     s_red[g][h] = acc;
     __syncthreads();
     if (t < 16) {

@@ -5,20 +5,24 @@
 // per-row gather of the selected ids is exactly the dense set-membership mask;
 // the serving kernel keeps an online softmax and no full score row).
 //
-// Work split (flash-decoding): workgroup (chunk, 64-head block, query) covers
-// one chunk of a query's selected ids for up to 64 heads.  Its 4 waves split
-// the 512 latent dims (128 each), not the heads:
-//  * each wave loads its 128-dim slice of the 32 gathered rows of a sub-chunk
-//    straight from HBM into the MFMA A-operand layout (two sub-chunks in
-//    flight: the next one loads while this one computes);
-//  * QK^T: each wave computes the partial S^T[32 tok x 64 heads] over its dims
+// Work split (flash-decoding): workgroup (chunk, 32-head block, query) covers
+// one chunk of a query's selected ids for up to 32 heads; two workgroups share
+// a compute unit (two waves per SIMD hide each other's latency), and the two
+// head blocks of a chunk sit on the same XCD, so the second reads the rows
+// from that XCD's L2.  The 4 waves of a workgroup split the 512 latent dims
+// (128 each), not the heads:
+//  * the chunk's ids are staged in LDS once; each wave loads its 128-dim slice
+//    of the 32 gathered rows of a sub-chunk straight from HBM into the MFMA
+//    A-operand layout, one sub-chunk ahead of the one it computes (a slot
+//    with no id loads this query's own Q row, zeroed before use);
+//  * QK^T: each wave computes the partial S^T[32 tok x 32 heads] over its dims
 //    (v_mfma_f32_16x16x32_bf16, Q^T in registers); the partials meet in LDS
-//    and wave w adds the four of head tile w in a fixed order, runs the online
-//    softmax (log2 domain, reference max moved only when it grows by > 2^8)
-//    for those 16 heads, and publishes P in the PV A-operand layout -- S^T's
-//    accumulator layout is that operand layout, with K index 8g+j of lane
-//    group g meaning token 4g+j (j < 4) or 16+4g+j-4;
-//  * PV: O[64 heads x its 128 dims] += P . C_slice, the B operand read from
+//    and wave w < 2 adds the four of head tile w in a fixed order, runs the
+//    online softmax (log2 domain, reference max moved only when it grows by
+//    more than 2^8) for those 16 heads, and publishes P in the PV A-operand
+//    layout -- S^T's accumulator layout is that operand layout, with K index
+//    8g+j of lane group g meaning token 4g+j (j < 4) or 16+4g+j-4;
+//  * PV: O[32 heads x its 128 dims] += P . C_slice, the B operand read from
 //    the wave's own slice in LDS (16 bytes = 8 dims per row per lane,
 //    regrouped into 8 operands, so each lane owns 8 consecutive output dims).
 // fp8 rows are widened to bf16 exactly in registers; the row scale multiplies
@@ -38,7 +42,9 @@ constexpr int L = DSA_KV_LORA;
 constexpr int kSub = 32;                  // tokens per sub-chunk
 constexpr int kSlice = 128;               // latent dims per wave
 constexpr int kSliceRow = kSlice * 2 + 16;  // LDS bytes per token row of a slice (+pad)
-constexpr int kTargetWG = 256;            // aim for one workgroup per CU
+constexpr int kHT = 2;                    // 16-head tiles per workgroup
+constexpr int kHeadsWG = 16 * kHT;        // heads per workgroup
+constexpr int kTargetWG = 512;            // aim for two workgroups per CU
 constexpr int kMinSubPerChunk = 4;        // >= 128 ids per chunk keeps partials small
 constexpr int kMaxTch = 2048;             // most ids per chunk
 constexpr float kLog2e = 1.4426950408889634f;
@@ -51,7 +57,7 @@ struct Chunking {
 
 Chunking mla_chunking(int Q, int Hm, int out_width) {
   const int nsub = (out_width + kSub - 1) / kSub;
-  const int hb = (Hm + 63) / 64;
+  const int hb = (Hm + kHeadsWG - 1) / kHeadsWG;
   const long long base = (long long)Q * hb;
   long long want = (kTargetWG + base - 1) / base;
   const int max_chunks = nsub / kMinSubPerChunk > 1 ? nsub / kMinSubPerChunk : 1;
@@ -93,21 +99,22 @@ struct RowSlice<true> {
 };
 
 template <bool FP8>
-__global__ __launch_bounds__(256) void sparse_mla_kernel(
+__global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ ckv_v,
     const float* __restrict__ ckv_scale, const int32_t* __restrict__ kv_off,
     const int32_t* __restrict__ q_req, const int32_t* __restrict__ tok, int Hm, int out_width,
     int tch, float sm_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
     uint16_t* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ __attribute__((aligned(16))) uint8_t s_slice[4][kSub * kSliceRow];
-  __shared__ f32x4_t s_exch[4][4][2][64];  // [source wave][head tile][token tile][lane]
-  __shared__ uint4 s_p[4][64];             // P operands per head tile
-  __shared__ float s_alpha[64];            // O rescale factor per head (when moved)
-  __shared__ int s_moved[4];               // a head tile moved its reference max
+  __shared__ f32x4_t s_exch[4][kHT][2][64];  // [source wave][head tile][token tile][lane]
+  __shared__ uint4 s_p[kHT][64];             // P operands per head tile
+  __shared__ float s_alpha[kHeadsWG];        // O rescale factor per head (when moved)
+  __shared__ int s_moved[kHT];               // a head tile moved its reference max
   __shared__ __attribute__((aligned(16))) float s_mul[kSub];   // sm_scale*log2e*row scale
   __shared__ __attribute__((aligned(16))) float s_bias[kSub];  // 0, or -inf for no token
   __shared__ __attribute__((aligned(16))) float s_scl[kSub];   // row scale (1 for bf16)
-  __shared__ float s_lrun[64];
+  __shared__ float s_lrun[kHeadsWG];
+  __shared__ int s_id[kMaxTch];            // the chunk's token ids (-1: none)
 
   const int chunk = blockIdx.x, nchunks = gridDim.x, hb = blockIdx.y, qx = blockIdx.z;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -122,49 +129,49 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
   // (always readable, at least one latent row long); the data is zeroed.
   const uint8_t* dummy = (const uint8_t*)(q + (int64_t)qx * Hm * L);
 
-  // Ids of sub-chunk s for this lane's two rows (tokens tt*16 + col), -1 past
-  // the chunk.  Every wave and lane group holds the same ids, so any decision
-  // taken on them is uniform over the workgroup.
-  auto load_ids = [&](int s, int (&id)[2]) {
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int j = j0 + s * kSub + tt * 16 + col;
-      const int v = trow[min(j, max(j1 - 1, 0))];
-      id[tt] = j < j1 ? v : -1;
-    }
-  };
-  int idA[2], idB[2];  // ids of the sub-chunk in registers, and of the next one
-  load_ids(0, idA);
-  load_ids(1, idB);
+  // The chunk's ids (one per thread; longer chunks loop, rarely), the Q rows
+  // and the request's first row are all in flight together; the ids then go
+  // to LDS, and from there every later id is read, so no register loaded in
+  // one sub-chunk is read in a later one except the latent rows.
+  const int nid = nsub * kSub;
   const int r = q_req[qx];
+  const int id0 = trow[min(j0 + t, max(j1 - 1, 0))];
 
-  // Q^T operand: qb[ht][kk] = Q[head hb*64 + ht*16 + col][dim0 + kk*32 + grp*8 .. +8]
-  bf16x8_t qb[4][4];
+  // Q^T operand: qb[ht][kk] = Q[head hb*32 + ht*16 + col][dim0 + kk*32 + grp*8 .. +8].
+  // Heads past Hm repeat head Hm-1: their softmax rows are computed and never
+  // stored.
+  bf16x8_t qb[kHT][4];
 #pragma unroll
-  for (int ht = 0; ht < 4; ++ht) {
-    const int h = hb * 64 + ht * 16 + col;
-    const uint16_t* qrow = q + ((int64_t)qx * Hm + (h < Hm ? h : Hm - 1)) * L + dim0 + grp * 8;
+  for (int ht = 0; ht < kHT; ++ht) {
+    const int h = min(hb * kHeadsWG + ht * 16 + col, Hm - 1);
+    const uint16_t* qrow = q + ((int64_t)qx * Hm + h) * L + dim0 + grp * 8;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const uint4 v = *(const uint4*)(qrow + kk * 32);
-      qb[ht][kk] = as_bf16x8(h < Hm ? v : make_uint4(0, 0, 0, 0));
-    }
+    for (int kk = 0; kk < 4; ++kk) qb[ht][kk] = as_bf16x8(*(const uint4*)(qrow + kk * 32));
   }
   const int64_t rowbase = kv_off[r];
+  asm volatile("" ::: "memory");  // every load above is issued before any wait below
+  s_id[t] = j0 + t < j1 ? id0 : -1;  // (entries past nid are never read)
+  for (int i = t + 256; i < nid; i += 256) {
+    const int j = j0 + i;
+    const int v = trow[min(j, j1 - 1)];
+    s_id[i] = j < j1 ? v : -1;
+  }
+  __syncthreads();
 
-  f32x4_t o[4][8];  // [head tile][e]: O[head ht*16 + grp*4 + i][dim0 + 8*col + e]
+  f32x4_t o[kHT][8];  // [head tile][e]: O[head ht*16 + grp*4 + i][dim0 + 8*col + e]
 #pragma unroll
-  for (int ht = 0; ht < 4; ++ht)
+  for (int ht = 0; ht < kHT; ++ht)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[ht][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;  // head w*16 + col (wave w owns head tile w)
+  float m_run = -INFINITY, l_run = 0.f;  // head w*16 + col (wave w < kHT owns head tile w)
 
   RowSlice<FP8> cr;
   float scl[2] = {1.f, 1.f};  // row scales of tokens col, 16 + col (wave 0, lanes < 16)
-  auto gather = [&](const int (&id)[2]) {
+  auto gather = [&](int s) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const uint8_t* src = id[tt] >= 0 ? (const uint8_t*)ckv_v + (rowbase + id[tt]) * kRowBytes : dummy;
+      const int id = s_id[s * kSub + tt * 16 + col];
+      const uint8_t* src = id >= 0 ? (const uint8_t*)ckv_v + (rowbase + id) * kRowBytes : dummy;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int d = dim0 + kk * 32 + grp * 8;
@@ -174,63 +181,67 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
           ((uint4*)cr.v[tt])[kk] = *(const uint4*)(src + 2 * d);
       }
       if (FP8 && t < 16) {
-        const float* sp = id[tt] >= 0 ? ckv_scale + rowbase + id[tt] : (const float*)dummy;
+        const float* sp = id >= 0 ? ckv_scale + rowbase + id : (const float*)dummy;
         const float v = *sp;
-        scl[tt] = id[tt] >= 0 ? v : 0.f;
+        scl[tt] = id >= 0 ? v : 0.f;
       }
     }
   };
-  gather(idA);
+  if (nsub > 0) gather(0);
 
   uint8_t* my_slice = s_slice[w];
   for (int s = 0; s < nsub; ++s) {
-    int idC[2];
-    load_ids(s + 2, idC);
-    const bool live = __any(idA[0] >= 0 || idA[1] >= 0);  // uniform over the workgroup
-    f32x4_t sacc[4][2];
+    const int ida[2] = {s_id[s * kSub + col], s_id[s * kSub + 16 + col]};
+    const bool live = __any(ida[0] >= 0 || ida[1] >= 0);  // uniform over the workgroup
+    f32x4_t sacc[kHT][2];
     if (live) {
       // per-token logit multiplier and mask of this sub-chunk
       if (t < 16) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           s_mul[tt * 16 + t] = sm_log2 * scl[tt];
-          s_bias[tt * 16 + t] = idA[tt] >= 0 ? 0.f : -INFINITY;
+          s_bias[tt * 16 + t] = ida[tt] >= 0 ? 0.f : -INFINITY;
           s_scl[tt * 16 + t] = scl[tt];
         }
       }
       // partial S^T over this wave's dims, and the slice into LDS for PV
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht)
+      for (int ht = 0; ht < kHT; ++ht)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) sacc[ht][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const bool ok = idA[tt] >= 0;
+        const bool ok = ida[tt] >= 0;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
+          // the empty asm makes the loaded words opaque registers, so the
+          // zeroing select stays a select (not a branch around the load)
           uint4 a;
           if (FP8) {
-            const uint2 raw = ((const uint2*)cr.v[tt])[kk];
+            uint2 raw = ((const uint2*)cr.v[tt])[kk];
+            asm volatile("" : "+v"(raw.x), "+v"(raw.y));
             a = widen_fp8x8(ok ? raw : make_uint2(0, 0));
           } else {
-            const uint4 raw = ((const uint4*)cr.v[tt])[kk];
+            uint4 raw = ((const uint4*)cr.v[tt])[kk];
+            asm volatile("" : "+v"(raw.x), "+v"(raw.y), "+v"(raw.z), "+v"(raw.w));
             a = ok ? raw : make_uint4(0, 0, 0, 0);
           }
           *(uint4*)(my_slice + (tt * 16 + col) * kSliceRow + (kk * 32 + grp * 8) * 2) = a;
 #pragma unroll
-          for (int ht = 0; ht < 4; ++ht) sacc[ht][tt] = mfma16x16x32(as_bf16x8(a), qb[ht][kk], sacc[ht][tt]);
+          for (int ht = 0; ht < kHT; ++ht) sacc[ht][tt] = mfma16x16x32(as_bf16x8(a), qb[ht][kk], sacc[ht][tt]);
         }
       }
     }
-    if (s + 1 < nsub) gather(idB);  // the next rows load while this sub-chunk computes
+    if (s + 1 < nsub) gather(s + 1);  // the next rows load while this sub-chunk computes
     if (live) {
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht)
+      for (int ht = 0; ht < kHT; ++ht)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) s_exch[w][ht][tt][lane] = sacc[ht][tt];
       __syncthreads();
 
-      // wave w: full S^T of head tile w, softmax, P
+      // wave w < kHT: full S^T of head tile w, softmax, P
+      if (w < kHT) {
       float x[8];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -281,12 +292,13 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
         }
         s_p[w][lane] = make_uint4(pw[0], pw[1], pw[2], pw[3]);
       }
+      }
       __syncthreads();
 
       // rescale O where a head tile moved its reference max (rare)
-      if (s_moved[0] | s_moved[1] | s_moved[2] | s_moved[3]) {
+      if (s_moved[0] | s_moved[kHT - 1]) {
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) {
+        for (int ht = 0; ht < kHT; ++ht) {
           if (!s_moved[ht]) continue;
           float ai[4];
 #pragma unroll
@@ -298,9 +310,9 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
         }
       }
       // PV over this wave's slice
-      bf16x8_t pa[4];
+      bf16x8_t pa[kHT];
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) pa[ht] = as_bf16x8(s_p[ht][lane]);
+      for (int ht = 0; ht < kHT; ++ht) pa[ht] = as_bf16x8(s_p[ht][lane]);
       uint4 u[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -318,24 +330,20 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
         }
         const bf16x8_t bv = as_bf16x8(make_uint4(bw[0], bw[1], bw[2], bw[3]));
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) o[ht][e] = mfma16x16x32(pa[ht], bv, o[ht][e]);
+        for (int ht = 0; ht < kHT; ++ht) o[ht][e] = mfma16x16x32(pa[ht], bv, o[ht][e]);
       }
     }
-    idA[0] = idB[0];
-    idA[1] = idB[1];
-    idB[0] = idC[0];
-    idB[1] = idC[1];
   }
 
   // epilogue: per-head sums to every wave, then this wave's dims of all heads
-  if (grp == 0) s_lrun[w * 16 + col] = l_run;
+  if (w < kHT && grp == 0) s_lrun[w * 16 + col] = l_run;
   __syncthreads();
   if (nchunks == 1) {
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht)
+    for (int ht = 0; ht < kHT; ++ht)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int h = hb * 64 + ht * 16 + grp * 4 + i;
+        const int h = hb * kHeadsWG + ht * 16 + grp * 4 + i;
         if (h >= Hm) continue;
         const float lv = s_lrun[ht * 16 + grp * 4 + i];
         const float inv = lv > 0.f ? 1.f / lv : 0.f;
@@ -344,24 +352,24 @@ __global__ __launch_bounds__(256) void sparse_mla_kernel(
         for (int e = 0; e < 8; e += 2) pk[e >> 1] = pack_bf16x2(o[ht][e][i] * inv, o[ht][e + 1][i] * inv);
         *(uint4*)(out + ((int64_t)qx * Hm + h) * L + dim0 + col * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       }
-    const int hq = hb * 64 + w * 16 + col;
-    if (lse && grp == 0 && hq < Hm)
+    const int hq = hb * kHeadsWG + w * 16 + col;
+    if (lse && w < kHT && grp == 0 && hq < Hm)
       lse[(int64_t)qx * Hm + hq] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   } else {
     const int64_t pbase = ((int64_t)qx * nchunks + chunk) * Hm;
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht)
+    for (int ht = 0; ht < kHT; ++ht)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int h = hb * 64 + ht * 16 + grp * 4 + i;
+        const int h = hb * kHeadsWG + ht * 16 + grp * 4 + i;
         if (h >= Hm) continue;
         uint32_t pk[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) pk[e >> 1] = pack_bf16x2(o[ht][e][i], o[ht][e + 1][i]);
         *(uint4*)(part_o + (pbase + h) * L + dim0 + col * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       }
-    const int hq = hb * 64 + w * 16 + col;
-    if (grp == 0 && hq < Hm) {
+    const int hq = hb * kHeadsWG + w * 16 + col;
+    if (w < kHT && grp == 0 && hq < Hm) {
       part_ml[(pbase + hq) * 2] = m_run;
       part_ml[(pbase + hq) * 2 + 1] = l_run;
     }
@@ -466,7 +474,7 @@ DSA_EXPORT dsa_status dsa_sparse_mla_decode(const uint16_t* q, const void* ckv,
   const Chunking ch = mla_chunking(Q, Hm, out_width);
   uint16_t* part_o = need ? (uint16_t*)ws : nullptr;
   float* part_ml = need ? (float*)((uint16_t*)ws + (size_t)Q * ch.nchunks * Hm * L) : nullptr;
-  dim3 grid(ch.nchunks, (Hm + 63) / 64, Q);
+  dim3 grid(ch.nchunks, (Hm + kHeadsWG - 1) / kHeadsWG, Q);
   const float sm_log2 = sm_scale * kLog2e;
   if (dsa::trace_enabled())
     fprintf(stderr, "[dsa] sparse_mla Q=%d Hm=%d out_width=%d fp8=%d chunks=%d tch=%d\n", Q, Hm,
