@@ -118,7 +118,10 @@ dsa_status dsa_head_gate(const float* hidden, const float* W, float* w, int M, i
  * new_from[r] for every r.  Then only the pools holding a row at or after
  * new_from[r] (p in [floor((new_from[r] - f_r)/kpool), P_r)) are written,
  * with n_pools; all other slots keep their contents (the sentinels and pools
- * of an earlier full call).  new_from = NULL recomputes every slot.
+ * of an earlier full call).  The slots must hold the result of an earlier call
+ * on the same rows before new_from[r] with the same pool_off: slot 0 of a
+ * request, when it holds a pool starting before new_from[r], supplies f_r.
+ * new_from = NULL recomputes every slot.
  * Errors: INVALID_ARG for kpool outside [1, 8] (never truncated), B < 0, NULL
  * pointers, max_cap < 0, max_new < 1 with new_from; UNSUPPORTED for D not in
  * {32, 64, 128, 256}.

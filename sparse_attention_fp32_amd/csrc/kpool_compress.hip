@@ -14,6 +14,13 @@
 // mean and variance are DPP reductions over the pool's lanes.
 // HBM-bound (2*kpool*D*2 bytes in, D*2 out per pool): no MFMA.
 //
+// Incremental mode (a decode step that appended rows) walks the rewritten
+// pools from the last one down and needs two dependent loads per request:
+// the request's geometry, then the first valid row together with the rows of
+// the pool ending at the newest row (which is where a step's work lies when
+// its newest row completes a pool).  The first valid row comes from slot 0 of
+// the earlier call whenever that slot holds a pool starting before new_from.
+//
 // Fused decode variant (dsa_gate_compress): the head-gate of the same step is
 // independent of the compression, so the same launch also runs it, split over
 // K (stkernel PR #227's split-K) in workgroups placed after the compression
@@ -123,7 +130,8 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
     const uint16_t* __restrict__ ape, const uint8_t* __restrict__ valid,
     const int32_t* __restrict__ tok_off, const int32_t* __restrict__ pool_off,
     const float* __restrict__ ln_w, const float* __restrict__ ln_b, float eps,
-    const int32_t* __restrict__ new_from, int pools_per_wg, uint16_t* __restrict__ keys,
+    const int32_t* __restrict__ new_from, int pools_per_wg, int spec_pools,
+    uint16_t* __restrict__ keys,
     int32_t* __restrict__ pool_start, uint8_t* __restrict__ pool_valid,
     int32_t* __restrict__ n_pools, int B, GateArgs ga) {
   constexpr int D = LPP * 8;
@@ -137,33 +145,15 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
   }
   const int r = blockIdx.y;
   const int t = threadIdx.x;
+  const int li = t % LPP;     // lane within the pool's lane group
+  const int grp = t / LPP;    // pool group within the workgroup
+  const int c0 = li * 8;      // first channel of this lane
+  // Loads that need no geometry go out with the geometry itself.
   const int64_t row0 = tok_off[r];
   const int T = tok_off[r + 1] - (int)row0;
   const int64_t pbase = pool_off[r];
   const int cap = pool_off[r + 1] - (int)pbase;
-
-  const int f = first_valid_row(valid, row0, T, &s_first);
-  int P = f < 0 ? 0 : (T - f) / kpool;
-  if (P > cap) P = cap;
-  if (blockIdx.x == 0 && t == 0) n_pools[r] = P;
-
-  int lo, hi;  // slots this launch rewrites
-  if (new_from) {
-    const int nf = new_from[r];
-    lo = (f >= 0 && nf >= f) ? min(P, (nf - f) / kpool) : 0;
-    hi = P;
-  } else {
-    lo = 0;
-    hi = cap;
-  }
-  const int s0 = lo + blockIdx.x * pools_per_wg;
-  const int s1 = min(hi, s0 + pools_per_wg);
-  if (s0 >= s1) return;
-
-  const int li = t % LPP;     // lane within the pool's lane group
-  const int grp = t / LPP;    // pool group within the workgroup
-  const int c0 = li * 8;      // first channel of this lane
-
+  const int nf = new_from ? new_from[r] : 0;
   float lw[8], lb[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
@@ -172,33 +162,10 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
   }
   uint4 ap[KP];
 #pragma unroll
-  for (int s = 0; s < KP; ++s)
-    ap[s] = *(const uint4*)(ape + s * D + c0);
+  for (int s = 0; s < KP; ++s) ap[s] = *(const uint4*)(ape + s * D + c0);
 
-  for (int p = s0 + grp; p < s1; p += kGroups) {
-    uint16_t* kout = keys + (pbase + p) * D + c0;
-    if (p >= P) {  // sentinel slot past the full pools
-      *(uint4*)kout = make_uint4(0, 0, 0, 0);
-      if (li == 0) {
-        pool_start[pbase + p] = -1;
-        pool_valid[pbase + p] = 0;
-      }
-      continue;
-    }
-    const int64_t rb = row0 + f + (int64_t)p * kpool;
-    // every slot load is issued at once
-    uint4 kr[KP], gr[KP];
-    uint8_t vb[KP];
-#pragma unroll
-    for (int s = 0; s < KP; ++s) {
-      const int64_t row = rb + s;
-      kr[s] = *(const uint4*)(k + row * D + c0);
-      gr[s] = *(const uint4*)(gate + row * D + c0);
-      vb[s] = valid[row];
-    }
-    int allv = 1;
-#pragma unroll
-    for (int s = 0; s < KP; ++s) allv &= vb[s] != 0;
+  // One pool: slot softmax per channel, pooling, LayerNorm, one bf16 rounding.
+  auto pool_out = [&](int p, int f, const uint4 (&kr)[KP], const uint4 (&gr)[KP], int allv) {
     float x[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -207,21 +174,17 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
       float m = -INFINITY;
 #pragma unroll
       for (int s = 0; s < KP; ++s) {
-        if (s < kpool) {
-          const uint32_t gw = u4_word(gr[s], word), aw = u4_word(ap[s], word);
-          g[s] = bf16_to_f32((gw >> sh) & 0xffffu) + bf16_to_f32((aw >> sh) & 0xffffu);
-          m = fmaxf(m, g[s]);
-        }
+        const uint32_t gw = u4_word(gr[s], word), aw = u4_word(ap[s], word);
+        g[s] = bf16_to_f32((gw >> sh) & 0xffffu) + bf16_to_f32((aw >> sh) & 0xffffu);
+        m = fmaxf(m, g[s]);
       }
       float z = 0.f, acc = 0.f;
 #pragma unroll
       for (int s = 0; s < KP; ++s) {
-        if (s < kpool) {
-          const float e = expf(g[s] - m);
-          z += e;
-          const uint32_t kw = u4_word(kr[s], word);
-          acc = fmaf(e, bf16_to_f32((kw >> sh) & 0xffffu), acc);
-        }
+        const float e = expf(g[s] - m);
+        z += e;
+        const uint32_t kw = u4_word(kr[s], word);
+        acc = fmaf(e, bf16_to_f32((kw >> sh) & 0xffffu), acc);
       }
       x[c] = acc / z;
     }
@@ -245,10 +208,86 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
       const float y1 = (x[c + 1] - mean) * rstd * lw[c + 1] + lb[c + 1];
       packed[c >> 1] = pack_bf16x2(y0, y1);
     }
-    *(uint4*)kout = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    *(uint4*)(keys + (pbase + p) * D + c0) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
     if (li == 0) {
       pool_start[pbase + p] = f + p * kpool;
       pool_valid[pbase + p] = (uint8_t)allv;
+    }
+  };
+  // The kpool rows from row0 + rs: all loads issued together; the validity
+  // bytes are consumed at once (so no later instruction waits on them alone).
+  auto load_rows = [&](const uint16_t* kb, const uint16_t* gb, const uint8_t* vbp, int64_t rs,
+                       uint4 (&kr)[KP], uint4 (&gr)[KP]) {
+    uint8_t vb[KP];
+#pragma unroll
+    for (int s = 0; s < KP; ++s) {
+      kr[s] = *(const uint4*)(kb + (rs + s) * D + c0);
+      gr[s] = *(const uint4*)(gb + (rs + s) * D + c0);
+      vb[s] = vbp[rs + s];
+    }
+    int allv = 1;
+#pragma unroll
+    for (int s = 0; s < KP; ++s) allv &= vb[s] != 0;
+    return allv;
+  };
+
+  if (!new_from) {
+    // full mode: every slot of the request, in ascending order
+    const int f = first_valid_row(valid, row0, T, &s_first);
+    int P = f < 0 ? 0 : (T - f) / kpool;
+    if (P > cap) P = cap;
+    if (blockIdx.x == 0 && t == 0) n_pools[r] = P;
+    const int s0 = blockIdx.x * pools_per_wg;
+    const int s1 = min(cap, s0 + pools_per_wg);
+    for (int p = s0 + grp; p < s1; p += kGroups) {
+      if (p >= P) {  // sentinel slot past the full pools
+        *(uint4*)(keys + (pbase + p) * D + c0) = make_uint4(0, 0, 0, 0);
+        if (li == 0) {
+          pool_start[pbase + p] = -1;
+          pool_valid[pbase + p] = 0;
+        }
+        continue;
+      }
+      uint4 kr[KP], gr[KP];
+      const int allv = load_rows(k, gate, valid, row0 + f + (int64_t)p * kpool, kr, gr);
+      pool_out(p, f, kr, gr, allv);
+    }
+    return;
+  }
+
+  // Incremental mode: the pools holding a row at or after new_from are
+  // rewritten, walked from the last pool down (group grp of workgroup x takes
+  // the (x*pools_per_wg + grp)-th pool from the end).  In decode the newest
+  // row creates work only when it completes a pool, and then the pools end
+  // exactly at row T; so the rows of this group's pool under that alignment
+  // load right away, before the first valid row f is known.  f itself comes
+  // from slot 0 of the earlier call (the start of pool 0) when that slot holds
+  // a pool starting before new_from -- rows before new_from are unchanged, so
+  // f is too -- and from the scan otherwise.
+  const int i0 = blockIdx.x * pools_per_wg + grp;
+  const bool spec = i0 < spec_pools && T >= kpool * (i0 + 1);
+  const int64_t srs = spec ? row0 + T - (int64_t)kpool * (i0 + 1) : 0;
+  uint4 skr[KP], sgr[KP];
+  // (with no such rows the loads read ln_w, which is at least a row long)
+  const int sallv = load_rows(spec ? k : (const uint16_t*)ln_w, spec ? gate : (const uint16_t*)ln_w,
+                              spec ? valid : (const uint8_t*)ln_w, srs, skr, sgr);
+  const int fc = *(cap > 0 ? pool_start + pbase : new_from + r);  // (unused when cap == 0)
+  const bool cached = cap > 0 && fc >= 0 && fc < nf;
+  const int f = cached ? fc : first_valid_row(valid, row0, T, &s_first);
+  int P = f < 0 ? 0 : (T - f) / kpool;
+  if (P > cap) P = cap;
+  if (blockIdx.x == 0 && t == 0) n_pools[r] = P;
+  const int lo = (f >= 0 && nf >= f) ? min(P, (nf - f) / kpool) : 0;
+  const bool aligned = f >= 0 && (T - f) % kpool == 0;
+  for (int i = i0, j = 0; j * kGroups < pools_per_wg; ++j, i += kGroups) {
+    const int p = P - 1 - i;
+    if (p < lo) break;
+    if (j == 0 && aligned) {
+      pool_out(p, f, skr, sgr, sallv);
+    } else {
+      uint4 kr[KP], gr[KP];
+      const int allv = load_rows(k, gate, valid, row0 + f + (int64_t)p * kpool, kr, gr);
+      pool_out(p, f, kr, gr, allv);
     }
   }
 }
@@ -283,11 +322,12 @@ dsa_status launch_compress(const uint16_t* k, const uint16_t* gate, const uint16
                            const char* who) {
   const int lpp = D / 8;
   const int groups = 256 / lpp;
-  int ppw, nx;
+  int ppw, nx, spec = 0;
   if (new_from) {
     const int touch = (max_new + kpool - 1) / kpool;  // pools one request can touch
     ppw = groups;
     nx = (touch + ppw - 1) / ppw;
+    spec = touch;
   } else {
     ppw = groups * 4;
     nx = (max_cap + ppw - 1) / ppw;
@@ -301,7 +341,7 @@ dsa_status launch_compress(const uint16_t* k, const uint16_t* gate, const uint16
             D, kpool, max_cap, new_from != nullptr, ga.nwg, grid.x, grid.y);
 #define DSA_LAUNCH_KP(LPP, KP)                                                                 \
   kpool_compress_kernel<LPP, KP><<<grid, 256, 0, stream>>>(                                     \
-      k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b, eps, new_from, ppw, keys, pool_start, \
+      k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b, eps, new_from, ppw, spec, keys, pool_start, \
       pool_valid, n_pools, B, ga)
 #define DSA_LAUNCH_KP_D(KP)            \
   switch (lpp) {                       \

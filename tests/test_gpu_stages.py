@@ -110,6 +110,46 @@ def test_kpool_compress_incremental(case):
     PT.check_compress(g, ref2)
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_kpool_compress_incremental_multi(case, fused):
+    """A step that rewrote the last kpool+1 rows of every request: several
+    pools per request are touched, the first and last of them in any
+    alignment with the request's first valid row."""
+    from sparse_attention_fp32_amd import dsa
+    spec, xn, ref, xg = case
+    _say(f"kpool_compress incremental kpool+1 rows {spec.name} fused={fused}")
+    st = _step(xg)
+    st.compress()
+    n = spec.kpool + 1
+    offs = xn["tok_off"]
+    k2, g2 = xg.k.clone(), xg.gate.clone()
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    nf = []
+    for r in range(spec.B):
+        T = int(offs[r + 1] - offs[r])
+        lo = max(T - n, 0)
+        nf.append(lo)
+        for row in range(int(offs[r]) + lo, int(offs[r + 1])):
+            k2[row] = torch.randn(spec.index_dim, generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+            g2[row] = torch.randn(spec.index_dim, generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+    nf_t = torch.tensor(nf, dtype=torch.int32, device="cuda")
+    x = xg
+    if fused:
+        dsa.dsa_gate_compress(x.hidden, x.W, st.gate_part, k2, g2, x.ape, x.valid, x.tok_off,
+                              x.pool_off, x.ln_w, x.ln_b, spec.eps, spec.kpool, st.max_cap, st.keys,
+                              st.pool_start, st.pool_valid, st.n_pools, new_from=nf_t, max_new=n)
+    else:
+        dsa.dsa_kpool_compress(k2, g2, x.ape, x.valid, x.tok_off, x.pool_off, x.ln_w, x.ln_b,
+                               spec.eps, spec.kpool, st.max_cap, st.keys, st.pool_start,
+                               st.pool_valid, st.n_pools, new_from=nf_t, max_new=n)
+    ref2 = O.kpool_compress(k2.cpu().numpy(), g2.cpu().numpy(), xn["ape"], xn["valid"], xn["tok_off"],
+                            xn["pool_off"], xn["ln_w"], xn["ln_b"], spec.eps, spec.kpool)
+    ncap = int(xn["pool_off"][-1])
+    g = {"keys": _np(st.keys).view(np.uint16)[:ncap], "pool_start": _np(st.pool_start)[:ncap],
+         "pool_valid": _np(st.pool_valid)[:ncap], "n_pools": _np(st.n_pools)}
+    PT.check_compress(g, ref2)
+
+
 def _load_oracle_front(st, ref):
     ncap = len(ref["pool_start"])
     st.w.copy_(torch.from_numpy(ref["w"]))
