@@ -30,6 +30,7 @@ using namespace dsa;
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+constexpr int kStage = 2048;  // largest select_k whose output is staged in LDS
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 // number of set bits of m below this lane
@@ -83,6 +84,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   __shared__ int s_ecnt[E * kWaves];  // per (e, wave) counts
   __shared__ int s_eoff[E * kWaves];  // their exclusive prefix in (e, wave) order
   __shared__ int s_bin, s_above, s_binc;
+  // kept ids and their start rows in output order (when select_k <= kStage),
+  // written out coalesced
+  __shared__ int s_kid[kStage], s_kps[EXPAND ? kStage : 1];
   const int q = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const float* srow = scores + (int64_t)q * pstride;
   const uint8_t* crow = cand + (int64_t)q * pstride;
@@ -307,6 +311,27 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   __syncthreads();
   if (wv == 0) wave0_offsets<E>(s_ecnt, s_eoff, lane);
   __syncthreads();
+  if (select_k <= kStage) {
+    // positions into LDS, then every output row written in order by all threads
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int pos = s_eoff[e * kWaves + wv] + lanes_below(bk[e]);
+      if (keep[e] && pos < k_eff) {
+        s_kid[pos] = t + kThreads * e;
+        if (EXPAND) s_kps[pos] = ps[e];
+      }
+    }
+    __syncthreads();
+    for (int i = t; i < select_k; i += kThreads) out[i] = i < k_eff ? s_kid[i] : -1;
+    if (EXPAND) {
+      const int kp = ex.kpool;
+      for (int i = t; i < ex.out_width; i += kThreads) {
+        const int j = i / kp;
+        trow[i] = j < k_eff ? s_kps[j] + (i - j * kp) : -1;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int pos = s_eoff[e * kWaves + wv] + lanes_below(bk[e]);

@@ -32,7 +32,48 @@ def _rows(rng, Q, P, kind):
 CASES = [(P, k, kind) for P in (30, 1000, 1024, 2047, 4096, 8192, 16384)
          for k in (1, 64, 512) for kind in ("normal", "ties", "wide")]
 CASES += [(8192, 512, "equal"), (8192, 512, "negative"), (4096, 100, "zeros"),
-          (16384, 256, "negative"), (1024, 2000, "normal")]
+          (16384, 256, "negative"), (1024, 2000, "normal"),
+          # budgets above the 2048 staged in LDS take the direct-store path
+          (16384, 4000, "normal"), (8192, 3000, "ties"), (4096, 2049, "wide")]
+
+
+def _case_rows(P, k, kind):
+    rng = np.random.default_rng(hash((P, k, kind)) & 0xFFFF)
+    Q = 6
+    s = _rows(rng, Q, P, kind)
+    c = (rng.random((Q, P)) < 0.8).astype(np.uint8)
+    c[1] = 0                          # a row without candidates
+    c[2, :] = 0
+    c[2, : min(P, 3)] = 1             # a row with fewer candidates than most k
+    s = np.where(c == 1, s, -np.inf).astype(np.float32)
+    return rng, s, c
+
+
+@pytest.mark.parametrize("P,k,kind", CASES)
+def test_topk_expand_exact(P, k, kind):
+    """The fused top-k + expansion: sel as the oracle's top-k, tok as the
+    oracle's expansion of it (one request per row, pool starts spaced by
+    kpool from a random first row, a -1 tail)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rng, s, c = _case_rows(P, k, kind)
+    Q = s.shape[0]
+    kpool = 3
+    out_width = k * kpool + 5
+    pool_off = np.arange(Q + 1, dtype=np.int32) * P
+    first = rng.integers(0, 50, size=Q)
+    pool_start = np.concatenate([f + kpool * np.arange(P) for f in first]).astype(np.int32)
+    q_req = np.arange(Q, dtype=np.int32)
+    ref_sel = O.topk_pools(s, c, k)
+    ref_tok = O.expand_selection(ref_sel, pool_start, pool_off, q_req, kpool, out_width)
+    sel = torch.full((Q, k), 12345, dtype=torch.int32, device="cuda")
+    tok = torch.full((Q, out_width), 12345, dtype=torch.int32, device="cuda")
+    dsa.dsa_topk_expand(torch.from_numpy(s).cuda(), torch.from_numpy(c).cuda(),
+                        torch.from_numpy(pool_start).cuda(), torch.from_numpy(pool_off).cuda(),
+                        torch.from_numpy(q_req).cuda(), kpool, sel, tok)
+    torch.cuda.synchronize()
+    assert np.array_equal(sel.cpu().numpy(), ref_sel)
+    assert np.array_equal(tok.cpu().numpy(), ref_tok)
 
 
 @pytest.mark.parametrize("P,k,kind", CASES)
