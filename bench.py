@@ -13,10 +13,12 @@ every step streams its keys and latent rows from HBM.  Each set's calls are
 captured once in a HIP graph; the timed region replays K graphs.  The same
 step through the six separate calls is timed too, for comparison.
 
-The JSON line also carries, for the kernel that takes the most time, its
-algorithmic bytes per launch over its average launch time (HIP events on the
-launch stream), against the 8 TB/s HBM peak; and the CPU oracle's throughput
-on a bounded sample of the same workload (rank 0 only).
+The JSON line also carries, for the call that takes the most time, its
+algorithmic bytes per launch over its average launch time (a graph of 32
+back-to-back calls of that kind, replayed between HIP events on the launch
+stream),
+against the 8 TB/s HBM peak; and the CPU oracle's throughput on a bounded
+sample of the same workload (rank 0 only).
 """
 from __future__ import annotations
 
@@ -150,7 +152,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="decode32k", choices=W.WORKLOADS)
     ap.add_argument("--sets", type=int, default=8)
-    ap.add_argument("--stage-reps", type=int, default=48)
+    ap.add_argument("--stage-reps", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -224,8 +226,24 @@ def main():
     six_us = ms6 / max(1, a.steps // 4) * 1e3
     del graphs6
 
-    # -- per-call launch times (HIP events on the launch stream) ---------------
+    # -- per-call launch times: a graph of kCallsPerGraph back-to-back calls of
+    # one kind (the input sets in rotation), replayed between HIP events on the
+    # launch stream; the time per call is what the step's own graph sees, with
+    # the host's graph-launch cost spread over many calls
     stream = torch.cuda.current_stream()
+    kCallsPerGraph = 32
+
+    def call_graph(fn):
+        for st in steps:
+            fn(st)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(kCallsPerGraph):
+                fn(steps[i % len(steps)])
+        torch.cuda.synchronize()
+        return g
+
     fns = {
         "gate_compress": lambda s: s.gate_compress(incremental=True),
         "index_scores_gated": lambda s: s.index_scores_gated(),
@@ -238,18 +256,12 @@ def main():
         "sparse_mla_decode": lambda s: s.mla(),
     }
     call_us = {}
-    for name in fns:
-        evs = []
-        for i in range(a.stage_reps):
-            s = steps[i % len(steps)]
-            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            ea.record(stream)
-            fns[name](s)
-            eb.record(stream)
-            evs.append((ea, eb))
-        torch.cuda.synchronize()
-        d = [ea.elapsed_time(eb) * 1e3 for ea, eb in evs[4:]]
-        call_us[name] = float(np.mean(d))
+    reps = max(1, a.stage_reps // kCallsPerGraph)
+    for name, fn in fns.items():
+        g = call_graph(fn)
+        ms_c, _ = timed([g], reps, 1)
+        call_us[name] = ms_c / (reps * kCallsPerGraph) * 1e3
+        del g
     stage_us = {k: call_us[k] for k in STAGES}
 
     xn0 = {"q_req": sets[0].q_req.cpu().numpy()}
