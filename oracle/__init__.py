@@ -21,6 +21,7 @@ from .dsa_oracle import (  # noqa: F401
     index_scores,
     topk_pools,
     expand_selection,
+    select_tail,
     sparse_mla_decode,
     select_k,
     out_width,

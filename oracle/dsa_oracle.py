@@ -279,6 +279,33 @@ def expand_selection(sel, pool_start, pool_off, q_req, kpool: int, out_width_: i
     return tok
 
 
+def select_tail(tok, valid, tok_off, q_req, q_pos, kpool: int, select_k_: int):
+    """always_select_tail  [Atlas DSA page, Glm5NextDsaConfig::out_width: the
+    tail adds kpool - 1 slots to the emitted row].
+
+    For a query at request-local position t of request r, with first valid row
+    f: the pools that are candidates for it are the full pools ending at or
+    before t, P_t = floor((t + 1 - f) / kpool) of them; the rows after them up
+    to t, f + P_t*kpool .. t (fewer than kpool rows), are the query's tail.
+    Its valid rows, in ascending order, go to the slots select_k*kpool,
+    select_k*kpool + 1, ...; the other tail slots are -1.  Nothing else of the
+    row changes.  A query before f has no tail."""
+    tok = np.array(tok, dtype=np.int32, copy=True)
+    first, _ = kpool_geometry(valid, tok_off, kpool)
+    base = select_k_ * kpool
+    tok[:, base:base + kpool - 1] = -1
+    for q in range(tok.shape[0]):
+        r = int(q_req[q])
+        f, t = int(first[r]), int(q_pos[q])
+        if f < 0 or t < f:
+            continue
+        lo = f + ((t + 1 - f) // kpool) * kpool
+        rows = [x for x in range(lo, t + 1) if valid[int(tok_off[r]) + x]]
+        assert len(rows) <= kpool - 1
+        tok[q, base:base + len(rows)] = rows
+    return tok
+
+
 # ---------------------------------------------------------------------------
 # a6: NoPE MLA over the selected tokens  [Atlas DSA page, Traps (NoPE) and the
 # MASKED_ATTN_MAX_KEYS note: a per-row gather equals the dense set-membership
@@ -331,11 +358,12 @@ def sparse_mla_decode(q, ckv, ckv_scale, kv_off, q_req, tok, sm_scale: float,
 
 def dsa_step(x: dict, kpool: int, select_k_: int, out_width_: int, pstride: int,
              eps: float, sm_scale: float, new_from=None, prev=None,
-             queries: Optional[Iterable[int]] = None) -> dict:
+             queries: Optional[Iterable[int]] = None, always_select_tail: bool = False) -> dict:
     """One pass of the whole path on the numpy arrays of one input set, in the
     order of the pipeline diagram: head gate, compression, scores, top-k,
-    expansion, sparse MLA.  ``queries`` restricts the per-query stages (and
-    the compression to those queries' requests)."""
+    expansion (with the tail when always_select_tail), sparse MLA.
+    ``queries`` restricts the per-query stages (and the compression to those
+    queries' requests)."""
     qlist = None if queries is None else list(queries)
     reqs = None if qlist is None else sorted({int(x["q_req"][q]) for q in qlist})
     w = head_gate(x["hidden"], x["W"])
@@ -347,6 +375,8 @@ def dsa_step(x: dict, kpool: int, select_k_: int, out_width_: int, pstride: int,
                                 pstride, queries=qlist)
     sel = topk_pools(scores, cand, select_k_, queries=qlist)
     tok = expand_selection(sel, comp["pool_start"], x["pool_off"], x["q_req"], kpool, out_width_)
+    if always_select_tail:
+        tok = select_tail(tok, x["valid"], x["tok_off"], x["q_req"], x["q_pos"], kpool, select_k_)
     mla = sparse_mla_decode(x["q_mla"], x["ckv"], x.get("ckv_scale"), x["kv_off"], x["q_req"],
                             tok, sm_scale, queries=qlist)
     return {"w": w, **comp, "scores": scores, "cand": cand, "sel": sel, "tok": tok, **mla}

@@ -50,6 +50,7 @@ class Spec:
     latent_fp8: bool = False
     sm_scale: float = 1.0
     eps: float = 1e-5
+    always_select_tail: bool = False  # out_width then holds select_k*kpool + kpool-1 ids
 
     @property
     def B(self) -> int:
@@ -119,6 +120,11 @@ def spec_by_name(name: str, seed: int = 0) -> Spec:
         return Spec(name, lengths=[1000, 517, 2053], pads=[3, 0, 61], kpool=4, index_heads=16,
                     index_dim=128, hidden=1024, select_k=100, out_width=404, mla_heads=64,
                     q_req=[0, 0, 1, 2, 2], q_pos=[999, 480, 516, 2052, 700])
+    if name == "medium_tail":    # the medium shape with always_select_tail
+        return Spec(name, lengths=[1000, 517, 2053], pads=[3, 0, 61], kpool=4, index_heads=16,
+                    index_dim=128, hidden=1024, select_k=100, out_width=403, mla_heads=64,
+                    q_req=[0, 0, 1, 2, 2], q_pos=[999, 480, 516, 2052, 62],
+                    always_select_tail=True)
     if name == "medium_fp8":
         return Spec(name, lengths=[777, 1500, 96, 2500], pads=[0, 17, 95, 5], kpool=8,
                     index_heads=12, index_dim=64, hidden=768, select_k=40, out_width=330,
@@ -127,7 +133,7 @@ def spec_by_name(name: str, seed: int = 0) -> Spec:
 
 
 WORKLOADS = ("tiny", "decode32k", "longctx", "prefill4k", "mixed64")
-PARITY_SHAPES = ("tiny", "medium", "medium_fp8")
+PARITY_SHAPES = ("tiny", "medium", "medium_fp8", "medium_tail")
 
 
 @dataclasses.dataclass

@@ -447,3 +447,74 @@ def test_mla_sm_scale_scales_logits():
     q2 = O.f64_to_bf16_bits(2 * O.bf16_bits_to_f64(q))        # doubling is exact in bf16
     b = O.sparse_mla_decode(q2, ckv, None, np.int32([0]), np.int32([0]), tok, 1.0)
     assert np.max(np.abs(a["out_f64"] - b["out_f64"])) < 1e-14
+
+
+# ---- always_select_tail ------------------------------------------------------
+
+def test_select_tail_worked_example_golden():
+    g = json.load(open(os.path.join(GOLD, "tail_worked.json")))
+    valid = np.array(g["valid"], dtype=np.uint8)
+    q = len(g["q_pos"])
+    out = O.select_tail(np.array(g["tok_in"], dtype=np.int32), valid, np.array([0, g["T"]]),
+                        np.zeros(q, dtype=np.int32), np.array(g["q_pos"]), g["kpool"], g["select_k"])
+    assert np.array_equal(out, np.array(g["tok_out"]))
+
+
+def test_select_tail_brute_force_against_pool_geometry():
+    """The tail of a query at t, row by row: a valid row at or after the first
+    valid row and at or before t that lies in no full pool ending at or before
+    t -- the pools taken from the compression's pool starts, not from the
+    tail's own arithmetic."""
+    rng = np.random.default_rng(21)
+    for trial in range(60):
+        kpool = int(rng.integers(1, 9))
+        B = 3
+        lengths = rng.integers(1, 60, size=B)
+        tok_off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+        valid = np.ones(int(tok_off[-1]), dtype=np.uint8)
+        for r in range(B):
+            pad = int(rng.integers(0, lengths[r] + 1))
+            valid[tok_off[r]:tok_off[r] + pad] = 0
+            if rng.random() < 0.5 and lengths[r] > pad + 2:      # a hole after f
+                valid[tok_off[r] + int(rng.integers(pad + 1, lengths[r]))] = 0
+        pool_off = np.concatenate([[0], np.cumsum(lengths // kpool)]).astype(np.int64)
+        D = 8
+        z = np.zeros((int(tok_off[-1]), D), dtype=np.uint16)
+        comp = O.kpool_compress(z, z, np.zeros((kpool, D), np.uint16), valid, tok_off, pool_off,
+                                np.ones(D), np.zeros(D), 1e-5, kpool)
+        q_req = np.repeat(np.arange(B), 4)
+        q_pos = np.array([int(rng.integers(0, lengths[r])) for r in q_req])
+        q_pos[::4] = lengths[q_req[::4]] - 1                       # one decode query each
+        select_k = 2
+        tok_in = np.full((len(q_req), select_k * kpool + kpool - 1), -1, dtype=np.int32)
+        out = O.select_tail(tok_in, valid, tok_off, q_req, q_pos, kpool, select_k)
+        for q in range(len(q_req)):
+            r, t = int(q_req[q]), int(q_pos[q])
+            starts = [int(comp["pool_start"][pool_off[r] + p]) for p in range(int(comp["n_pools"][r]))]
+            v = valid[tok_off[r]:tok_off[r + 1]]
+            nz = np.flatnonzero(v)
+            f = int(nz[0]) if len(nz) else -1
+            want = []
+            for x in range(0, t + 1):
+                if not v[x] or f < 0 or x < f:
+                    continue
+                if any(s <= x <= s + kpool - 1 and s + kpool - 1 <= t for s in starts):
+                    continue
+                want.append(x)
+            got = [int(x) for x in out[q, select_k * kpool:] if x >= 0]
+            assert got == want, (trial, q, got, want)
+            assert len(got) <= kpool - 1
+            assert np.all(out[q, :select_k * kpool] == -1)
+
+
+def test_select_tail_decode_closed_form():
+    """Decode (t = T-1) with no holes: the tail is exactly the trailing partial
+    pool, rows f + P*kpool .. T-1 of the geometry."""
+    valid = np.array([0] * 3 + [1] * 30, dtype=np.uint8)
+    tok_off = np.array([0, 33])
+    first, n_pools = O.kpool_geometry(valid, tok_off, 4)
+    out = O.select_tail(np.full((1, 8 + 3), -1, np.int32), valid, tok_off, np.array([0]),
+                        np.array([32]), 4, 2)
+    lo = int(first[0] + n_pools[0] * 4)
+    assert list(out[0, 8:8 + (33 - lo)]) == list(range(lo, 33))
+    assert lo == 31 and out[0, 10] == -1
