@@ -183,8 +183,8 @@ dsa_status dsa_topk_pools(const float* scores, const uint8_t* cand, int Q, int p
  * for sel[q, j] >= 0 and s < kpool; every other element of the [Q, out_width]
  * row is -1.  Ids are request-local row positions.
  * sel [Q, select_k] i32; pool_start, pool_off, q_req as above; tok
- * [Q, out_width] i32.  flags must be 0 (bit 0, always_select_tail, is not
- * built yet).
+ * [Q, out_width] i32.  flags must be 0 (bit 0 is reserved: the
+ * always_select_tail slots are written by dsa_select_tail afterwards).
  * Errors: INVALID_ARG for out_width < select_k * kpool (the page's
  * topk-multiple-of-kpool rule), kpool outside [1, 8], select_k < 1, unknown
  * flag bits, NULL pointers; UNSUPPORTED for flag bit 0.
@@ -193,6 +193,31 @@ dsa_status dsa_expand_selection(const int32_t* sel, const int32_t* pool_start,
                                 const int32_t* pool_off, const int32_t* q_req, int Q, int select_k,
                                 int kpool, int out_width, int flags, int32_t* tok,
                                 hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * always_select_tail   [Atlas page, Glm5NextDsaConfig::out_width: the tail adds
+ *     kpool - 1 slots to the emitted row]
+ *
+ * Run after dsa_expand_selection or dsa_topk_expand on the same tok rows.  For
+ * query q at request-local position t = q_pos[q] of request r = q_req[q], with
+ * first valid row f_r: the pools that count for q are the full pools ending at
+ * or before t, P_t = floor((t + 1 - f_r) / kpool) of them; the rows after them
+ * up to t (fewer than kpool) are q's tail.  Its valid rows, in ascending
+ * order, are written to tok[q, select_k*kpool + i]; the rest of those kpool-1
+ * slots get -1.  No other element of the row is touched; a query before f_r
+ * has no tail.  f_r is read as pool_start of the request's pool 0 when
+ * n_pools[r] > 0 (so pool_start and n_pools must be this step's compression
+ * output).
+ * valid [sumT] u8; tok_off [B+1], pool_start, pool_off [B+1], n_pools [B],
+ * q_req, q_pos [Q] i32; tok [Q, out_width] i32.
+ * Errors: INVALID_ARG for kpool outside [1, 8], select_k < 1, out_width <
+ * select_k*kpool + kpool - 1, Q < 0, NULL pointers.  kpool = 1 has no tail
+ * slots and launches nothing.
+ * ------------------------------------------------------------------------- */
+dsa_status dsa_select_tail(const uint8_t* valid, const int32_t* tok_off, const int32_t* pool_start,
+                           const int32_t* pool_off, const int32_t* n_pools, const int32_t* q_req,
+                           const int32_t* q_pos, int Q, int kpool, int select_k, int out_width,
+                           int32_t* tok, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * a6. NoPE sparse MLA decode   [Atlas page, "Traps" (NoPE: the latent is both

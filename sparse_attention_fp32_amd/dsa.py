@@ -51,6 +51,7 @@ _SIGS = {
     "dsa_index_scores_gated": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                                     _I, _P, _P, _P]),
     "dsa_topk_expand": (_I, [_P, _P, _I, _I, _I, _P, _P, _P, _I, _I, _I, _P, _P, _P]),
+    "dsa_select_tail": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
 }
 
 
@@ -264,3 +265,13 @@ def dsa_topk_expand(scores, cand, pool_start, pool_off, q_req, kpool: int, sel, 
         _dev(pool_start, _I32, "pool_start"), _dev(pool_off, _I32, "pool_off"),
         _dev(q_req, _I32, "q_req"), kpool, out_width, flags, _dev(sel, _I32, "sel"),
         _dev(tok, _I32, "tok"), _stream(stream)))
+
+
+def dsa_select_tail(valid, tok_off, pool_start, pool_off, n_pools, q_req, q_pos, kpool: int,
+                    select_k: int, tok, stream=None) -> None:
+    Q, out_width = tok.shape
+    _check(lib().dsa_select_tail(
+        _dev(valid, _U8, "valid"), _dev(tok_off, _I32, "tok_off"), _dev(pool_start, _I32, "pool_start"),
+        _dev(pool_off, _I32, "pool_off"), _dev(n_pools, _I32, "n_pools"), _dev(q_req, _I32, "q_req"),
+        _dev(q_pos, _I32, "q_pos"), Q, kpool, select_k, out_width, _dev(tok, _I32, "tok"),
+        _stream(stream)))

@@ -71,6 +71,15 @@ class DsaStep:
     def expand(self):
         dsa.dsa_expand_selection(self.sel, self.pool_start, self.x.pool_off, self.x.q_req,
                                  self.spec.kpool, self.tok, stream=self.stream)
+        self.tail()
+
+    def tail(self):
+        """always_select_tail: the query's own recent rows after the pools' tokens."""
+        if self.spec.always_select_tail:
+            x = self.x
+            dsa.dsa_select_tail(x.valid, x.tok_off, self.pool_start, x.pool_off, self.n_pools,
+                                x.q_req, x.q_pos, self.spec.kpool, self.spec.select_k, self.tok,
+                                stream=self.stream)
 
     def mla(self):
         x = self.x
@@ -97,6 +106,7 @@ class DsaStep:
     def topk_expand(self):
         dsa.dsa_topk_expand(self.scores, self.cand, self.pool_start, self.x.pool_off, self.x.q_req,
                             self.spec.kpool, self.sel, self.tok, stream=self.stream)
+        self.tail()
 
     def run_fused(self, incremental: bool = False):
         """The decode step through the fused calls: four calls, five launches."""

@@ -17,7 +17,7 @@ NUL = ctypes.c_void_p(None)
 
 def test_exports_every_declared_function():
     names = dsa.header_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     import subprocess
     out = subprocess.run(["nm", "-D", "--defined-only", dsa.LIB_PATH], capture_output=True, text=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
@@ -160,3 +160,19 @@ def test_fused_call_errors():
     assert te(kpool=9) == INV
     assert te(flags=1) == UNS
     assert te(tok=NUL) == INV
+
+
+def test_select_tail_errors():
+    L = dsa.lib()
+    def call(kpool=4, select_k=2, out_width=11, Q=3, tok=FAKE):
+        return L.dsa_select_tail(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, Q, kpool, select_k,
+                                 out_width, tok, NUL)
+    assert call(out_width=10) == INV          # select_k*kpool + kpool-1 slots needed
+    assert "kpool-1" in dsa.last_error()
+    assert call(kpool=0) == INV
+    assert call(kpool=9) == INV
+    assert call(select_k=0) == INV
+    assert call(Q=-1) == INV
+    assert call(tok=NUL) == INV
+    assert call(Q=0) == dsa.DSA_OK
+    assert call(kpool=1, out_width=2) == dsa.DSA_OK   # kpool 1 has no tail slots

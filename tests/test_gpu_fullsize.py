@@ -51,7 +51,7 @@ def test_fullsize(name):
 
     _say(f"fullsize {name}: oracle on queries {sample}")
     ref = O.dsa_step(xn, spec.kpool, spec.select_k, spec.out_width, spec.pstride(), spec.eps,
-                     spec.sm_scale, queries=sample)
+                     spec.sm_scale, queries=sample, always_select_tail=spec.always_select_tail)
 
     ncap = int(xn["pool_off"][-1])
 

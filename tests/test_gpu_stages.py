@@ -33,7 +33,7 @@ def case(request):
     x = W.make_inputs(spec, seed=0)
     xn = x.numpy()
     ref = O.dsa_step(xn, spec.kpool, spec.select_k, spec.out_width, spec.pstride(), spec.eps,
-                     spec.sm_scale)
+                     spec.sm_scale, always_select_tail=spec.always_select_tail)
     return spec, xn, ref, x.to("cuda")
 
 
@@ -191,6 +191,26 @@ def test_expand_isolated(case):
     _poison(st.tok)
     st.expand()
     assert np.array_equal(_np(st.tok), ref["tok"])
+
+
+def test_select_tail_isolated(case):
+    """The tail alone, on the oracle's expansion without it."""
+    from sparse_attention_fp32_amd import dsa
+    spec, xn, ref, xg = case
+    if not spec.always_select_tail:
+        pytest.skip("shape without always_select_tail")
+    _say(f"select_tail {spec.name}")
+    st = _step(xg)
+    _load_oracle_front(st, ref)
+    pre = O.expand_selection(ref["sel"], ref["pool_start"], xn["pool_off"], xn["q_req"], spec.kpool,
+                             spec.out_width)
+    st.tok.copy_(torch.from_numpy(pre))
+    dsa.dsa_select_tail(xg.valid, xg.tok_off, st.pool_start, xg.pool_off, st.n_pools, xg.q_req,
+                        xg.q_pos, spec.kpool, spec.select_k, st.tok)
+    assert np.array_equal(_np(st.tok), ref["tok"])
+    # every query of this shape has a tail slot in use or a -1 there, never a stale id
+    base = spec.select_k * spec.kpool
+    assert np.any(ref["tok"][:, base:] >= 0)
 
 
 def test_mla_isolated(case):
