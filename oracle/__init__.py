@@ -23,6 +23,10 @@ from .dsa_oracle import (  # noqa: F401
     expand_selection,
     select_tail,
     sparse_mla_decode,
+    sparse_mla_decode_paged,
+    paged_rows,
+    kv_index,
+    attend_rows,
     select_k,
     out_width,
     dsa_step,

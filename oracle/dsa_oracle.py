@@ -27,6 +27,8 @@ Readings of points the pages leave open (each repeated where it is used):
   the lower pool id, and lists them by ascending pool id; the rest is -1.
 * an empty selection row gives O = 0 and lse = -inf.
 * fp8 latent rows are OCP E4M3FN codes times one f32 scale per row.
+* a paged latent cache is a pool of equal pages; a [B, max_blocks] block
+  table names the page of each request's block of page_rows logical rows.
 """
 from __future__ import annotations
 
@@ -328,19 +330,66 @@ def sparse_mla_decode(q, ckv, ckv_scale, kv_off, q_req, tok, sm_scale: float,
     so keys and values are both the kv_lora-wide latent):
     l_j = sm_scale * <Q[q,h], c_j>, O = sum_j softmax(l)_j c_j, lse = log sum_j
     exp l_j.  O is rounded once to bf16; an empty row gives O = 0, lse = -inf."""
+    tok = np.asarray(tok)
+    base = np.asarray(kv_off, dtype=np.int64)[np.asarray(q_req, dtype=np.int64)]
+    rows = np.where(tok >= 0, base[:, None] + tok.astype(np.int64), -1)
+    return attend_rows(q, ckv, ckv_scale, rows, sm_scale, queries, heads)
+
+
+def paged_rows(block_table, page_rows: int, r: int, t) -> np.ndarray:
+    """Physical cache row of request r's logical positions t in a paged latent
+    cache (the block-table paged decode of the Atlas DSA page's
+    MASKED_ATTN_MAX_KEYS note): the cache is a pool of pages of page_rows rows;
+    block b = t // page_rows of request r sits in physical page
+    block_table[r, b], at row t % page_rows of it.  Reading: block_table is
+    [B, max_blocks] row-major, page ids index pages from the start of the
+    cache."""
+    t = np.asarray(t, dtype=np.int64)
+    bt = np.asarray(block_table, dtype=np.int64)
+    return bt[r, t // page_rows] * page_rows + t % page_rows
+
+
+def kv_index(tok, q_req, block_table, page_rows: int) -> np.ndarray:
+    """The physical index row of every query (the page's step taps keep the
+    logical selection and the physical indices apart): paged_rows of each
+    selected id, -1 where tok is -1."""
+    tok = np.asarray(tok)
+    out = np.full(tok.shape, -1, dtype=np.int64)
+    for qq in range(tok.shape[0]):
+        sel = tok[qq] >= 0
+        out[qq, sel] = paged_rows(block_table, page_rows, int(q_req[qq]), tok[qq, sel])
+    return out
+
+
+def sparse_mla_decode_paged(q, ckv, ckv_scale, block_table, page_rows: int, q_req, tok,
+                            sm_scale: float, queries: Optional[Iterable[int]] = None,
+                            heads: Optional[Iterable[int]] = None) -> dict:
+    """sparse_mla_decode over a paged latent cache: the selected logical ids
+    are mapped to physical rows through the block table (kv_index), then the
+    same attention.  Also returns the physical index rows as "kvidx"."""
+    rows = kv_index(tok, q_req, block_table, page_rows)
+    res = attend_rows(q, ckv, ckv_scale, rows, sm_scale, queries, heads)
+    res["kvidx"] = rows
+    return res
+
+
+def attend_rows(q, ckv, ckv_scale, rows, sm_scale: float,
+                queries: Optional[Iterable[int]] = None,
+                heads: Optional[Iterable[int]] = None) -> dict:
+    """The attention of sparse_mla_decode over explicit cache rows: rows[q, j]
+    is a row of ckv, or -1 for no token."""
     Q, Hm, L = q.shape
     out64 = np.zeros((Q, Hm, L), dtype=np.float64)
     lse = np.full((Q, Hm), -np.inf, dtype=np.float64)
     qs = range(Q) if queries is None else queries
     hs = np.arange(Hm) if heads is None else np.asarray(list(heads))
     for qq in qs:
-        r = int(q_req[qq])
-        t = np.asarray(tok[qq])
+        t = np.asarray(rows[qq])
         t = t[t >= 0]
         if len(t) == 0:
             continue
-        assert len(np.unique(t)) == len(t), "duplicate token ids in one selection row"
-        C = latent_rows_f64(ckv, ckv_scale, int(kv_off[r]) + t.astype(np.int64))   # [n, L]
+        assert len(np.unique(t)) == len(t), "duplicate rows in one selection row"
+        C = latent_rows_f64(ckv, ckv_scale, t.astype(np.int64))                    # [n, L]
         Qh = bf16_bits_to_f64(q[qq][hs])                                           # [h, L]
         logits = sm_scale * (Qh @ C.T)                                             # [h, n]
         m = logits.max(axis=1, keepdims=True)

@@ -387,8 +387,8 @@ def test_expand_worked_example_golden():
 # a6 sparse MLA
 # ---------------------------------------------------------------------------
 
-def _mla_case(rng, T=40, Hm=4, L=512, n_sel=None, fp8=False):
-    q = bf16(rng.standard_normal((1, Hm, L)))
+def _mla_case(rng, T=40, Hm=4, L=512, n_sel=None, fp8=False, Q=1):
+    q = bf16(rng.standard_normal((Q, Hm, L)))
     lat = rng.standard_normal((T, L)) / math.sqrt(L)
     if fp8:
         scale = (np.abs(lat).max(1) / 448).astype(np.float32)
@@ -518,3 +518,72 @@ def test_select_tail_decode_closed_form():
     lo = int(first[0] + n_pools[0] * 4)
     assert list(out[0, 8:8 + (33 - lo)]) == list(range(lo, 33))
     assert lo == 31 and out[0, 10] == -1
+
+
+# ---- paged latent cache ------------------------------------------------------
+
+def test_paged_kv_index_worked_example_golden():
+    g = gold("paged_worked.json")
+    for c in g["cases"]:
+        got = O.kv_index(np.array(c["tok"]), np.array(c["q_req"]), np.array(c["block_table"]),
+                         c["page_rows"])
+        assert np.array_equal(got, np.array(c["kvidx"]))
+
+
+def _scatter_pages(ckv, scale, kv_off, lengths, page_rows, rng):
+    """Lay each request's rows into pages taken in a random order from a pool
+    that also holds junk pages, one row at a time; returns the paged cache and
+    its block table."""
+    nblk = [(n + page_rows - 1) // page_rows for n in lengths]
+    n_pages = sum(nblk) + 3
+    order = rng.permutation(n_pages)
+    pages = np.empty((n_pages * page_rows,) + ckv.shape[1:], dtype=ckv.dtype)
+    pages[...] = rng.integers(0, 1 << 14, size=pages.shape).astype(ckv.dtype)   # junk rows
+    pscale = None if scale is None else rng.uniform(0.5, 2.0, n_pages * page_rows)
+    table = np.zeros((len(lengths), max(nblk) + 2), dtype=np.int32)
+    k = 0
+    for r, n in enumerate(lengths):
+        for b in range(nblk[r]):
+            table[r, b] = order[k]
+            k += 1
+        for t in range(n):
+            dst = table[r, t // page_rows] * page_rows + t % page_rows
+            pages[dst] = ckv[kv_off[r] + t]
+            if scale is not None:
+                pscale[dst] = scale[kv_off[r] + t]
+    return pages, pscale, table
+
+
+@pytest.mark.parametrize("page_rows", [1, 3, 16])
+def test_paged_mla_equals_flat_over_shuffled_pages(page_rows):
+    """The same logical rows laid out in shuffled pages (among junk pages) give
+    exactly the flat cache's attention, in bf16 and fp8."""
+    rng = np.random.default_rng(22)
+    lengths = [37, 20, 45]
+    kv_off = np.concatenate([[0], np.cumsum(lengths)[:-1]]).astype(np.int64)
+    for fp8 in (False, True):
+        q, ckv, scale = _mla_case(rng, fp8=fp8, T=int(sum(lengths)), Q=4)
+        q_req = np.array([0, 1, 2, 2])
+        tok = np.full((4, 24), -1, dtype=np.int32)
+        for qq, r in enumerate(q_req):
+            ids = rng.choice(lengths[r], size=min(18, lengths[r]), replace=False)
+            tok[qq, rng.choice(24, size=len(ids), replace=False)] = ids
+        flat = O.sparse_mla_decode(q, ckv, scale, kv_off, q_req, tok, 0.9)
+        pages, pscale, table = _scatter_pages(ckv, scale, kv_off, lengths, page_rows, rng)
+        paged = O.sparse_mla_decode_paged(q, pages, pscale, table, page_rows, q_req, tok, 0.9)
+        assert np.array_equal(paged["out_f64"], flat["out_f64"])
+        assert np.array_equal(paged["lse"], flat["lse"])
+        assert np.all((paged["kvidx"] >= 0) == (tok >= 0))
+
+
+def test_paged_identity_table_is_the_flat_cache():
+    """page_rows = 1 and block_table[r, b] = kv_off[r] + b is the flat layout."""
+    rng = np.random.default_rng(23)
+    q, ckv, _ = _mla_case(rng, T=30, Q=2)
+    kv_off = np.array([0, 11])
+    table = np.stack([np.arange(19), 11 + np.arange(19)])
+    tok = np.int32([[0, 4, 10, -1], [18, 3, -1, 7]])
+    flat = O.sparse_mla_decode(q, ckv, None, kv_off, np.array([0, 1]), tok, 1.0)
+    paged = O.sparse_mla_decode_paged(q, ckv, None, table, 1, np.array([0, 1]), tok, 1.0)
+    assert np.array_equal(paged["out"], flat["out"])
+    assert np.array_equal(paged["kvidx"], np.int64([[0, 4, 10, -1], [29, 14, -1, 18]]))
