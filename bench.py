@@ -11,7 +11,9 @@ cached rows, one query each) by default.  Eight input sets (each larger than
 the 256 MB last-level cache together with its outputs) are rotated so that
 every step streams its keys and latent rows from HBM.  Each set's calls are
 captured once in a HIP graph; the timed region replays K graphs.  The same
-step through the six separate calls is timed too, for comparison.
+step through the six separate calls is timed too, for comparison, and the
+step with the attention reading a paged copy of the latent cache (64-row pages
+in shuffled order, through a block table).
 
 The JSON line also carries, for the call that takes the most time, its
 algorithmic bytes per launch over its average launch time (a graph of 32
@@ -154,6 +156,8 @@ def main():
     ap.add_argument("--sets", type=int, default=8)
     ap.add_argument("--stage-reps", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--page-rows", type=int, default=64,
+                    help="also time the step over a paged copy of the latent cache (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     a = ap.parse_args()
@@ -225,6 +229,17 @@ def main():
     ms6, _ = timed(graphs6, max(1, a.steps // 4), max(1, a.warmup // 4))
     six_us = ms6 / max(1, a.steps // 4) * 1e3
     del graphs6
+    # the same step with the attention over a paged copy of the latent cache
+    paged = None
+    if a.page_rows > 0:
+        for i, st in enumerate(steps):
+            st.pc = W.make_paged_cache(sets[i], a.page_rows, seed=i)
+        graphs_p = capture(lambda st: st.run_fused(incremental=True, paged=st.pc))
+        ms_p, _ = timed(graphs_p, max(1, a.steps // 4), max(1, a.warmup // 4))
+        paged = {"page_rows": a.page_rows,
+                 "table_cols": int(steps[0].pc.block_table.shape[1]),
+                 "step_us": round(ms_p / max(1, a.steps // 4) * 1e3, 2)}
+        del graphs_p
 
     # -- per-call launch times: a graph of kCallsPerGraph back-to-back calls of
     # one kind (the input sets in rotation), replayed between HIP events on the
@@ -255,6 +270,8 @@ def main():
         "expand_selection": lambda s: s.expand(),
         "sparse_mla_decode": lambda s: s.mla(),
     }
+    if paged is not None:
+        fns["sparse_mla_decode_paged"] = lambda s: s.mla_paged(s.pc)
     call_us = {}
     reps = max(1, a.stage_reps // kCallsPerGraph)
     for name, fn in fns.items():
@@ -263,6 +280,8 @@ def main():
         call_us[name] = ms_c / (reps * kCallsPerGraph) * 1e3
         del g
     stage_us = {k: call_us[k] for k in STAGES}
+    if paged is not None:
+        paged["mla_us"] = round(call_us["sparse_mla_decode_paged"], 2)
 
     xn0 = {"q_req": sets[0].q_req.cpu().numpy()}
     nb = algorithmic_bytes(spec, xn0, steps[0].n_pools.cpu().numpy(), steps[0].tok.cpu().numpy())
@@ -308,6 +327,7 @@ def main():
         "stage_bytes": {k: int(nb[k]) for k in STAGES},
         "six_call_step_us": round(six_us, 2),
         "call_us": {k: round(call_us[k], 2) for k in CALLS},
+        "paged": paged,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),

@@ -251,6 +251,36 @@ dsa_status dsa_sparse_mla_decode(const uint16_t* q, const void* ckv, const float
                                  size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * a6 over a paged latent cache   [Atlas page, the MASKED_ATTN_MAX_KEYS note
+ *     (the serving decode is a block-table paged, online-softmax MLA that walks
+ *     a selected-index row) and the step taps (the logical selection and the
+ *     physical indices are kept apart)]
+ *
+ * As dsa_sparse_mla_decode, with the rows found through a block table instead
+ * of kv_off: the cache is n_pages pages of page_rows rows each (ckv
+ * [n_pages * page_rows, L], ckv_scale the same rows for fp8), and request r's
+ * logical row x is physical row
+ *     block_table[r * bt_stride + x / page_rows] * page_rows + x % page_rows.
+ * block_table [B, bt_stride] i32, row-major (entries past a request's blocks
+ * are never read as pages; any value).  kvidx [Q, out_width] i32 or NULL:
+ * receives the physical row of every selected id, -1 where tok is -1.
+ * The workspace is dsa_sparse_mla_decode_workspace_size's.
+ * Ids must lie inside their request's blocks and table entries inside the
+ * cache; out-of-range block numbers and page numbers are clamped (to the table
+ * row, to the cache), so a bad table gives wrong rows, never an access outside
+ * block_table or ckv.
+ * Errors: those of dsa_sparse_mla_decode; INVALID_ARG for bt_stride,
+ * page_rows or n_pages < 1; UNSUPPORTED for n_pages * page_rows > 2^31 - 1.
+ * ------------------------------------------------------------------------- */
+dsa_status dsa_sparse_mla_decode_paged(const uint16_t* q, const void* ckv, const float* ckv_scale,
+                                       int latent_dtype, const int32_t* block_table,
+                                       int bt_stride, int page_rows, int n_pages,
+                                       const int32_t* q_req, const int32_t* tok, int Q, int Hm,
+                                       int L, int out_width, float sm_scale, uint16_t* out,
+                                       float* lse, int32_t* kvidx, void* ws, size_t ws_bytes,
+                                       hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Fused decode calls   [stkernel pull request #290 measures what each launch
  *     of a serving step costs; the Atlas page's pipeline order is kept]
  *

@@ -29,6 +29,14 @@
 // the logits and the probabilities instead of the data.  With more than one
 // chunk, per-chunk (max, sum) pairs and unnormalised O (bf16) go to the
 // workspace and mla_combine_kernel merges them in chunk order.
+//
+// Paged cache (dsa_sparse_mla_decode_paged): the same kernel with the chunk's
+// ids mapped to physical rows in the prologue.  The request's block-table row
+// (up to kMaxBt entries) loads together with the ids and the Q rows and goes
+// to LDS; each id then becomes page * page_rows + offset before it is staged,
+// so the main loop is the flat kernel's.  Longer table rows read the entries
+// past kMaxBt from memory.  Page numbers are clamped to the cache and block
+// numbers to the table row, so no id can address memory outside them.
 #include <limits.h>
 
 #include "dsa_device.hpp"
@@ -47,6 +55,7 @@ constexpr int kHeadsWG = 16 * kHT;        // heads per workgroup
 constexpr int kTargetWG = 512;            // aim for two workgroups per CU
 constexpr int kMinSubPerChunk = 4;        // >= 128 ids per chunk keeps partials small
 constexpr int kMaxTch = 2048;             // most ids per chunk
+constexpr int kMaxBt = 2048;              // block-table entries staged in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -98,10 +107,18 @@ struct RowSlice<true> {
   uint2 v[2][4];  // 8 fp8 codes
 };
 
-template <bool FP8>
+// Where the rows live: flat (request r's row x at kv_off[r] + x) or paged.
+struct CacheMap {
+  const int32_t* kv_off;       // flat
+  const int32_t* block_table;  // paged: [B, bt_stride]
+  int bt_stride, page_rows, n_pages;
+  int32_t* kvidx;              // paged, optional: [Q, out_width] physical rows
+};
+
+template <bool FP8, bool PAGED>
 __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ ckv_v,
-    const float* __restrict__ ckv_scale, const int32_t* __restrict__ kv_off,
+    const float* __restrict__ ckv_scale, const CacheMap cm,
     const int32_t* __restrict__ q_req, const int32_t* __restrict__ tok, int Hm, int out_width,
     int tch, float sm_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
     uint16_t* __restrict__ part_o, float* __restrict__ part_ml) {
@@ -114,7 +131,8 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
   __shared__ __attribute__((aligned(16))) float s_bias[kSub];  // 0, or -inf for no token
   __shared__ __attribute__((aligned(16))) float s_scl[kSub];   // row scale (1 for bf16)
   __shared__ float s_lrun[kHeadsWG];
-  __shared__ int s_id[kMaxTch];            // the chunk's token ids (-1: none)
+  __shared__ int s_id[kMaxTch];            // the chunk's cache rows (-1: none)
+  __shared__ int s_bt[PAGED ? kMaxBt : 1];  // the request's block-table row
 
   const int chunk = blockIdx.x, nchunks = gridDim.x, hb = blockIdx.y, qx = blockIdx.z;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -135,7 +153,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
   // one sub-chunk is read in a later one except the latent rows.
   const int nid = nsub * kSub;
   const int r = q_req[qx];
-  const int id0 = trow[min(j0 + t, max(j1 - 1, 0))];
+  int id0 = trow[min(j0 + t, max(j1 - 1, 0))];
 
   // Q^T operand: qb[ht][kk] = Q[head hb*32 + ht*16 + col][dim0 + kk*32 + grp*8 .. +8].
   // Heads past Hm repeat head Hm-1: their softmax rows are computed and never
@@ -148,13 +166,47 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) qb[ht][kk] = as_bf16x8(*(const uint4*)(qrow + kk * 32));
   }
-  const int64_t rowbase = kv_off[r];
+  int64_t rowbase = 0;
+  constexpr int kBtPerThread = PAGED ? kMaxBt / 256 : 1;
+  int btv[kBtPerThread];
+  const int32_t* btrow = nullptr;
+  if constexpr (PAGED) {
+    btrow = cm.block_table + (int64_t)r * cm.bt_stride;
+#pragma unroll
+    for (int k = 0; k < kBtPerThread; ++k) btv[k] = btrow[min(t + 256 * k, cm.bt_stride - 1)];
+  } else {
+    rowbase = cm.kv_off[r];
+  }
   asm volatile("" ::: "memory");  // every load above is issued before any wait below
-  s_id[t] = j0 + t < j1 ? id0 : -1;  // (entries past nid are never read)
-  for (int i = t + 256; i < nid; i += 256) {
-    const int j = j0 + i;
-    const int v = trow[min(j, j1 - 1)];
-    s_id[i] = j < j1 ? v : -1;
+  if constexpr (PAGED) {
+    asm volatile("" : "+v"(id0));  // loaded here, before the table's loads are waited for
+#pragma unroll
+    for (int k = 0; k < kBtPerThread; ++k) s_bt[t + 256 * k] = btv[k];
+    __syncthreads();
+    // logical id -> physical row; the optional index row is written once per
+    // chunk (by the first head block)
+    const unsigned pr = cm.page_rows;
+    auto phys = [&](int id) {
+      const unsigned b = (unsigned)id / pr, off = (unsigned)id - b * pr;
+      const unsigned bc = min(b, (unsigned)cm.bt_stride - 1);
+      const int pg = bc < (unsigned)kMaxBt ? s_bt[bc] : btrow[bc];
+      return (int)(min((unsigned)pg, (unsigned)cm.n_pages - 1) * pr + off);
+    };
+    int32_t* krow = cm.kvidx && hb == 0 ? cm.kvidx + (int64_t)qx * out_width : nullptr;
+    for (int i = t; i < nid; i += 256) {
+      const int j = j0 + i;
+      const int v = i < 256 ? id0 : trow[min(j, j1 - 1)];
+      const int pv = j < j1 && v >= 0 ? phys(v) : -1;
+      s_id[i] = pv;
+      if (krow && j < j1) krow[j] = pv;
+    }
+  } else {
+    s_id[t] = j0 + t < j1 ? id0 : -1;  // (entries past nid are never read)
+    for (int i = t + 256; i < nid; i += 256) {
+      const int j = j0 + i;
+      const int v = trow[min(j, j1 - 1)];
+      s_id[i] = j < j1 ? v : -1;
+    }
   }
   __syncthreads();
 
@@ -445,6 +497,69 @@ DSA_EXPORT size_t dsa_sparse_mla_decode_workspace_size(int Q, int Hm, int L_, in
   return rows * L * sizeof(uint16_t) + rows * 2 * sizeof(float);
 }
 
+namespace {
+
+dsa_status launch_mla(const uint16_t* q, const void* ckv, const float* ckv_scale, int latent_dtype,
+                      const CacheMap& cm, bool paged, const int32_t* q_req, const int32_t* tok,
+                      int Q, int Hm, int L_, int out_width, float sm_scale, uint16_t* out,
+                      float* lse, void* ws, size_t ws_bytes, hipStream_t stream, const char* who) {
+  DSA_REQUIRE(L_ == L, DSA_ERR_UNSUPPORTED,
+              "%s: latent width L=%d, the kernels read exactly %d (a NoPE cache row is "
+              "kv_lora_rank wide)",
+              who, L_, L);
+  DSA_REQUIRE(Hm >= 1, DSA_ERR_INVALID_ARG, "%s: Hm=%d < 1 (no heads)", who, Hm);
+  DSA_REQUIRE(out_width >= 1, DSA_ERR_INVALID_ARG, "%s: out_width=%d < 1", who, out_width);
+  DSA_REQUIRE(Q >= 0, DSA_ERR_INVALID_ARG, "%s: Q=%d < 0", who, Q);
+  DSA_REQUIRE(latent_dtype == DSA_LATENT_BF16 || latent_dtype == DSA_LATENT_FP8_E4M3,
+              DSA_ERR_INVALID_ARG, "%s: unknown latent dtype %d", who, latent_dtype);
+  DSA_REQUIRE(latent_dtype != DSA_LATENT_FP8_E4M3 || ckv_scale, DSA_ERR_INVALID_ARG,
+              "%s: fp8 latent without row scales", who);
+  if (paged) {
+    DSA_REQUIRE(cm.bt_stride >= 1 && cm.page_rows >= 1 && cm.n_pages >= 1, DSA_ERR_INVALID_ARG,
+                "%s: bt_stride=%d, page_rows=%d, n_pages=%d (each must be >= 1)", who,
+                cm.bt_stride, cm.page_rows, cm.n_pages);
+    DSA_REQUIRE((long long)cm.n_pages * cm.page_rows <= INT_MAX, DSA_ERR_UNSUPPORTED,
+                "%s: %d pages of %d rows exceed 2^31-1 cache rows", who, cm.n_pages,
+                cm.page_rows);
+  }
+  if (Q == 0) return DSA_OK;
+  DSA_REQUIRE(q && ckv && (paged ? cm.block_table != nullptr : cm.kv_off != nullptr) && q_req &&
+                  tok && out,
+              DSA_ERR_INVALID_ARG, "%s: NULL tensor pointer", who);
+  const size_t need = dsa_sparse_mla_decode_workspace_size(Q, Hm, L_, out_width, latent_dtype);
+  DSA_REQUIRE(ws_bytes >= need && (need == 0 || ws), DSA_ERR_INVALID_ARG,
+              "%s: workspace %zu bytes, need %zu", who, ws_bytes, need);
+  const Chunking ch = mla_chunking(Q, Hm, out_width);
+  uint16_t* part_o = need ? (uint16_t*)ws : nullptr;
+  float* part_ml = need ? (float*)((uint16_t*)ws + (size_t)Q * ch.nchunks * Hm * L) : nullptr;
+  dim3 grid(ch.nchunks, (Hm + kHeadsWG - 1) / kHeadsWG, Q);
+  DSA_REQUIRE(grid.y <= 65535u && grid.z <= 65535u, DSA_ERR_UNSUPPORTED,
+              "%s: Q=%d or Hm=%d outside the launch grid", who, Q, Hm);
+  const float sm_log2 = sm_scale * kLog2e;
+  if (dsa::trace_enabled())
+    fprintf(stderr, "[dsa] %s Q=%d Hm=%d out_width=%d fp8=%d paged=%d chunks=%d tch=%d\n", who, Q,
+            Hm, out_width, latent_dtype, (int)paged, ch.nchunks, ch.tch);
+#define DSA_LAUNCH_MLA(F, P)                                                              \
+  sparse_mla_kernel<F, P><<<grid, 256, 0, stream>>>(q, ckv, ckv_scale, cm, q_req, tok, Hm, \
+                                                    out_width, ch.tch, sm_log2, out, lse,  \
+                                                    part_o, part_ml)
+  const bool fp8 = latent_dtype == DSA_LATENT_FP8_E4M3;
+  if (paged) {
+    if (fp8) DSA_LAUNCH_MLA(true, true);
+    else DSA_LAUNCH_MLA(false, true);
+  } else {
+    if (fp8) DSA_LAUNCH_MLA(true, false);
+    else DSA_LAUNCH_MLA(false, false);
+  }
+#undef DSA_LAUNCH_MLA
+  dsa_status st = dsa::check_launch(who);
+  if (st != DSA_OK || ch.nchunks == 1) return st;
+  mla_combine_kernel<<<dim3((Hm + 3) / 4, Q), 256, 0, stream>>>(part_o, part_ml, ch.nchunks, Hm, out, lse);
+  return dsa::check_launch(who);
+}
+
+}  // namespace
+
 DSA_EXPORT dsa_status dsa_sparse_mla_decode(const uint16_t* q, const void* ckv,
                                             const float* ckv_scale, int latent_dtype,
                                             const int32_t* kv_off, const int32_t* q_req,
@@ -452,43 +567,17 @@ DSA_EXPORT dsa_status dsa_sparse_mla_decode(const uint16_t* q, const void* ckv,
                                             int out_width, float sm_scale, uint16_t* out,
                                             float* lse, void* ws, size_t ws_bytes,
                                             hipStream_t stream) {
-  DSA_REQUIRE(L_ == L, DSA_ERR_UNSUPPORTED,
-              "dsa_sparse_mla_decode: latent width L=%d, the kernels read exactly %d (a NoPE "
-              "cache row is kv_lora_rank wide)",
-              L_, L);
-  DSA_REQUIRE(Hm >= 1, DSA_ERR_INVALID_ARG, "dsa_sparse_mla_decode: Hm=%d < 1 (no heads)", Hm);
-  DSA_REQUIRE(out_width >= 1, DSA_ERR_INVALID_ARG, "dsa_sparse_mla_decode: out_width=%d < 1",
-              out_width);
-  DSA_REQUIRE(Q >= 0, DSA_ERR_INVALID_ARG, "dsa_sparse_mla_decode: Q=%d < 0", Q);
-  DSA_REQUIRE(latent_dtype == DSA_LATENT_BF16 || latent_dtype == DSA_LATENT_FP8_E4M3,
-              DSA_ERR_INVALID_ARG, "dsa_sparse_mla_decode: unknown latent dtype %d",
-              latent_dtype);
-  DSA_REQUIRE(latent_dtype != DSA_LATENT_FP8_E4M3 || ckv_scale, DSA_ERR_INVALID_ARG,
-              "dsa_sparse_mla_decode: fp8 latent without row scales");
-  if (Q == 0) return DSA_OK;
-  DSA_REQUIRE(q && ckv && kv_off && q_req && tok && out, DSA_ERR_INVALID_ARG,
-              "dsa_sparse_mla_decode: NULL tensor pointer");
-  const size_t need = dsa_sparse_mla_decode_workspace_size(Q, Hm, L_, out_width, latent_dtype);
-  DSA_REQUIRE(ws_bytes >= need && (need == 0 || ws), DSA_ERR_INVALID_ARG,
-              "dsa_sparse_mla_decode: workspace %zu bytes, need %zu", ws_bytes, need);
-  const Chunking ch = mla_chunking(Q, Hm, out_width);
-  uint16_t* part_o = need ? (uint16_t*)ws : nullptr;
-  float* part_ml = need ? (float*)((uint16_t*)ws + (size_t)Q * ch.nchunks * Hm * L) : nullptr;
-  dim3 grid(ch.nchunks, (Hm + kHeadsWG - 1) / kHeadsWG, Q);
-  const float sm_log2 = sm_scale * kLog2e;
-  if (dsa::trace_enabled())
-    fprintf(stderr, "[dsa] sparse_mla Q=%d Hm=%d out_width=%d fp8=%d chunks=%d tch=%d\n", Q, Hm,
-            out_width, latent_dtype, ch.nchunks, ch.tch);
-  if (latent_dtype == DSA_LATENT_FP8_E4M3)
-    sparse_mla_kernel<true><<<grid, 256, 0, stream>>>(q, ckv, ckv_scale, kv_off, q_req, tok, Hm,
-                                                      out_width, ch.tch, sm_log2, out, lse,
-                                                      part_o, part_ml);
-  else
-    sparse_mla_kernel<false><<<grid, 256, 0, stream>>>(q, ckv, ckv_scale, kv_off, q_req, tok, Hm,
-                                                       out_width, ch.tch, sm_log2, out, lse,
-                                                       part_o, part_ml);
-  dsa_status st = dsa::check_launch("dsa_sparse_mla_decode");
-  if (st != DSA_OK || ch.nchunks == 1) return st;
-  mla_combine_kernel<<<dim3((Hm + 3) / 4, Q), 256, 0, stream>>>(part_o, part_ml, ch.nchunks, Hm, out, lse);
-  return dsa::check_launch("dsa_sparse_mla_decode (combine)");
+  CacheMap cm{kv_off, nullptr, 0, 0, 0, nullptr};
+  return launch_mla(q, ckv, ckv_scale, latent_dtype, cm, false, q_req, tok, Q, Hm, L_, out_width,
+                    sm_scale, out, lse, ws, ws_bytes, stream, "dsa_sparse_mla_decode");
+}
+
+DSA_EXPORT dsa_status dsa_sparse_mla_decode_paged(
+    const uint16_t* q, const void* ckv, const float* ckv_scale, int latent_dtype,
+    const int32_t* block_table, int bt_stride, int page_rows, int n_pages, const int32_t* q_req,
+    const int32_t* tok, int Q, int Hm, int L_, int out_width, float sm_scale, uint16_t* out,
+    float* lse, int32_t* kvidx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  CacheMap cm{nullptr, block_table, bt_stride, page_rows, n_pages, kvidx};
+  return launch_mla(q, ckv, ckv_scale, latent_dtype, cm, true, q_req, tok, Q, Hm, L_, out_width,
+                    sm_scale, out, lse, ws, ws_bytes, stream, "dsa_sparse_mla_decode_paged");
 }

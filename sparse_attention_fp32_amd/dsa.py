@@ -44,6 +44,8 @@ _SIGS = {
     "dsa_sparse_mla_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "dsa_sparse_mla_decode": (_I, [_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P,
                                    _Z, _P]),
+    "dsa_sparse_mla_decode_paged": (_I, [_P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _I, _I, _I, _I,
+                                         _F, _P, _P, _P, _P, _Z, _P]),
     "dsa_gate_split_count": (_I, [_I, _I, _I]),
     "dsa_gate_compress_workspace_size": (_Z, [_I, _I, _I]),
     "dsa_gate_compress": (_I, [_P, _P, _I, _I, _I, _P, _Z, _P, _P, _P, _P, _P, _P, _P, _P, _F,
@@ -210,6 +212,30 @@ def dsa_sparse_mla_decode(q, ckv, ckv_scale, kv_off, q_req, tok, sm_scale: float
         _dev(kv_off, _I32, "kv_off"), _dev(q_req, _I32, "q_req"), _dev(tok, _I32, "tok"), Q, Hm, L,
         out_width, float(sm_scale), _dev(out, _BF, "out"), _dev(lse, torch.float32, "lse", allow_none=True),
         wp, wb, _stream(stream)))
+
+
+def dsa_sparse_mla_decode_paged(q, ckv, ckv_scale, block_table, page_rows: int, q_req, tok,
+                                sm_scale: float, out, lse=None, ws=None, kvidx=None,
+                                stream=None) -> None:
+    """ckv: [n_pages * page_rows, L] (bf16 bits, or fp8 codes with ckv_scale);
+    block_table: [B, bt_stride] i32; kvidx: optional [Q, out_width] i32 output."""
+    Q, Hm, L = q.shape
+    out_width = tok.shape[1]
+    fp8 = ckv.dtype in (torch.uint8, torch.float8_e4m3fn)
+    dt = LATENT_FP8_E4M3 if fp8 else LATENT_BF16
+    if page_rows < 1 or ckv.shape[0] % page_rows:
+        raise ValueError(f"cache of {ckv.shape[0]} rows is not a whole number of {page_rows}-row pages")
+    if fp8 and (ckv_scale is None or ckv_scale.numel() < ckv.shape[0]):
+        raise ValueError("fp8 cache needs one scale per cache row")
+    wp, wb = _ws(ws)
+    _check(lib().dsa_sparse_mla_decode_paged(
+        _dev(q, _BF, "q"), _dev(ckv, (torch.uint8, torch.float8_e4m3fn) if fp8 else _BF, "ckv"),
+        _dev(ckv_scale, torch.float32, "ckv_scale", allow_none=not fp8), dt,
+        _dev(block_table, _I32, "block_table"), block_table.shape[1], int(page_rows),
+        ckv.shape[0] // page_rows, _dev(q_req, _I32, "q_req"), _dev(tok, _I32, "tok"), Q, Hm, L,
+        out_width, float(sm_scale), _dev(out, _BF, "out"),
+        _dev(lse, torch.float32, "lse", allow_none=True),
+        _dev(kvidx, _I32, "kvidx", allow_none=True), wp, wb, _stream(stream)))
 
 
 # --- fused decode calls ----------------------------------------------------

@@ -87,6 +87,18 @@ class DsaStep:
                                   self.spec.sm_scale, self.out, self.lse, self.ws_mla,
                                   stream=self.stream)
 
+    def mla_paged(self, pc, kvidx: bool = False):
+        """The MLA over a paged copy of the latent cache (a workloads.PagedCache);
+        with kvidx, the physical index rows go to self.kvidx."""
+        x = self.x
+        if kvidx and getattr(self, "kvidx", None) is None:
+            self.kvidx = torch.empty(self.spec.Q, self.spec.out_width, dtype=torch.int32,
+                                     device=x.k.device)
+        dsa.dsa_sparse_mla_decode_paged(x.q_mla, pc.ckv, pc.ckv_scale, pc.block_table,
+                                        pc.page_rows, x.q_req, self.tok, self.spec.sm_scale,
+                                        self.out, self.lse, self.ws_mla,
+                                        kvidx=self.kvidx if kvidx else None, stream=self.stream)
+
     # -- fused decode calls (same outputs, fewer launches) ---------------------
     def gate_compress(self, incremental: bool = False):
         x = self.x
@@ -108,12 +120,16 @@ class DsaStep:
                             self.spec.kpool, self.sel, self.tok, stream=self.stream)
         self.tail()
 
-    def run_fused(self, incremental: bool = False):
-        """The decode step through the fused calls: four calls, five launches."""
+    def run_fused(self, incremental: bool = False, paged=None):
+        """The decode step through the fused calls: four calls, five launches
+        (the MLA over ``paged``, a workloads.PagedCache, when given)."""
         self.gate_compress(incremental)
         self.index_scores_gated()
         self.topk_expand()
-        self.mla()
+        if paged is None:
+            self.mla()
+        else:
+            self.mla_paged(paged)
 
     def run(self, incremental: bool = False):
         self.head_gate()

@@ -256,3 +256,72 @@ def make_inputs(spec: Spec, seed: int = 0, device: str = "cpu") -> Inputs:
         q_mla=q_mla, ckv=ckv, ckv_scale=ckv_scale,
         kv_off=torch.tensor(offs[:-1], **i32),
     )
+
+
+@dataclasses.dataclass
+class PagedCache:
+    """The latent cache of an input set laid out in pages."""
+    ckv: torch.Tensor                  # [n_pages * page_rows, L] bf16 bits or fp8 codes
+    ckv_scale: Optional[torch.Tensor]  # [n_pages * page_rows] f32 for fp8, else None
+    block_table: torch.Tensor          # [B, bt_stride] i32
+    page_rows: int
+
+    @property
+    def n_pages(self) -> int:
+        return self.ckv.shape[0] // self.page_rows
+
+
+def make_paged_cache(x: Inputs, page_rows: int, seed: int = 0, spare_pages: int = 3,
+                     extra_blocks: int = 1) -> PagedCache:
+    """Copy the latent rows of ``x`` into pages of ``page_rows`` rows.  Page 0
+    and ``spare_pages`` more hold junk rows (large values, so that reading
+    one changes a result); every request's blocks take the other pages in a
+    seeded random order, and the rows past its length in its last page are
+    junk too.  The table has ``extra_blocks`` columns more than the longest
+    request needs; entries past a request's blocks name page 0."""
+    s = x.spec
+    dev = x.ckv.device
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 104, page_rows])))
+    nblk = [(t + page_rows - 1) // page_rows for t in s.lengths]
+    n_pages = 1 + spare_pages + sum(nblk)
+    order = 1 + rng.permutation(n_pages - 1)
+    table = np.zeros((s.B, max(nblk) + extra_blocks), dtype=np.int32)
+    k = 0
+    for r in range(s.B):
+        table[r, :nblk[r]] = order[k:k + nblk[r]]
+        k += nblk[r]
+    st = _Streams(int(rng.integers(1 << 30)), str(dev))
+    junk = st.normal((n_pages * page_rows, s.latent), std=50.0)
+    if s.latent_fp8:
+        ckv, scale = _fp8_rows(junk)
+    else:
+        ckv, scale = _bf16_bits(junk), None
+    del junk
+    # destination row of every logical row, request by request
+    dst = []
+    for r in range(s.B):
+        t = np.arange(s.lengths[r], dtype=np.int64)
+        dst.append(table[r, t // page_rows].astype(np.int64) * page_rows + t % page_rows)
+    dst_t = torch.from_numpy(np.concatenate(dst)).to(dev)
+    ckv[dst_t] = x.ckv
+    if scale is not None:
+        scale[dst_t] = x.ckv_scale
+    return PagedCache(ckv=ckv, ckv_scale=scale, block_table=torch.from_numpy(table).to(dev),
+                      page_rows=page_rows)
+
+
+def random_selection(spec: Spec, seed: int = 0, holes: float = 0.1) -> torch.Tensor:
+    """A selection row per query for running the attention stage on its own:
+    distinct request-local ids drawn uniformly from the query's request, in
+    random order, with about ``holes`` of the slots left at -1.  [Q, out_width]
+    i32 on the CPU."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 105])))
+    q_req = spec.query_req()
+    tok = np.full((spec.Q, spec.out_width), -1, dtype=np.int32)
+    for q, r in enumerate(q_req):
+        n = min(spec.out_width, spec.lengths[r])
+        ids = rng.choice(spec.lengths[r], size=n, replace=False)
+        keep = rng.random(n) >= holes
+        slots = rng.permutation(spec.out_width)[:n]
+        tok[q, slots[keep]] = ids[keep]
+    return torch.from_numpy(tok)

@@ -17,7 +17,7 @@ NUL = ctypes.c_void_p(None)
 
 def test_exports_every_declared_function():
     names = dsa.header_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     import subprocess
     out = subprocess.run(["nm", "-D", "--defined-only", dsa.LIB_PATH], capture_output=True, text=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
@@ -176,3 +176,21 @@ def test_select_tail_errors():
     assert call(tok=NUL) == INV
     assert call(Q=0) == dsa.DSA_OK
     assert call(kpool=1, out_width=2) == dsa.DSA_OK   # kpool 1 has no tail slots
+
+
+def test_sparse_mla_paged_errors():
+    L = dsa.lib()
+    need = dsa.sparse_mla_decode_workspace_size(16, 64, 512, 2048, 0)
+    def call(L_=512, bt_stride=512, page_rows=64, n_pages=9000, Q=16, bt=FAKE, ws=FAKE, wsb=need):
+        return L.dsa_sparse_mla_decode_paged(FAKE, FAKE, NUL, 0, bt, bt_stride, page_rows, n_pages,
+                                             FAKE, FAKE, Q, 64, L_, 2048, 1.0, FAKE, NUL, NUL, ws,
+                                             wsb, NUL)
+    assert call(L_=576) == UNS
+    assert call(bt_stride=0) == INV
+    assert call(page_rows=0) == INV
+    assert "page_rows=0" in dsa.last_error()
+    assert call(n_pages=0) == INV
+    assert call(n_pages=1 << 20, page_rows=4096) == UNS     # 2^32 rows
+    assert call(bt=NUL) == INV
+    assert call(wsb=need - 1) == INV
+    assert call(Q=0) == dsa.DSA_OK
