@@ -17,6 +17,10 @@ from .dsa_oracle import (  # noqa: F401
     head_gate,
     kpool_geometry,
     kpool_compress,
+    request_rows,
+    layer_norm_rows,
+    indexer_store,
+    write_geom,
     slot_weights,
     index_scores,
     topk_pools,

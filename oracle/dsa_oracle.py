@@ -108,7 +108,19 @@ def head_gate(hidden: np.ndarray, W: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 
-def kpool_geometry(valid: np.ndarray, tok_off: np.ndarray, kpool: int):
+def request_rows(tok_off, r: int, seq_len=None) -> tuple:
+    """The cache rows of request r: [tok_off[r], tok_off[r] + T_r) with T_r the
+    live length seq_len[r] when given (a request's region may hold more rows
+    than it has written), else the whole region up to tok_off[r+1]."""
+    lo = int(tok_off[r])
+    hi = int(tok_off[r + 1])
+    if seq_len is not None:
+        assert 0 <= int(seq_len[r]) <= hi - lo, "live length outside the request's region"
+        hi = lo + int(seq_len[r])
+    return lo, hi
+
+
+def kpool_geometry(valid: np.ndarray, tok_off: np.ndarray, kpool: int, seq_len=None):
     """Per request r: the first valid row f_r (request-local; -1 if none) and the
     number of full pools P_r = floor((T_r - f_r) / kpool).  Pooling starts at the
     first valid row, so left padding is skipped; the rows after the last full
@@ -117,7 +129,8 @@ def kpool_geometry(valid: np.ndarray, tok_off: np.ndarray, kpool: int):
     first = np.full(B, -1, dtype=np.int64)
     n_pools = np.zeros(B, dtype=np.int64)
     for r in range(B):
-        v = valid[tok_off[r]:tok_off[r + 1]]
+        lo, hi = request_rows(tok_off, r, seq_len)
+        v = valid[lo:hi]
         nz = np.flatnonzero(v)
         if len(nz):
             first[r] = nz[0]
@@ -137,7 +150,7 @@ def slot_weights(gate_rows: np.ndarray, ape: np.ndarray) -> np.ndarray:
 
 def kpool_compress(k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b, eps, kpool,
                    new_from: Optional[np.ndarray] = None, prev: Optional[dict] = None,
-                   requests: Optional[Iterable[int]] = None) -> dict:
+                   requests: Optional[Iterable[int]] = None, seq_len=None) -> dict:
     """Gated pool compression followed by k_norm.
 
     For request r with first valid row f and P full pools, pool p covers the
@@ -154,7 +167,12 @@ def kpool_compress(k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b, eps, kpoo
     p in [floor((new_from[r] - f)/kpool), P), are recomputed; every other slot
     (sentinels included) is copied from ``prev``.  ``requests`` limits the
     work to some requests (the others are left as they are), for sampled
-    checks at full size."""
+    checks at full size.  ``seq_len`` [B] (optional) is each request's live
+    length (request_rows).
+
+    ln_w = ln_b = None is the per-token k_normed reading: the rows were
+    normalised when they were stored (indexer_store with a LayerNorm), so the
+    pooled value is rounded to bf16 with no LayerNorm after it."""
     k = np.asarray(k)
     gate = np.asarray(gate)
     D = k.shape[1]
@@ -168,10 +186,12 @@ def kpool_compress(k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b, eps, kpoo
         keys = np.zeros((ncap, D), dtype=np.uint16)
         start = np.full(ncap, -1, dtype=np.int32)
         pvalid = np.zeros(ncap, dtype=np.uint8)
-    first, n_pools = kpool_geometry(valid, tok_off, kpool)
+    first, n_pools = kpool_geometry(valid, tok_off, kpool, seq_len)
     ape64 = bf16_bits_to_f64(ape)
-    lw = np.asarray(ln_w, dtype=np.float64)
-    lb = np.asarray(ln_b, dtype=np.float64)
+    post_ln = ln_w is not None
+    if post_ln:
+        lw = np.asarray(ln_w, dtype=np.float64)
+        lb = np.asarray(ln_b, dtype=np.float64)
     reqs = range(B) if requests is None else requests
     for r in reqs:
         cap = int(pool_off[r + 1] - pool_off[r])
@@ -192,14 +212,77 @@ def kpool_compress(k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b, eps, kpoo
         rows = int(tok_off[r]) + f + p[:, None] * kpool + np.arange(kpool)[None, :]
         alpha = slot_weights(bf16_bits_to_f64(gate[rows]), ape64)       # [n, kpool, D]
         x = (alpha * bf16_bits_to_f64(k[rows])).sum(axis=1)           # [n, D]
-        mu = x.mean(axis=1, keepdims=True)
-        var = ((x - mu) ** 2).mean(axis=1, keepdims=True)
-        y = (x - mu) / np.sqrt(var + eps) * lw[None, :] + lb[None, :]
+        if post_ln:
+            mu = x.mean(axis=1, keepdims=True)
+            var = ((x - mu) ** 2).mean(axis=1, keepdims=True)
+            y = (x - mu) / np.sqrt(var + eps) * lw[None, :] + lb[None, :]
+        else:
+            y = x
         keys[base + p_from:base + P] = f64_to_bf16_bits(y)
         start[base + p_from:base + P] = f + p * kpool
         pvalid[base + p_from:base + P] = np.asarray(valid)[rows].astype(bool).all(axis=1)
     return {"keys": keys, "pool_start": start, "pool_valid": pvalid,
             "n_pools": n_pools.astype(np.int32)}
+
+
+# ---------------------------------------------------------------------------
+# the cache-write side  [Atlas DSA page, Glm5NextDsaKernels: indexer_store and
+# write_geom]
+# ---------------------------------------------------------------------------
+
+
+def layer_norm_rows(x, ln_w, ln_b, eps: float) -> np.ndarray:
+    """k_norm of rows (float64): an nn.LayerNorm with a bias, biased variance."""
+    x = np.asarray(x, dtype=np.float64)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * np.asarray(ln_w, np.float64) + np.asarray(ln_b, np.float64)
+
+
+def indexer_store(k, gate, valid, tok_off, pos, k_new, gate_new, ln_w=None, ln_b=None,
+                  eps: float = 1e-5) -> dict:
+    """Place each request's staged indexer row at its device-side position:
+    row tok_off[r] + pos[r] of k and gate receives k_new[r] and gate_new[r],
+    and that row is marked valid.  With ln_w / ln_b (the per-token k_normed
+    reading of the page's k_normed buffer) the stored k row is k_norm of the
+    staged row, rounded once to bf16.  A position outside the request's region
+    (negative, or at or past tok_off[r+1]) stores nothing.  Returns new
+    arrays; the inputs are not modified."""
+    k = np.array(k, copy=True)
+    gate = np.array(gate, copy=True)
+    valid = np.array(valid, copy=True)
+    for r in range(len(tok_off) - 1):
+        p = int(pos[r])
+        if p < 0 or int(tok_off[r]) + p >= int(tok_off[r + 1]):
+            continue
+        row = int(tok_off[r]) + p
+        if ln_w is None:
+            k[row] = k_new[r]
+        else:
+            k[row] = f64_to_bf16_bits(layer_norm_rows(bf16_bits_to_f64(k_new[r]), ln_w, ln_b, eps))
+        gate[row] = gate_new[r]
+        valid[row] = 1
+    return {"k": k, "gate": gate, "valid": valid}
+
+
+def write_geom(seq_len, block_table=None, page_rows: Optional[int] = None) -> dict:
+    """The decode step's geometry from the live lengths, one query per
+    request: q_req[r] = r; q_pos[r] = seq_len[r] - 1 (the newest row; -1 for an
+    empty request, which then has no candidate and no tail); new_from[r] = the
+    row this step writes (max(seq_len[r] - 1, 0)), from which the incremental
+    compression recomputes; slot[r] = the physical latent row of position
+    seq_len[r] - 1 under the block table (paged_rows), -1 for an empty request."""
+    n = np.asarray(seq_len, dtype=np.int64)
+    B = len(n)
+    out = {"q_req": np.arange(B, dtype=np.int32), "q_pos": (n - 1).astype(np.int32),
+           "new_from": np.maximum(n - 1, 0).astype(np.int32)}
+    if block_table is not None:
+        slot = np.full(B, -1, dtype=np.int64)
+        for r in range(B):
+            if n[r] > 0:
+                slot[r] = paged_rows(block_table, page_rows, r, n[r] - 1)
+        out["slot"] = slot
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -407,18 +490,21 @@ def attend_rows(q, ckv, ckv_scale, rows, sm_scale: float,
 
 def dsa_step(x: dict, kpool: int, select_k_: int, out_width_: int, pstride: int,
              eps: float, sm_scale: float, new_from=None, prev=None,
-             queries: Optional[Iterable[int]] = None, always_select_tail: bool = False) -> dict:
+             queries: Optional[Iterable[int]] = None, always_select_tail: bool = False,
+             seq_len=None, post_ln: bool = True) -> dict:
     """One pass of the whole path on the numpy arrays of one input set, in the
     order of the pipeline diagram: head gate, compression, scores, top-k,
     expansion (with the tail when always_select_tail), sparse MLA.
     ``queries`` restricts the per-query stages (and the compression to those
-    queries' requests)."""
+    queries' requests).  ``seq_len``: live lengths (request_rows);
+    ``post_ln=False``: the k rows were normalised when stored, so the
+    compression applies no LayerNorm."""
     qlist = None if queries is None else list(queries)
     reqs = None if qlist is None else sorted({int(x["q_req"][q]) for q in qlist})
     w = head_gate(x["hidden"], x["W"])
     comp = kpool_compress(x["k"], x["gate"], x["ape"], x["valid"], x["tok_off"], x["pool_off"],
-                          x["ln_w"], x["ln_b"], eps, kpool, new_from=new_from, prev=prev,
-                          requests=reqs)
+                          x["ln_w"] if post_ln else None, x["ln_b"] if post_ln else None, eps,
+                          kpool, new_from=new_from, prev=prev, requests=reqs, seq_len=seq_len)
     scores, cand = index_scores(x["qi"], w, comp["keys"], comp["pool_start"], comp["pool_valid"],
                                 x["pool_off"], comp["n_pools"], x["q_req"], x["q_pos"], kpool,
                                 pstride, queries=qlist)

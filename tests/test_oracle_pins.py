@@ -587,3 +587,149 @@ def test_paged_identity_table_is_the_flat_cache():
     paged = O.sparse_mla_decode_paged(q, ckv, None, table, 1, np.array([0, 1]), tok, 1.0)
     assert np.array_equal(paged["out"], flat["out"])
     assert np.array_equal(paged["kvidx"], np.int64([[0, 4, 10, -1], [29, 14, -1, 18]]))
+
+
+# ---- the cache-write side: live lengths, indexer_store, write_geom -----------
+
+def _regions(rng, B=3, cap=(40, 60), D=16):
+    lengths = rng.integers(cap[0], cap[1], size=B)
+    tok_off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    n = int(tok_off[-1])
+    k = bf16(rng.standard_normal((n, D)))
+    gate = bf16(rng.standard_normal((n, D)))
+    valid = (rng.random(n) < 0.97).astype(np.uint8)
+    return lengths, tok_off, k, gate, valid
+
+
+def test_live_length_equals_truncated_region():
+    """Compression over live lengths inside larger regions equals compression
+    of the regions cut to those lengths: rows past a live length (junk,
+    mostly valid) have no influence."""
+    rng = np.random.default_rng(31)
+    for kpool in (1, 3, 4, 8):
+        lengths, tok_off, k, gate, valid = _regions(rng)
+        D = k.shape[1]
+        ape = bf16(rng.standard_normal((kpool, D)))
+        lw, lb = 1 + 0.1 * rng.standard_normal(D), 0.1 * rng.standard_normal(D)
+        seq_len = np.array([int(rng.integers(0, n + 1)) for n in lengths])
+        seq_len[0] = lengths[0]
+        pool_off = np.concatenate([[0], np.cumsum(lengths // kpool)]).astype(np.int64)
+        got = O.kpool_compress(k, gate, ape, valid, tok_off, pool_off, lw, lb, 1e-5, kpool,
+                               seq_len=seq_len)
+        cut = [np.arange(tok_off[r], tok_off[r] + seq_len[r]) for r in range(len(lengths))]
+        idx = np.concatenate(cut)
+        toff2 = np.concatenate([[0], np.cumsum(seq_len)]).astype(np.int64)
+        want = O.kpool_compress(k[idx], gate[idx], ape, valid[idx], toff2, pool_off, lw, lb, 1e-5,
+                                kpool)
+        for name in ("keys", "pool_start", "pool_valid", "n_pools"):
+            assert np.array_equal(got[name], want[name]), (kpool, name)
+
+
+def test_compress_without_layernorm():
+    """The k_normed reading: no LayerNorm after pooling.  kpool 1 stores each
+    row's key as the row itself; a constant gate with no ape gives the slots'
+    mean, rounded once."""
+    rng = np.random.default_rng(32)
+    lengths, tok_off, k, gate, valid = _regions(rng, B=2)
+    valid[:] = 1
+    D = k.shape[1]
+    pool_off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    r1 = O.kpool_compress(k, gate, np.zeros((1, D), np.uint16), valid, tok_off, pool_off, None,
+                          None, 1e-5, 1)
+    assert np.array_equal(r1["keys"], k)
+    g0 = np.zeros_like(gate)
+    pool_off4 = np.concatenate([[0], np.cumsum(lengths // 4)]).astype(np.int64)
+    r4 = O.kpool_compress(k, g0, np.zeros((4, D), np.uint16), valid, tok_off, pool_off4, None,
+                          None, 1e-5, 4)
+    for r in range(2):
+        for p in range(int(r4["n_pools"][r])):
+            rows = tok_off[r] + 4 * p + np.arange(4)
+            mean = O.bf16_bits_to_f64(k[rows]).sum(axis=0) / 4
+            assert np.array_equal(r4["keys"][pool_off4[r] + p], O.f64_to_bf16_bits(mean))
+
+
+def test_indexer_store_places_rows_and_marks_them_valid():
+    rng = np.random.default_rng(33)
+    lengths, tok_off, k, gate, valid = _regions(rng, B=4)
+    D = k.shape[1]
+    valid[:] = 0
+    pos = np.array([0, int(lengths[1]) - 1, int(lengths[2]), -1])   # first, last, past, before
+    k_new, g_new = bf16(rng.standard_normal((4, D))), bf16(rng.standard_normal((4, D)))
+    out = O.indexer_store(k, gate, valid, tok_off, pos, k_new, g_new)
+    written = {int(tok_off[0]): 0, int(tok_off[1]) + int(lengths[1]) - 1: 1}
+    for row in range(len(valid)):
+        if row in written:
+            r = written[row]
+            assert np.array_equal(out["k"][row], k_new[r]) and np.array_equal(out["gate"][row], g_new[r])
+            assert out["valid"][row] == 1
+        else:
+            assert np.array_equal(out["k"][row], k[row]) and out["valid"][row] == 0
+    # with the LayerNorm: torch's layer_norm in float64, rounded by torch to bf16
+    lw, lb = 1 + 0.1 * rng.standard_normal(D), 0.1 * rng.standard_normal(D)
+    out = O.indexer_store(k, gate, valid, tok_off, pos, k_new, g_new, lw, lb, 1e-5)
+    x = torch.from_numpy(k_new.astype(np.int16)).view(torch.bfloat16).to(torch.float64)
+    y = torch.nn.functional.layer_norm(x, (D,), torch.from_numpy(lw), torch.from_numpy(lb), 1e-5)
+    yb = y.to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    assert np.array_equal(out["k"][int(tok_off[0])], yb[0])
+    assert np.array_equal(out["gate"][int(tok_off[0])], g_new[0])
+
+
+def test_k_normed_variant_equals_post_pool_norm_at_kpool_one():
+    """With one slot per pool, normalising each row when it is stored and
+    pooling without a LayerNorm gives the same keys as pooling then
+    normalising."""
+    rng = np.random.default_rng(34)
+    lengths, tok_off, k, gate, valid = _regions(rng, B=2)
+    valid[:] = 1
+    D = k.shape[1]
+    lw, lb = 1 + 0.1 * rng.standard_normal(D), 0.1 * rng.standard_normal(D)
+    pool_off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    ape = np.zeros((1, D), np.uint16)
+    post = O.kpool_compress(k, gate, ape, valid, tok_off, pool_off, lw, lb, 1e-5, 1)
+    kn = k.copy()
+    for r in range(2):
+        for t in range(int(lengths[r])):
+            st = O.indexer_store(kn, gate, valid, tok_off, np.array([t, -1]) if r == 0 else
+                                 np.array([-1, t]), k[[tok_off[r] + t] * 2], gate[[0, 0]], lw, lb,
+                                 1e-5)
+            kn = st["k"]
+    pre = O.kpool_compress(kn, gate, ape, valid, tok_off, pool_off, None, None, 1e-5, 1)
+    assert np.array_equal(pre["keys"], post["keys"])
+
+
+def test_write_geom_worked_example_golden():
+    g = gold("write_geom_worked.json")
+    out = O.write_geom(np.array(g["seq_len"]), np.array(g["block_table"]), g["page_rows"])
+    for name in ("q_req", "q_pos", "new_from", "slot"):
+        assert list(out[name]) == g[name], name
+
+
+def test_decode_steps_over_live_lengths_equal_full_recompression():
+    """A run of decode steps that each store one row at the live length, grow
+    it by one and recompress from the stored row (write_geom's new_from)
+    keeps the pools equal to a full compression at every step."""
+    rng = np.random.default_rng(35)
+    kpool, D, B = 4, 16, 3
+    lengths, tok_off, k, gate, valid = _regions(rng, B=B, cap=(30, 40), D=D)
+    valid[:] = 1
+    valid[tok_off[1]:tok_off[1] + 3] = 0                    # left padding in request 1
+    ape = bf16(rng.standard_normal((kpool, D)))
+    lw, lb = 1 + 0.1 * rng.standard_normal(D), 0.1 * rng.standard_normal(D)
+    pool_off = np.concatenate([[0], np.cumsum(lengths // kpool)]).astype(np.int64)
+    seq_len = np.array([5, 0, 9])
+    state = O.kpool_compress(k, gate, ape, valid, tok_off, pool_off, lw, lb, 1e-5, kpool,
+                             seq_len=seq_len)
+    for step in range(14):
+        pos = seq_len.copy()
+        st = O.indexer_store(k, gate, valid, tok_off, pos, bf16(rng.standard_normal((B, D))),
+                             bf16(rng.standard_normal((B, D))))
+        k, gate, valid = st["k"], st["gate"], st["valid"]
+        seq_len = seq_len + 1
+        geo = O.write_geom(seq_len)
+        assert np.array_equal(geo["new_from"], pos)
+        state = O.kpool_compress(k, gate, ape, valid, tok_off, pool_off, lw, lb, 1e-5, kpool,
+                                 new_from=geo["new_from"], prev=state, seq_len=seq_len)
+        full = O.kpool_compress(k, gate, ape, valid, tok_off, pool_off, lw, lb, 1e-5, kpool,
+                                seq_len=seq_len)
+        for name in ("keys", "pool_start", "pool_valid", "n_pools"):
+            assert np.array_equal(state[name], full[name]), (step, name)
