@@ -13,7 +13,9 @@ every step streams its keys and latent rows from HBM.  Each set's calls are
 captured once in a HIP graph; the timed region replays K graphs.  The same
 step through the six separate calls is timed too, for comparison, and the
 step with the attention reading a paged copy of the latent cache (64-row pages
-in shuffled order, through a block table).
+in shuffled order, through a block table), and the whole decode step from
+device-side live lengths (geometry, the store of the step's indexer row, the
+fused calls, the paged attention).
 
 The JSON line also carries, for the call that takes the most time, its
 algorithmic bytes per launch over its average launch time (a graph of 32
@@ -240,6 +242,23 @@ def main():
                  "table_cols": int(steps[0].pc.block_table.shape[1]),
                  "step_us": round(ms_p / max(1, a.steps // 4) * 1e3, 2)}
         del graphs_p
+    # the whole decode step from device-side live lengths: geometry, the store
+    # of the step's indexer row, the fused step, the attention (paged when
+    # timed above)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    for st in steps:
+        st.seq_len = torch.tensor(spec.live_lengths(), dtype=torch.int32, device=dev)
+        st.k_new = torch.randn(spec.B, spec.index_dim, generator=gen, device=dev) \
+            .to(torch.bfloat16).view(torch.int16)
+        st.gate_new = torch.randn(spec.B, spec.index_dim, generator=gen, device=dev) \
+            .to(torch.bfloat16).view(torch.int16)
+        st.slot = torch.empty(spec.B, dtype=torch.int32, device=dev)
+    graphs_l = capture(lambda st: st.run_live(st.k_new, st.gate_new, paged=getattr(st, "pc", None),
+                                              slot=st.slot if paged is not None else None))
+    ms_l, _ = timed(graphs_l, max(1, a.steps // 4), max(1, a.warmup // 4))
+    live = {"step_us": round(ms_l / max(1, a.steps // 4) * 1e3, 2)}
+    del graphs_l
 
     # -- per-call launch times: a graph of kCallsPerGraph back-to-back calls of
     # one kind (the input sets in rotation), replayed between HIP events on the
@@ -272,6 +291,9 @@ def main():
     }
     if paged is not None:
         fns["sparse_mla_decode_paged"] = lambda s: s.mla_paged(s.pc)
+    fns["write_geom"] = lambda s: s.write_geom(getattr(s, "pc", None),
+                                               s.slot if paged is not None else None)
+    fns["indexer_store"] = lambda s: s.store(s.k_new, s.gate_new)
     call_us = {}
     reps = max(1, a.stage_reps // kCallsPerGraph)
     for name, fn in fns.items():
@@ -282,6 +304,8 @@ def main():
     stage_us = {k: call_us[k] for k in STAGES}
     if paged is not None:
         paged["mla_us"] = round(call_us["sparse_mla_decode_paged"], 2)
+    live["write_geom_us"] = round(call_us["write_geom"], 2)
+    live["indexer_store_us"] = round(call_us["indexer_store"], 2)
 
     xn0 = {"q_req": sets[0].q_req.cpu().numpy()}
     nb = algorithmic_bytes(spec, xn0, steps[0].n_pools.cpu().numpy(), steps[0].tok.cpu().numpy())
@@ -328,6 +352,7 @@ def main():
         "six_call_step_us": round(six_us, 2),
         "call_us": {k: round(call_us[k], 2) for k in CALLS},
         "paged": paged,
+        "live_step": live,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 typedef int dsa_status;
 #define DSA_OK 0
@@ -107,9 +107,16 @@ dsa_status dsa_head_gate(const float* hidden, const float* W, float* w, int M, i
  *   n_pools[r] = P_r.
  * Left padding is skipped, and a trailing partial pool is not a pool.
  *
+ * T_r is the region's size tok_off[r+1] - tok_off[r], or, when seq_len [B]
+ * i32 is given, the live length seq_len[r] (clamped to [0, region]): a
+ * request's region may hold more rows than it has written (rows past the live
+ * length are not read).  ln_w = ln_b = NULL: the k rows were normalised when
+ * stored (dsa_indexer_store with a LayerNorm, the per-token k_normed form) and
+ * keys[p] = bf16_rne(x), with no LayerNorm.
+ *
  * k, gate [sumT, D] bf16; ape [kpool, D] bf16; valid [sumT] u8 (0/1);
  * tok_off [B+1] i32; pool_off [B+1] i32 with cap_r >= floor(T_r / kpool);
- * ln_w, ln_b [D] f32; keys [sum cap, D] bf16; pool_start [sum cap] i32;
+ * ln_w, ln_b [D] f32 (or both NULL); keys [sum cap, D] bf16; pool_start [sum cap] i32;
  * pool_valid [sum cap] u8; n_pools [B] i32.  max_cap >= every cap_r (host
  * bound that sizes the grid).
  *
@@ -123,12 +130,13 @@ dsa_status dsa_head_gate(const float* hidden, const float* W, float* w, int M, i
  * request, when it holds a pool starting before new_from[r], supplies f_r.
  * new_from = NULL recomputes every slot.
  * Errors: INVALID_ARG for kpool outside [1, 8] (never truncated), B < 0, NULL
- * pointers, max_cap < 0, max_new < 1 with new_from; UNSUPPORTED for D not in
- * {32, 64, 128, 256}.
+ * pointers, exactly one of ln_w / ln_b NULL, max_cap < 0, max_new < 1 with
+ * new_from; UNSUPPORTED for D not in {32, 64, 128, 256}.
  * ------------------------------------------------------------------------- */
 dsa_status dsa_kpool_compress(const uint16_t* k, const uint16_t* gate, const uint16_t* ape,
                               const uint8_t* valid, const int32_t* tok_off, const int32_t* pool_off,
-                              const float* ln_w, const float* ln_b, float eps, int B, int D,
+                              const int32_t* seq_len, const float* ln_w, const float* ln_b,
+                              float eps, int B, int D,
                               int kpool, int max_cap, const int32_t* new_from, int max_new,
                               uint16_t* keys, int32_t* pool_start, uint8_t* pool_valid,
                               int32_t* n_pools, hipStream_t stream);
@@ -281,6 +289,44 @@ dsa_status dsa_sparse_mla_decode_paged(const uint16_t* q, const void* ckv, const
                                        hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * The cache-write side of a decode step   [Atlas page, Glm5NextDsaKernels:
+ *     write_geom (the step's selector geometry derived on the device from
+ *     seq_len, so a captured graph replays over the live context) and
+ *     indexer_store (the staged indexer row placed at a device-side position
+ *     and marked valid; the page's per-token k_normed row)]
+ *
+ * dsa_write_geom: one decode query per request, from the live lengths
+ * seq_len [B] i32 (a negative length counts as 0):
+ *   q_req[r] = r;  q_pos[r] = seq_len[r] - 1 (-1 for an empty request: no
+ *   candidate pool and no tail);  new_from[r] = max(seq_len[r] - 1, 0) (the
+ *   row the step writes, where dsa_kpool_compress's incremental mode starts);
+ *   slot[r] = the physical latent row of position seq_len[r] - 1 under the
+ *   block table, as dsa_sparse_mla_decode_paged maps it (-1 when empty).
+ * q_req, new_from and slot may be NULL (not written); slot needs block_table
+ * [B, bt_stride], page_rows and n_pages as in dsa_sparse_mla_decode_paged.
+ * Errors: INVALID_ARG for B < 0, NULL seq_len / q_pos, slot without a valid
+ * table geometry.
+ *
+ * dsa_indexer_store: for each request r with 0 <= pos[r] < tok_off[r+1] -
+ * tok_off[r], row tok_off[r] + pos[r] of k and gate receives k_new[r] and
+ * gate_new[r], and valid of that row becomes 1; other positions store nothing.
+ * With ln_w / ln_b the stored k row is k_norm of the staged row (LayerNorm
+ * with bias, biased variance, eps), rounded once to bf16; use then
+ * dsa_kpool_compress without ln_w / ln_b.  k_new, gate_new [B, D] bf16; pos
+ * [B] i32 (for a decode step, dsa_write_geom's new_from); tok_off [B+1] i32;
+ * ln_w, ln_b [D] f32 or both NULL; k, gate [rows, D] bf16, valid [rows] u8.
+ * Errors: INVALID_ARG for B < 0, NULL pointers, exactly one of ln_w / ln_b
+ * NULL, eps < 0; UNSUPPORTED for D not in {32, 64, 128, 256}.
+ * ------------------------------------------------------------------------- */
+dsa_status dsa_write_geom(const int32_t* seq_len, int B, const int32_t* block_table, int bt_stride,
+                          int page_rows, int n_pages, int32_t* q_req, int32_t* q_pos,
+                          int32_t* new_from, int32_t* slot, hipStream_t stream);
+dsa_status dsa_indexer_store(const uint16_t* k_new, const uint16_t* gate_new, const int32_t* pos,
+                             const int32_t* tok_off, const float* ln_w, const float* ln_b,
+                             float eps, int B, int D, uint16_t* k, uint16_t* gate,
+                             uint8_t* valid, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Fused decode calls   [stkernel pull request #290 measures what each launch
  *     of a serving step costs; the Atlas page's pipeline order is kept]
  *
@@ -324,7 +370,8 @@ size_t dsa_gate_compress_workspace_size(int M, int K, int N);
 dsa_status dsa_gate_compress(const float* hidden, const float* W, int M, int K, int N,
                              float* gate_part, size_t gate_part_bytes, const uint16_t* k,
                              const uint16_t* gate, const uint16_t* ape, const uint8_t* valid,
-                             const int32_t* tok_off, const int32_t* pool_off, const float* ln_w,
+                             const int32_t* tok_off, const int32_t* pool_off,
+                             const int32_t* seq_len, const float* ln_w,
                              const float* ln_b, float eps, int B, int D, int kpool, int max_cap,
                              const int32_t* new_from, int max_new, uint16_t* keys,
                              int32_t* pool_start, uint8_t* pool_valid, int32_t* n_pools,

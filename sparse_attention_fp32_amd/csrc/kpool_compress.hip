@@ -21,6 +21,11 @@
 // its newest row completes a pool).  The first valid row comes from slot 0 of
 // the earlier call whenever that slot holds a pool starting before new_from.
 //
+// Live lengths: with seq_len, request r holds seq_len[r] rows of its region
+// (the rest of the region is not read).  Without ln_w / ln_b the rows were
+// normalised when stored (per-token k_normed) and the pooled row is rounded to
+// bf16 with no LayerNorm.
+//
 // Fused decode variant (dsa_gate_compress): the head-gate of the same step is
 // independent of the compression, so the same launch also runs it, split over
 // K (stkernel PR #227's split-K) in workgroups placed after the compression
@@ -62,6 +67,10 @@ __device__ int first_valid_row(const uint8_t* __restrict__ valid, int64_t row0, 
   const int f = *s_first;
   return f == INT_MAX ? -1 : f;
 }
+
+// Read in place of ln_w / ln_b when there is no LayerNorm (values unused;
+// global, not constant, memory, so the loads stay plain global loads).
+__device__ float kNoLn[256];
 
 constexpr int kGateSlice = 128;  // K per gate partial
 constexpr int kGateRows = 16;    // gate rows per partial workgroup
@@ -129,7 +138,8 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ gate,
     const uint16_t* __restrict__ ape, const uint8_t* __restrict__ valid,
     const int32_t* __restrict__ tok_off, const int32_t* __restrict__ pool_off,
-    const float* __restrict__ ln_w, const float* __restrict__ ln_b, float eps,
+    const int32_t* __restrict__ live_len, int has_live, const float* __restrict__ ln_w,
+    const float* __restrict__ ln_b, float eps,
     const int32_t* __restrict__ new_from, int pools_per_wg, int spec_pools,
     uint16_t* __restrict__ keys,
     int32_t* __restrict__ pool_start, uint8_t* __restrict__ pool_valid,
@@ -149,16 +159,26 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
   const int grp = t / LPP;    // pool group within the workgroup
   const int c0 = li * 8;      // first channel of this lane
   // Loads that need no geometry go out with the geometry itself.
-  const int64_t row0 = tok_off[r];
-  const int T = tok_off[r + 1] - (int)row0;
-  const int64_t pbase = pool_off[r];
-  const int cap = pool_off[r + 1] - (int)pbase;
-  const int nf = new_from ? new_from[r] : 0;
+  // the geometry loads, issued together (the empty asm keeps the compiler
+  // from moving the live-length load into a branch of its own)
+  int g_lo = tok_off[r], g_hi = tok_off[r + 1], g_pb = pool_off[r], g_pe = pool_off[r + 1];
+  int live = live_len[r];  // (tok_off when there are no live lengths)
+  int g_nf = *(new_from ? new_from + r : tok_off + r);
+  asm volatile("" : "+s"(g_lo), "+s"(g_hi), "+s"(g_pb), "+s"(g_pe), "+s"(live), "+s"(g_nf));
+  const int64_t row0 = g_lo;
+  const int region = g_hi - g_lo;
+  const int T = has_live ? min(max(live, 0), region) : region;
+  const int64_t pbase = g_pb;
+  const int cap = g_pe - g_pb;
+  const int nf = new_from ? g_nf : 0;
+  const bool post_ln = ln_w != nullptr;
+  const float* lwp = post_ln ? ln_w : kNoLn;
+  const float* lbp = post_ln ? ln_b : kNoLn;
   float lw[8], lb[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    lw[c] = ln_w[c0 + c];
-    lb[c] = ln_b[c0 + c];
+    lw[c] = lwp[c0 + c];
+    lb[c] = lbp[c0 + c];
   }
   uint4 ap[KP];
 #pragma unroll
@@ -188,6 +208,11 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
       }
       x[c] = acc / z;
     }
+    uint32_t packed[4];
+    if (!post_ln) {
+#pragma unroll
+      for (int c = 0; c < 8; c += 2) packed[c >> 1] = pack_bf16x2(x[c], x[c + 1]);
+    } else {
     float sum = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) sum += x[c];
@@ -201,12 +226,12 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
     }
     sq = group_sum<LPP>(sq);
     const float rstd = 1.0f / sqrtf(sq / (float)D + eps);
-    uint32_t packed[4];
 #pragma unroll
     for (int c = 0; c < 8; c += 2) {
       const float y0 = (x[c] - mean) * rstd * lw[c] + lb[c];
       const float y1 = (x[c + 1] - mean) * rstd * lw[c + 1] + lb[c + 1];
       packed[c >> 1] = pack_bf16x2(y0, y1);
+    }
     }
     *(uint4*)(keys + (pbase + p) * D + c0) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
     if (li == 0) {
@@ -268,9 +293,9 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
   const bool spec = i0 < spec_pools && T >= kpool * (i0 + 1);
   const int64_t srs = spec ? row0 + T - (int64_t)kpool * (i0 + 1) : 0;
   uint4 skr[KP], sgr[KP];
-  // (with no such rows the loads read ln_w, which is at least a row long)
-  const int sallv = load_rows(spec ? k : (const uint16_t*)ln_w, spec ? gate : (const uint16_t*)ln_w,
-                              spec ? valid : (const uint8_t*)ln_w, srs, skr, sgr);
+  // (with no such rows the loads read ape's kpool rows)
+  const int sallv = load_rows(spec ? k : ape, spec ? gate : ape,
+                              spec ? valid : (const uint8_t*)ape, srs, skr, sgr);
   const int fc = *(cap > 0 ? pool_start + pbase : new_from + r);  // (unused when cap == 0)
   const bool cached = cap > 0 && fc >= 0 && fc < nf;
   const int f = cached ? fc : first_valid_row(valid, row0, T, &s_first);
@@ -297,7 +322,7 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
 namespace {
 
 dsa_status check_compress_args(int B, int D, int kpool, int max_cap, const int32_t* new_from,
-                               int max_new, float eps) {
+                               int max_new, float eps, const float* ln_w, const float* ln_b) {
   DSA_REQUIRE(kpool >= 1 && kpool <= DSA_MAX_KPOOL, DSA_ERR_INVALID_ARG,
               "dsa_kpool_compress: kpool=%d outside [1,%d] (larger pools are refused, never "
               "truncated)",
@@ -309,13 +334,15 @@ dsa_status check_compress_args(int B, int D, int kpool, int max_cap, const int32
   DSA_REQUIRE(!new_from || max_new >= 1, DSA_ERR_INVALID_ARG,
               "dsa_kpool_compress: max_new=%d < 1 with new_from", max_new);
   DSA_REQUIRE(eps >= 0.f, DSA_ERR_INVALID_ARG, "dsa_kpool_compress: eps < 0");
+  DSA_REQUIRE((ln_w == nullptr) == (ln_b == nullptr), DSA_ERR_INVALID_ARG,
+              "dsa_kpool_compress: ln_w and ln_b must both be given or both be NULL");
   return DSA_OK;
 }
 
 // One launch: B rows of compression workgroups, then ga.nwg gate workgroups.
 dsa_status launch_compress(const uint16_t* k, const uint16_t* gate, const uint16_t* ape,
                            const uint8_t* valid, const int32_t* tok_off, const int32_t* pool_off,
-                           const float* ln_w, const float* ln_b, float eps, int B, int D,
+                           const int32_t* seq_len, const float* ln_w, const float* ln_b, float eps, int B, int D,
                            int kpool, int max_cap, const int32_t* new_from, int max_new,
                            uint16_t* keys, int32_t* pool_start, uint8_t* pool_valid,
                            int32_t* n_pools, const GateArgs& ga, hipStream_t stream,
@@ -341,8 +368,9 @@ dsa_status launch_compress(const uint16_t* k, const uint16_t* gate, const uint16
             D, kpool, max_cap, new_from != nullptr, ga.nwg, grid.x, grid.y);
 #define DSA_LAUNCH_KP(LPP, KP)                                                                 \
   kpool_compress_kernel<LPP, KP><<<grid, 256, 0, stream>>>(                                     \
-      k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b, eps, new_from, ppw, spec, keys, pool_start, \
-      pool_valid, n_pools, B, ga)
+      k, gate, ape, valid, tok_off, pool_off, seq_len ? seq_len : tok_off, seq_len != nullptr, ln_w, \
+      ln_b, eps, new_from, ppw, spec, keys, \
+      pool_start, pool_valid, n_pools, B, ga)
 #define DSA_LAUNCH_KP_D(KP)            \
   switch (lpp) {                       \
     case 4: DSA_LAUNCH_KP(4, KP); break;   \
@@ -378,20 +406,22 @@ int gate_slices(int M, int K) {
 DSA_EXPORT dsa_status dsa_kpool_compress(const uint16_t* k, const uint16_t* gate,
                                          const uint16_t* ape, const uint8_t* valid,
                                          const int32_t* tok_off, const int32_t* pool_off,
-                                         const float* ln_w, const float* ln_b, float eps, int B,
-                                         int D, int kpool, int max_cap, const int32_t* new_from,
-                                         int max_new, uint16_t* keys, int32_t* pool_start,
+                                         const int32_t* seq_len, const float* ln_w,
+                                         const float* ln_b, float eps, int B, int D, int kpool,
+                                         int max_cap, const int32_t* new_from, int max_new,
+                                         uint16_t* keys, int32_t* pool_start,
                                          uint8_t* pool_valid, int32_t* n_pools,
                                          hipStream_t stream) {
-  const dsa_status st = check_compress_args(B, D, kpool, max_cap, new_from, max_new, eps);
+  const dsa_status st =
+      check_compress_args(B, D, kpool, max_cap, new_from, max_new, eps, ln_w, ln_b);
   if (st != DSA_OK) return st;
   if (B == 0) return DSA_OK;
-  DSA_REQUIRE(k && gate && ape && valid && tok_off && pool_off && ln_w && ln_b && keys &&
-                  pool_start && pool_valid && n_pools,
+  DSA_REQUIRE(k && gate && ape && valid && tok_off && pool_off && keys && pool_start &&
+                  pool_valid && n_pools,
               DSA_ERR_INVALID_ARG, "dsa_kpool_compress: NULL tensor pointer");
-  return launch_compress(k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b, eps, B, D, kpool,
-                         max_cap, new_from, max_new, keys, pool_start, pool_valid, n_pools,
-                         GateArgs{}, stream, "dsa_kpool_compress");
+  return launch_compress(k, gate, ape, valid, tok_off, pool_off, seq_len, ln_w, ln_b, eps, B, D,
+                         kpool, max_cap, new_from, max_new, keys, pool_start, pool_valid,
+                         n_pools, GateArgs{}, stream, "dsa_kpool_compress");
 }
 
 DSA_EXPORT int dsa_gate_split_count(int M, int K, int N) {
@@ -410,38 +440,40 @@ DSA_EXPORT dsa_status dsa_gate_compress(const float* hidden, const float* W, int
                                         const uint16_t* k, const uint16_t* gate,
                                         const uint16_t* ape, const uint8_t* valid,
                                         const int32_t* tok_off, const int32_t* pool_off,
-                                        const float* ln_w, const float* ln_b, float eps, int B,
-                                        int D, int kpool, int max_cap, const int32_t* new_from,
-                                        int max_new, uint16_t* keys, int32_t* pool_start,
+                                        const int32_t* seq_len, const float* ln_w,
+                                        const float* ln_b, float eps, int B, int D, int kpool,
+                                        int max_cap, const int32_t* new_from, int max_new,
+                                        uint16_t* keys, int32_t* pool_start,
                                         uint8_t* pool_valid, int32_t* n_pools,
                                         hipStream_t stream) {
   DSA_REQUIRE(N >= 1 && N <= DSA_MAX_INDEX_HEADS, DSA_ERR_INVALID_ARG,
               "dsa_gate_compress: N=%d outside [1,%d]", N, DSA_MAX_INDEX_HEADS);
   DSA_REQUIRE(M >= 0 && K >= 1, DSA_ERR_INVALID_ARG, "dsa_gate_compress: M=%d K=%d", M, K);
-  const dsa_status st = check_compress_args(B, D, kpool, max_cap, new_from, max_new, eps);
+  const dsa_status st =
+      check_compress_args(B, D, kpool, max_cap, new_from, max_new, eps, ln_w, ln_b);
   if (st != DSA_OK) return st;
   const size_t need = dsa_gate_compress_workspace_size(M, K, N);
   DSA_REQUIRE(M == 0 || (gate_part && gate_part_bytes >= need), DSA_ERR_INVALID_ARG,
               "dsa_gate_compress: gate partials %zu bytes, need %zu", gate_part_bytes, need);
   DSA_REQUIRE(M == 0 || (hidden && W), DSA_ERR_INVALID_ARG,
               "dsa_gate_compress: NULL tensor pointer");
-  DSA_REQUIRE(B == 0 || (k && gate && ape && valid && tok_off && pool_off && ln_w && ln_b &&
-                         keys && pool_start && pool_valid && n_pools),
+  DSA_REQUIRE(B == 0 || (k && gate && ape && valid && tok_off && pool_off && keys &&
+                         pool_start && pool_valid && n_pools),
               DSA_ERR_INVALID_ARG, "dsa_gate_compress: NULL tensor pointer");
   const int ns = gate_slices(M, K);
   if (M > 0 && ns == 1) {  // dense head-gate: the partials buffer receives w
     const dsa_status g = dsa_head_gate(hidden, W, gate_part, M, K, N, nullptr, 0, stream);
     if (g != DSA_OK) return g;
     if (B == 0) return DSA_OK;
-    return launch_compress(k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b, eps, B, D, kpool,
-                           max_cap, new_from, max_new, keys, pool_start, pool_valid, n_pools,
-                           GateArgs{}, stream, "dsa_gate_compress");
+    return launch_compress(k, gate, ape, valid, tok_off, pool_off, seq_len, ln_w, ln_b, eps, B,
+                           D, kpool, max_cap, new_from, max_new, keys, pool_start, pool_valid,
+                           n_pools, GateArgs{}, stream, "dsa_gate_compress");
   }
   GateArgs ga{hidden, W, gate_part, M, K, N, ns, M > 0 ? ns * ((M + kGateRows - 1) / kGateRows) : 0};
   if (B == 0 && ga.nwg == 0) return DSA_OK;
   // with B == 0 the launch holds only gate workgroups (its compression
   // arguments are never read)
-  return launch_compress(k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b, eps, B, D, kpool,
-                         max_cap, new_from, max_new, keys, pool_start, pool_valid, n_pools, ga,
-                         stream, "dsa_gate_compress");
+  return launch_compress(k, gate, ape, valid, tok_off, pool_off, seq_len, ln_w, ln_b, eps, B, D,
+                         kpool, max_cap, new_from, max_new, keys, pool_start, pool_valid,
+                         n_pools, ga, stream, "dsa_gate_compress");
 }

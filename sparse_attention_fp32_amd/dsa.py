@@ -35,8 +35,8 @@ _SIGS = {
     "dsa_last_error": (ctypes.c_char_p, []),
     "dsa_head_gate_workspace_size": (_Z, [_I, _I, _I]),
     "dsa_head_gate": (_I, [_P, _P, _P, _I, _I, _I, _P, _Z, _P]),
-    "dsa_kpool_compress": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _F, _I, _I, _I, _I, _P, _I,
-                                _P, _P, _P, _P, _P]),
+    "dsa_kpool_compress": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _F, _I, _I, _I, _I, _P,
+                                _I, _P, _P, _P, _P, _P]),
     "dsa_index_scores": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
     "dsa_topk_pools_workspace_size": (_Z, [_I, _I, _I]),
     "dsa_topk_pools": (_I, [_P, _P, _I, _I, _I, _P, _P, _Z, _P]),
@@ -48,8 +48,10 @@ _SIGS = {
                                          _F, _P, _P, _P, _P, _Z, _P]),
     "dsa_gate_split_count": (_I, [_I, _I, _I]),
     "dsa_gate_compress_workspace_size": (_Z, [_I, _I, _I]),
-    "dsa_gate_compress": (_I, [_P, _P, _I, _I, _I, _P, _Z, _P, _P, _P, _P, _P, _P, _P, _P, _F,
-                               _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P]),
+    "dsa_gate_compress": (_I, [_P, _P, _I, _I, _I, _P, _Z, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                               _F, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P]),
+    "dsa_write_geom": (_I, [_P, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P]),
+    "dsa_indexer_store": (_I, [_P, _P, _P, _P, _P, _P, _F, _I, _I, _P, _P, _P, _P]),
     "dsa_index_scores_gated": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                                     _I, _P, _P, _P]),
     "dsa_topk_expand": (_I, [_P, _P, _I, _I, _I, _P, _P, _P, _I, _I, _I, _P, _P, _P]),
@@ -157,13 +159,17 @@ def dsa_head_gate(hidden, W, w, ws=None, stream=None) -> None:
 
 def dsa_kpool_compress(k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b, eps: float, kpool: int,
                        max_cap: int, keys, pool_start, pool_valid, n_pools, new_from=None,
-                       max_new: int = 0, stream=None) -> None:
+                       max_new: int = 0, seq_len=None, stream=None) -> None:
+    """ln_w = ln_b = None: rows normalised when stored (no LayerNorm here);
+    seq_len: live lengths [B] i32 (None: the whole regions)."""
     B = tok_off.numel() - 1
     D = k.shape[1]
     _check(lib().dsa_kpool_compress(
         _dev(k, _BF, "k"), _dev(gate, _BF, "gate"), _dev(ape, _BF, "ape"), _dev(valid, _U8, "valid"),
         _dev(tok_off, _I32, "tok_off"), _dev(pool_off, _I32, "pool_off"),
-        _dev(ln_w, torch.float32, "ln_w"), _dev(ln_b, torch.float32, "ln_b"), float(eps), B, D,
+        _dev(seq_len, _I32, "seq_len", allow_none=True),
+        _dev(ln_w, torch.float32, "ln_w", allow_none=True),
+        _dev(ln_b, torch.float32, "ln_b", allow_none=True), float(eps), B, D,
         kpool, max_cap, _dev(new_from, _I32, "new_from", allow_none=True), int(max_new),
         _dev(keys, _BF, "keys"), _dev(pool_start, _I32, "pool_start"),
         _dev(pool_valid, _U8, "pool_valid"), _dev(n_pools, _I32, "n_pools"), _stream(stream)))
@@ -250,7 +256,7 @@ def gate_compress_workspace_size(M: int, K: int, N: int) -> int:
 
 def dsa_gate_compress(hidden, W, gate_part, k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b,
                       eps: float, kpool: int, max_cap: int, keys, pool_start, pool_valid, n_pools,
-                      new_from=None, max_new: int = 0, stream=None) -> None:
+                      new_from=None, max_new: int = 0, seq_len=None, stream=None) -> None:
     M, K = hidden.shape
     N = W.shape[1]
     B = tok_off.numel() - 1
@@ -262,10 +268,35 @@ def dsa_gate_compress(hidden, W, gate_part, k, gate, ape, valid, tok_off, pool_o
         _dev(hidden, torch.float32, "hidden"), _dev(W, torch.float32, "W"), M, K, N, gp, gb,
         _dev(k, _BF, "k"), _dev(gate, _BF, "gate"), _dev(ape, _BF, "ape"), _dev(valid, _U8, "valid"),
         _dev(tok_off, _I32, "tok_off"), _dev(pool_off, _I32, "pool_off"),
-        _dev(ln_w, torch.float32, "ln_w"), _dev(ln_b, torch.float32, "ln_b"), float(eps), B, D,
+        _dev(seq_len, _I32, "seq_len", allow_none=True),
+        _dev(ln_w, torch.float32, "ln_w", allow_none=True),
+        _dev(ln_b, torch.float32, "ln_b", allow_none=True), float(eps), B, D,
         kpool, max_cap, _dev(new_from, _I32, "new_from", allow_none=True), int(max_new),
         _dev(keys, _BF, "keys"), _dev(pool_start, _I32, "pool_start"),
         _dev(pool_valid, _U8, "pool_valid"), _dev(n_pools, _I32, "n_pools"), _stream(stream)))
+
+
+# --- the cache-write side --------------------------------------------------
+
+def dsa_write_geom(seq_len, q_pos, q_req=None, new_from=None, slot=None, block_table=None,
+                   page_rows: int = 0, n_pages: int = 0, stream=None) -> None:
+    B = seq_len.numel()
+    bt_stride = block_table.shape[1] if block_table is not None else 0
+    _check(lib().dsa_write_geom(
+        _dev(seq_len, _I32, "seq_len"), B, _dev(block_table, _I32, "block_table", allow_none=True),
+        bt_stride, int(page_rows), int(n_pages), _dev(q_req, _I32, "q_req", allow_none=True),
+        _dev(q_pos, _I32, "q_pos"), _dev(new_from, _I32, "new_from", allow_none=True),
+        _dev(slot, _I32, "slot", allow_none=True), _stream(stream)))
+
+
+def dsa_indexer_store(k_new, gate_new, pos, tok_off, k, gate, valid, ln_w=None, ln_b=None,
+                      eps: float = 1e-5, stream=None) -> None:
+    B, D = k_new.shape
+    _check(lib().dsa_indexer_store(
+        _dev(k_new, _BF, "k_new"), _dev(gate_new, _BF, "gate_new"), _dev(pos, _I32, "pos"),
+        _dev(tok_off, _I32, "tok_off"), _dev(ln_w, torch.float32, "ln_w", allow_none=True),
+        _dev(ln_b, torch.float32, "ln_b", allow_none=True), float(eps), B, D, _dev(k, _BF, "k"),
+        _dev(gate, _BF, "gate"), _dev(valid, _U8, "valid"), _stream(stream)))
 
 
 def dsa_index_scores_gated(qi, gate_part, nslices: int, w, keys, pool_start, pool_valid, pool_off,

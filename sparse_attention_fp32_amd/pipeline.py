@@ -14,13 +14,19 @@ class DsaStep:
 
     ``run(incremental=True)`` is a decode step over cached pools: the pools
     that hold the newest row of each request are recompressed and every other
-    stage runs in full."""
+    stage runs in full.
+
+    ``seq_len`` (a [B] i32 device tensor, or None) gives live lengths inside
+    the requests' regions; ``post_ln=False`` compresses rows that were
+    normalised when stored (no LayerNorm after pooling)."""
 
     def __init__(self, x: Inputs, stream=None):
         s = x.spec
         dev = x.k.device
         assert dev.type == "cuda", "DsaStep needs inputs resident on the GPU"
         self.x, self.spec, self.stream = x, s, stream
+        self.seq_len = None
+        self.post_ln = True
         Q, B, H, D = s.Q, s.B, s.index_heads, s.index_dim
         ncap = int(sum(s.pool_caps()))
         self.max_cap = max(s.pool_caps()) if s.B else 0
@@ -53,11 +59,13 @@ class DsaStep:
 
     def compress(self, incremental: bool = False):
         x = self.x
-        dsa.dsa_kpool_compress(x.k, x.gate, x.ape, x.valid, x.tok_off, x.pool_off, x.ln_w, x.ln_b,
+        lw, lb = (x.ln_w, x.ln_b) if self.post_ln else (None, None)
+        dsa.dsa_kpool_compress(x.k, x.gate, x.ape, x.valid, x.tok_off, x.pool_off, lw, lb,
                                self.spec.eps, self.spec.kpool, self.max_cap, self.keys,
                                self.pool_start, self.pool_valid, self.n_pools,
                                new_from=x.new_from if incremental else None,
-                               max_new=1 if incremental else 0, stream=self.stream)
+                               max_new=1 if incremental else 0, seq_len=self.seq_len,
+                               stream=self.stream)
 
     def index_scores(self):
         x = self.x
@@ -102,11 +110,13 @@ class DsaStep:
     # -- fused decode calls (same outputs, fewer launches) ---------------------
     def gate_compress(self, incremental: bool = False):
         x = self.x
+        lw, lb = (x.ln_w, x.ln_b) if self.post_ln else (None, None)
         dsa.dsa_gate_compress(x.hidden, x.W, self.gate_part, x.k, x.gate, x.ape, x.valid, x.tok_off,
-                              x.pool_off, x.ln_w, x.ln_b, self.spec.eps, self.spec.kpool,
+                              x.pool_off, lw, lb, self.spec.eps, self.spec.kpool,
                               self.max_cap, self.keys, self.pool_start, self.pool_valid,
                               self.n_pools, new_from=x.new_from if incremental else None,
-                              max_new=1 if incremental else 0, stream=self.stream)
+                              max_new=1 if incremental else 0, seq_len=self.seq_len,
+                              stream=self.stream)
 
     def index_scores_gated(self):
         x = self.x
@@ -130,6 +140,32 @@ class DsaStep:
             self.mla()
         else:
             self.mla_paged(paged)
+
+    # -- the cache-write side of a decode step --------------------------------
+    def write_geom(self, paged=None, slot=None):
+        """q_req, q_pos and new_from of the inputs (one query per request)
+        from self.seq_len; with a paged cache and a slot buffer, the physical
+        row of each request's newest position."""
+        x = self.x
+        dsa.dsa_write_geom(self.seq_len, x.q_pos, q_req=x.q_req, new_from=x.new_from, slot=slot,
+                           block_table=None if paged is None else paged.block_table,
+                           page_rows=0 if paged is None else paged.page_rows,
+                           n_pages=0 if paged is None else paged.n_pages, stream=self.stream)
+
+    def store(self, k_new, gate_new):
+        """The step's staged indexer rows at new_from (normalised when
+        post_ln is False)."""
+        x = self.x
+        lw, lb = (None, None) if self.post_ln else (x.ln_w, x.ln_b)
+        dsa.dsa_indexer_store(k_new, gate_new, x.new_from, x.tok_off, x.k, x.gate, x.valid,
+                              ln_w=lw, ln_b=lb, eps=self.spec.eps, stream=self.stream)
+
+    def run_live(self, k_new, gate_new, paged=None, slot=None):
+        """A whole decode step from the live lengths: geometry, the row store,
+        then the fused step over cached pools."""
+        self.write_geom(paged, slot)
+        self.store(k_new, gate_new)
+        self.run_fused(incremental=True, paged=paged)
 
     def run(self, incremental: bool = False):
         self.head_gate()

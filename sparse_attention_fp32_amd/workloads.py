@@ -51,6 +51,7 @@ class Spec:
     sm_scale: float = 1.0
     eps: float = 1e-5
     always_select_tail: bool = False  # out_width then holds select_k*kpool + kpool-1 ids
+    live: Optional[List[int]] = None  # live lengths inside the regions (None: the whole regions)
 
     @property
     def B(self) -> int:
@@ -66,7 +67,11 @@ class Spec:
     def query_pos(self) -> List[int]:
         if self.q_pos is not None:
             return list(self.q_pos)
-        return [self.lengths[r] - 1 for r in self.query_req()]
+        n = self.live_lengths()
+        return [n[r] - 1 for r in self.query_req()]
+
+    def live_lengths(self) -> List[int]:
+        return list(self.live) if self.live is not None else list(self.lengths)
 
     def total_rows(self) -> int:
         return int(sum(self.lengths))
@@ -125,6 +130,10 @@ def spec_by_name(name: str, seed: int = 0) -> Spec:
                     index_dim=128, hidden=1024, select_k=100, out_width=403, mla_heads=64,
                     q_req=[0, 0, 1, 2, 2], q_pos=[999, 480, 516, 2052, 62],
                     always_select_tail=True)
+    if name == "medium_live":    # live lengths inside larger regions, one query per request
+        return Spec(name, lengths=[1000, 517, 2053], pads=[3, 0, 61], kpool=4, index_heads=16,
+                    index_dim=128, hidden=1024, select_k=100, out_width=403, mla_heads=64,
+                    always_select_tail=True, live=[901, 398, 1990])
     if name == "medium_fp8":
         return Spec(name, lengths=[777, 1500, 96, 2500], pads=[0, 17, 95, 5], kpool=8,
                     index_heads=12, index_dim=64, hidden=768, select_k=40, out_width=330,
@@ -252,7 +261,7 @@ def make_inputs(spec: Spec, seed: int = 0, device: str = "cpu") -> Inputs:
         ln_w=ln_w, ln_b=ln_b, qi=qi,
         q_req=torch.tensor(spec.query_req(), **i32),
         q_pos=torch.tensor(spec.query_pos(), **i32),
-        new_from=torch.tensor([t - 1 for t in spec.lengths], **i32),
+        new_from=torch.tensor([max(t - 1, 0) for t in spec.live_lengths()], **i32),
         q_mla=q_mla, ckv=ckv, ckv_scale=ckv_scale,
         kv_off=torch.tensor(offs[:-1], **i32),
     )

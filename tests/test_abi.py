@@ -17,14 +17,14 @@ NUL = ctypes.c_void_p(None)
 
 def test_exports_every_declared_function():
     names = dsa.header_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     import subprocess
     out = subprocess.run(["nm", "-D", "--defined-only", dsa.LIB_PATH], capture_output=True, text=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
     for n in names:
         assert n in exported, n
         getattr(dsa.lib(), n)
-    assert dsa.abi_version() == 1
+    assert dsa.abi_version() == 2
 
 
 def _code(fn, *args):
@@ -45,9 +45,11 @@ def test_head_gate_errors():
     assert L.dsa_head_gate(FAKE, FAKE, FAKE, 0, 4096, 16, NUL, 0, NUL) == dsa.DSA_OK  # no-op
 
 
-def _compress(kpool=4, D=128, B=2, max_cap=10, new_from=NUL, max_new=0, k=FAKE):
-    return dsa.lib().dsa_kpool_compress(k, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-5, B, D,
-                                        kpool, max_cap, new_from, max_new, FAKE, FAKE, FAKE, FAKE, NUL)
+def _compress(kpool=4, D=128, B=2, max_cap=10, new_from=NUL, max_new=0, k=FAKE, ln_w=FAKE,
+              ln_b=FAKE):
+    return dsa.lib().dsa_kpool_compress(k, FAKE, FAKE, FAKE, FAKE, FAKE, NUL, ln_w, ln_b, 1e-5, B,
+                                        D, kpool, max_cap, new_from, max_new, FAKE, FAKE, FAKE,
+                                        FAKE, NUL)
 
 
 def test_kpool_compress_errors():
@@ -61,6 +63,8 @@ def test_kpool_compress_errors():
     assert _compress(max_cap=-1) == INV
     assert _compress(new_from=FAKE, max_new=0) == INV
     assert _compress(k=NUL) == INV
+    assert _compress(ln_w=NUL) == INV             # both LayerNorm vectors, or neither
+    assert "both" in dsa.last_error()
     assert _compress(B=0) == dsa.DSA_OK
 
 
@@ -135,8 +139,8 @@ def test_fused_call_errors():
 
     def gc(M=16, K=4096, N=16, part_bytes=32 * 16 * 16 * 4, kpool=4, B=2, hidden=FAKE):
         return L.dsa_gate_compress(hidden, FAKE, M, K, N, FAKE, part_bytes, FAKE, FAKE, FAKE, FAKE,
-                                   FAKE, FAKE, FAKE, FAKE, 1e-5, B, 128, kpool, 10, NUL, 0, FAKE,
-                                   FAKE, FAKE, FAKE, NUL)
+                                   FAKE, FAKE, NUL, FAKE, FAKE, 1e-5, B, 128, kpool, 10, NUL, 0,
+                                   FAKE, FAKE, FAKE, FAKE, NUL)
     assert gc(N=17) == INV
     assert gc(part_bytes=32 * 16 * 16 * 4 - 1) == INV
     assert "need" in dsa.last_error()
@@ -194,3 +198,26 @@ def test_sparse_mla_paged_errors():
     assert call(bt=NUL) == INV
     assert call(wsb=need - 1) == INV
     assert call(Q=0) == dsa.DSA_OK
+
+
+def test_cache_write_errors():
+    L = dsa.lib()
+    def geom(B=3, slot=NUL, bt=NUL, bt_stride=0, page_rows=0, n_pages=0, seq_len=FAKE):
+        return L.dsa_write_geom(seq_len, B, bt, bt_stride, page_rows, n_pages, NUL, FAKE, NUL, slot,
+                                NUL)
+    assert geom(B=-1) == INV
+    assert geom(slot=FAKE) == INV                   # a slot needs the block table
+    assert "block table" in dsa.last_error()
+    assert geom(slot=FAKE, bt=FAKE, bt_stride=4, page_rows=0, n_pages=3) == INV
+    assert geom(seq_len=NUL) == INV
+    assert geom(B=0) == dsa.DSA_OK
+
+    def store(B=2, D=128, ln_w=NUL, ln_b=NUL, pos=FAKE, eps=1e-5):
+        return L.dsa_indexer_store(FAKE, FAKE, pos, FAKE, ln_w, ln_b, eps, B, D, FAKE, FAKE, FAKE,
+                                   NUL)
+    assert store(D=96) == UNS
+    assert store(ln_w=FAKE) == INV
+    assert store(eps=-1.0) == INV
+    assert store(pos=NUL) == INV
+    assert store(B=-1) == INV
+    assert store(B=0) == dsa.DSA_OK
