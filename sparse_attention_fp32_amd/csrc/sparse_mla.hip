@@ -55,6 +55,7 @@ constexpr int kHeadsWG = 16 * kHT;        // heads per workgroup
 constexpr int kTargetWG = 512;            // aim for two workgroups per CU
 constexpr int kMinSubPerChunk = 4;        // >= 128 ids per chunk keeps partials small
 constexpr int kMaxTch = 2048;             // most ids per chunk
+constexpr int kPF = 1;                    // sub-chunks of rows loading ahead of the one computed
 constexpr int kMaxBt = 2048;              // block-table entries staged in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
   __shared__ __attribute__((aligned(16))) float s_bias[kSub];  // 0, or -inf for no token
   __shared__ __attribute__((aligned(16))) float s_scl[kSub];   // row scale (1 for bf16)
   __shared__ float s_lrun[kHeadsWG];
-  __shared__ int s_id[kMaxTch];            // the chunk's cache rows (-1: none)
+  __shared__ int s_id[kMaxTch + kPF * kSub];  // the chunk's cache rows (-1: none)
   __shared__ int s_bt[PAGED ? kMaxBt : 1];  // the request's block-table row
 
   const int chunk = blockIdx.x, nchunks = gridDim.x, hb = blockIdx.y, qx = blockIdx.z;
@@ -193,7 +194,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
       return (int)(min((unsigned)pg, (unsigned)cm.n_pages - 1) * pr + off);
     };
     int32_t* krow = cm.kvidx && hb == 0 ? cm.kvidx + (int64_t)qx * out_width : nullptr;
-    for (int i = t; i < nid; i += 256) {
+    for (int i = t; i < nid + kPF * kSub; i += 256) {
       const int j = j0 + i;
       const int v = i < 256 ? id0 : trow[min(j, j1 - 1)];
       const int pv = j < j1 && v >= 0 ? phys(v) : -1;
@@ -201,8 +202,9 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
       if (krow && j < j1) krow[j] = pv;
     }
   } else {
-    s_id[t] = j0 + t < j1 ? id0 : -1;  // (entries past nid are never read)
-    for (int i = t + 256; i < nid; i += 256) {
+    // (entries from nid on are the -1 slots of the sub-chunks gathered past the end)
+    s_id[t] = j0 + t < j1 ? id0 : -1;
+    for (int i = t + 256; i < nid + kPF * kSub; i += 256) {
       const int j = j0 + i;
       const int v = trow[min(j, j1 - 1)];
       s_id[i] = j < j1 ? v : -1;
@@ -217,9 +219,11 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
     for (int e = 0; e < 8; ++e) o[ht][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;  // head w*16 + col (wave w < kHT owns head tile w)
 
-  RowSlice<FP8> cr;
-  float scl[2] = {1.f, 1.f};  // row scales of tokens col, 16 + col (wave 0, lanes < 16)
-  auto gather = [&](int s) {
+  // a ring of kPF row sets: sub-chunk s is gathered into slot s mod kPF, kPF
+  // sub-chunks ahead of its use; past the last sub-chunk every slot is empty
+  RowSlice<FP8> ring[kPF];
+  float rscl[kPF][2];  // row scales of tokens col, 16 + col (wave 0, lanes < 16)
+  auto gather = [&](int s, RowSlice<FP8>& cr, float (&scl)[2]) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int id = s_id[s * kSub + tt * 16 + col];
@@ -239,10 +243,14 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
       }
     }
   };
-  if (nsub > 0) gather(0);
+#pragma unroll
+  for (int j = 0; j < kPF; ++j) {
+    rscl[j][0] = rscl[j][1] = 1.f;
+    gather(j, ring[j], rscl[j]);
+  }
 
   uint8_t* my_slice = s_slice[w];
-  for (int s = 0; s < nsub; ++s) {
+  auto body = [&](int s, RowSlice<FP8>& cr, float (&scl)[2]) {
     const int ida[2] = {s_id[s * kSub + col], s_id[s * kSub + 16 + col]};
     const bool live = __any(ida[0] >= 0 || ida[1] >= 0);  // uniform over the workgroup
     f32x4_t sacc[kHT][2];
@@ -284,7 +292,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
         }
       }
     }
-    if (s + 1 < nsub) gather(s + 1);  // the next rows load while this sub-chunk computes
+    gather(s + kPF, cr, scl);  // later rows load while this sub-chunk computes
     if (live) {
 #pragma unroll
       for (int ht = 0; ht < kHT; ++ht)
@@ -385,6 +393,11 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
         for (int ht = 0; ht < kHT; ++ht) o[ht][e] = mfma16x16x32(pa[ht], bv, o[ht][e]);
       }
     }
+  };
+  for (int s0 = 0; s0 < nsub; s0 += kPF) {
+#pragma unroll
+    for (int j = 0; j < kPF; ++j)
+      if (s0 + j < nsub) body(s0 + j, ring[j], rscl[j]);
   }
 
   // epilogue: per-head sums to every wave, then this wave's dims of all heads
