@@ -257,8 +257,13 @@ def main():
     graphs_l = capture(lambda st: st.run_live(st.k_new, st.gate_new, paged=getattr(st, "pc", None),
                                               slot=st.slot if paged is not None else None))
     ms_l, _ = timed(graphs_l, max(1, a.steps // 4), max(1, a.warmup // 4))
-    live = {"step_us": round(ms_l / max(1, a.steps // 4) * 1e3, 2)}
     del graphs_l
+    graphs_l = capture(lambda st: st.run_live(st.k_new, st.gate_new, paged=getattr(st, "pc", None),
+                                              fused=True))
+    ms_lf, _ = timed(graphs_l, max(1, a.steps // 4), max(1, a.warmup // 4))
+    del graphs_l
+    live = {"step_us": round(ms_l / max(1, a.steps // 4) * 1e3, 2),
+            "fused_step_us": round(ms_lf / max(1, a.steps // 4) * 1e3, 2)}
 
     # -- per-call launch times: a graph of kCallsPerGraph back-to-back calls of
     # one kind (the input sets in rotation), replayed between HIP events on the
@@ -294,6 +299,7 @@ def main():
     fns["write_geom"] = lambda s: s.write_geom(getattr(s, "pc", None),
                                                s.slot if paged is not None else None)
     fns["indexer_store"] = lambda s: s.store(s.k_new, s.gate_new)
+    fns["gate_compress_live"] = lambda s: s.gate_compress_live(s.k_new, s.gate_new)
     call_us = {}
     reps = max(1, a.stage_reps // kCallsPerGraph)
     for name, fn in fns.items():
@@ -306,6 +312,7 @@ def main():
         paged["mla_us"] = round(call_us["sparse_mla_decode_paged"], 2)
     live["write_geom_us"] = round(call_us["write_geom"], 2)
     live["indexer_store_us"] = round(call_us["indexer_store"], 2)
+    live["gate_compress_live_us"] = round(call_us["gate_compress_live"], 2)
 
     xn0 = {"q_req": sets[0].q_req.cpu().numpy()}
     nb = algorithmic_bytes(spec, xn0, steps[0].n_pools.cpu().numpy(), steps[0].tok.cpu().numpy())

@@ -317,6 +317,16 @@ dsa_status dsa_sparse_mla_decode_paged(const uint16_t* q, const void* ckv, const
  * ln_w, ln_b [D] f32 or both NULL; k, gate [rows, D] bf16, valid [rows] u8.
  * Errors: INVALID_ARG for B < 0, NULL pointers, exactly one of ln_w / ln_b
  * NULL, eps < 0; UNSUPPORTED for D not in {32, 64, 128, 256}.
+ *
+ * dsa_gate_compress_live: the start of a decode step in one launch, with the
+ * results of dsa_write_geom (q_req, q_pos, new_from; no slot), then
+ * dsa_indexer_store (pos = new_from), then dsa_gate_compress in incremental
+ * mode (new_from, max_new = 1, seq_len).  ln_w / ln_b are required;
+ * normed_rows = 0 applies them after pooling (the stored row is raw),
+ * normed_rows = 1 to the stored row only (the per-token k_normed form).  The
+ * pool that the stored row completes takes that row from registers.  k, gate
+ * and valid are written (the stored row); every other argument as in those
+ * calls.  Errors: the union of theirs.
  * ------------------------------------------------------------------------- */
 dsa_status dsa_write_geom(const int32_t* seq_len, int B, const int32_t* block_table, int bt_stride,
                           int page_rows, int n_pages, int32_t* q_req, int32_t* q_pos,
@@ -325,6 +335,16 @@ dsa_status dsa_indexer_store(const uint16_t* k_new, const uint16_t* gate_new, co
                              const int32_t* tok_off, const float* ln_w, const float* ln_b,
                              float eps, int B, int D, uint16_t* k, uint16_t* gate,
                              uint8_t* valid, hipStream_t stream);
+dsa_status dsa_gate_compress_live(const float* hidden, const float* W, int M, int K, int N,
+                                  float* gate_part, size_t gate_part_bytes, uint16_t* k,
+                                  uint16_t* gate, const uint16_t* ape, uint8_t* valid,
+                                  const int32_t* tok_off, const int32_t* pool_off,
+                                  const int32_t* seq_len, const uint16_t* k_new,
+                                  const uint16_t* gate_new, const float* ln_w, const float* ln_b,
+                                  int normed_rows, float eps, int B, int D, int kpool,
+                                  int max_cap, uint16_t* keys, int32_t* pool_start,
+                                  uint8_t* pool_valid, int32_t* n_pools, int32_t* q_req,
+                                  int32_t* q_pos, int32_t* new_from, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Fused decode calls   [stkernel pull request #290 measures what each launch

@@ -64,29 +64,14 @@ __global__ __launch_bounds__(256) void indexer_store_kernel(
   const int region = tok_off[r + 1] - (int)row0;
   uint4 out = kv;
   if (ln_w) {
-    float x[8];
+    float x[8], lw[8], lb[8];
+    bf16x8_to_f32(kv, x);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const uint32_t w = u4_word(kv, c >> 1);
-      x[c] = bf16_to_f32((c & 1) ? (w >> 16) : (w & 0xffffu));
+      lw[c] = ln_w[c0 + c];
+      lb[c] = ln_b[c0 + c];
     }
-    float sum = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) sum += x[c];
-    const float mean = group_sum<LPP>(sum) / (float)D;
-    float sq = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const float d = x[c] - mean;
-      sq = fmaf(d, d, sq);
-    }
-    const float rstd = 1.0f / sqrtf(group_sum<LPP>(sq) / (float)D + eps);
-    uint32_t pk[4];
-#pragma unroll
-    for (int c = 0; c < 8; c += 2)
-      pk[c >> 1] = pack_bf16x2((x[c] - mean) * rstd * ln_w[c0 + c] + ln_b[c0 + c],
-                               (x[c + 1] - mean) * rstd * ln_w[c0 + c + 1] + ln_b[c0 + c + 1]);
-    out = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    out = layer_norm8_bf16<LPP>(x, lw, lb, eps);
   }
   if (p < 0 || p >= region) return;  // outside the request's region: nothing stored
   const int64_t row = row0 + p;

@@ -166,4 +166,39 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// k_norm (LayerNorm with bias, biased variance) of a row of W*8 channels held
+// 8 per lane over an aligned group of W lanes; returns this lane's 8 outputs
+// as bf16 (round to nearest even).
+template <int W>
+__device__ __forceinline__ uint4 layer_norm8_bf16(const float (&x)[8], const float (&lw)[8],
+                                                  const float (&lb)[8], float eps) {
+  constexpr int D = W * 8;
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) sum += x[c];
+  const float mean = group_sum<W>(sum) / (float)D;
+  float sq = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float d = x[c] - mean;
+    sq = fmaf(d, d, sq);
+  }
+  const float rstd = 1.0f / sqrtf(group_sum<W>(sq) / (float)D + eps);
+  uint32_t pk[4];
+#pragma unroll
+  for (int c = 0; c < 8; c += 2)
+    pk[c >> 1] = pack_bf16x2((x[c] - mean) * rstd * lw[c] + lb[c],
+                             (x[c + 1] - mean) * rstd * lw[c + 1] + lb[c + 1]);
+  return make_uint4(pk[0], pk[1], pk[2], pk[3]);
+}
+
+// The 8 bf16 values of a 16-byte word as floats (exact).
+__device__ __forceinline__ void bf16x8_to_f32(uint4 v, float (&x)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t w = u4_word(v, c >> 1);
+    x[c] = bf16_to_f32((c & 1) ? (w >> 16) : (w & 0xffffu));
+  }
+}
+
 }  // namespace dsa

@@ -133,17 +133,32 @@ __device__ void gate_partial(const GateArgs& ga, int g) {
   if (m0 + m < M && n < N) ga.part[((int64_t)sl * M + m0 + m) * N + n] = acc;
 }
 
+// A whole decode step's start in the compression launch (dsa_gate_compress_live):
+// the geometry from the live lengths, the store of the staged indexer row, and
+// the recompression of the pool that row completes, which takes the row from
+// registers rather than re-reading what this launch stores.
+struct LiveArgs {
+  const uint16_t* k_new;     // [B, D] staged rows; NULL: not a live call
+  const uint16_t* gate_new;  // [B, D]
+  int store_ln;              // normalise the stored k row (the per-token k_normed form)
+  const float* sln_w;        // [D] LayerNorm of the stored row
+  const float* sln_b;
+  int32_t* q_req;            // [B] outputs of the geometry
+  int32_t* q_pos;
+  int32_t* new_from;
+};
+
 template <int LPP, int KP>  // lanes per pool = D / 8; pool slots
 __global__ __launch_bounds__(256) void kpool_compress_kernel(
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ gate,
-    const uint16_t* __restrict__ ape, const uint8_t* __restrict__ valid,
+    uint16_t* __restrict__ k, uint16_t* __restrict__ gate,  // (written by a live call only)
+    const uint16_t* __restrict__ ape, uint8_t* __restrict__ valid,
     const int32_t* __restrict__ tok_off, const int32_t* __restrict__ pool_off,
     const int32_t* __restrict__ live_len, int has_live, const float* __restrict__ ln_w,
     const float* __restrict__ ln_b, float eps,
     const int32_t* __restrict__ new_from, int pools_per_wg, int spec_pools,
     uint16_t* __restrict__ keys,
     int32_t* __restrict__ pool_start, uint8_t* __restrict__ pool_valid,
-    int32_t* __restrict__ n_pools, int B, GateArgs ga) {
+    int32_t* __restrict__ n_pools, int B, GateArgs ga, LiveArgs la) {
   constexpr int D = LPP * 8;
   constexpr int kpool = KP;
   constexpr int kGroups = 256 / LPP;  // pools in flight per workgroup
@@ -158,19 +173,26 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
   const int li = t % LPP;     // lane within the pool's lane group
   const int grp = t / LPP;    // pool group within the workgroup
   const int c0 = li * 8;      // first channel of this lane
-  // Loads that need no geometry go out with the geometry itself.
-  // the geometry loads, issued together (the empty asm keeps the compiler
-  // from moving the live-length load into a branch of its own)
+  const bool live_call = la.k_new != nullptr;
+  // The geometry loads, issued together (the empty asm keeps the compiler
+  // from moving the live-length load into a branch of its own); the loads
+  // that need no geometry go out with them.
   int g_lo = tok_off[r], g_hi = tok_off[r + 1], g_pb = pool_off[r], g_pe = pool_off[r + 1];
   int live = live_len[r];  // (tok_off when there are no live lengths)
   int g_nf = *(new_from ? new_from + r : tok_off + r);
   asm volatile("" : "+s"(g_lo), "+s"(g_hi), "+s"(g_pb), "+s"(g_pe), "+s"(live), "+s"(g_nf));
   const int64_t row0 = g_lo;
   const int region = g_hi - g_lo;
-  const int T = has_live ? min(max(live, 0), region) : region;
+  const int n_live = max(live, 0);
+  const int T = has_live ? min(n_live, region) : region;
   const int64_t pbase = g_pb;
   const int cap = g_pe - g_pb;
-  const int nf = new_from ? g_nf : 0;
+  // a live call writes row n_live - 1 and recompresses from it
+  const int nf = live_call ? max(n_live - 1, 0) : new_from ? g_nf : 0;
+  const bool incremental = live_call || new_from != nullptr;
+  // the staged row (every lane loads its channels; one lane group uses them)
+  const uint4 kst = *(const uint4*)(live_call ? la.k_new + (int64_t)r * D + c0 : ape + c0);
+  const uint4 gst = *(const uint4*)(live_call ? la.gate_new + (int64_t)r * D + c0 : ape + c0);
   const bool post_ln = ln_w != nullptr;
   const float* lwp = post_ln ? ln_w : kNoLn;
   const float* lbp = post_ln ? ln_b : kNoLn;
@@ -208,32 +230,16 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
       }
       x[c] = acc / z;
     }
-    uint32_t packed[4];
+    uint4 key;
     if (!post_ln) {
+      uint32_t pk[4];
 #pragma unroll
-      for (int c = 0; c < 8; c += 2) packed[c >> 1] = pack_bf16x2(x[c], x[c + 1]);
+      for (int c = 0; c < 8; c += 2) pk[c >> 1] = pack_bf16x2(x[c], x[c + 1]);
+      key = make_uint4(pk[0], pk[1], pk[2], pk[3]);
     } else {
-    float sum = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) sum += x[c];
-    sum = group_sum<LPP>(sum);
-    const float mean = sum / (float)D;
-    float sq = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const float d = x[c] - mean;
-      sq = fmaf(d, d, sq);
+      key = layer_norm8_bf16<LPP>(x, lw, lb, eps);
     }
-    sq = group_sum<LPP>(sq);
-    const float rstd = 1.0f / sqrtf(sq / (float)D + eps);
-#pragma unroll
-    for (int c = 0; c < 8; c += 2) {
-      const float y0 = (x[c] - mean) * rstd * lw[c] + lb[c];
-      const float y1 = (x[c + 1] - mean) * rstd * lw[c + 1] + lb[c + 1];
-      packed[c >> 1] = pack_bf16x2(y0, y1);
-    }
-    }
-    *(uint4*)(keys + (pbase + p) * D + c0) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    *(uint4*)(keys + (pbase + p) * D + c0) = key;
     if (li == 0) {
       pool_start[pbase + p] = f + p * kpool;
       pool_valid[pbase + p] = (uint8_t)allv;
@@ -242,7 +248,7 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
   // The kpool rows from row0 + rs: all loads issued together; the validity
   // bytes are consumed at once (so no later instruction waits on them alone).
   auto load_rows = [&](const uint16_t* kb, const uint16_t* gb, const uint8_t* vbp, int64_t rs,
-                       uint4 (&kr)[KP], uint4 (&gr)[KP]) {
+                       uint4 (&kr)[KP], uint4 (&gr)[KP], bool last_valid = false) {
     uint8_t vb[KP];
 #pragma unroll
     for (int s = 0; s < KP; ++s) {
@@ -252,11 +258,11 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
     }
     int allv = 1;
 #pragma unroll
-    for (int s = 0; s < KP; ++s) allv &= vb[s] != 0;
+    for (int s = 0; s < KP; ++s) allv &= (s == KP - 1 && last_valid) || vb[s] != 0;
     return allv;
   };
 
-  if (!new_from) {
+  if (!incremental) {
     // full mode: every slot of the request, in ascending order
     const int f = first_valid_row(valid, row0, T, &s_first);
     int P = f < 0 ? 0 : (T - f) / kpool;
@@ -289,16 +295,51 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
   // from slot 0 of the earlier call (the start of pool 0) when that slot holds
   // a pool starting before new_from -- rows before new_from are unchanged, so
   // f is too -- and from the scan otherwise.
+  //
+  // A live call also stores the staged row at nf (group 0 of the request's
+  // first workgroup) and, when that row is the newest live row, uses it from
+  // registers as the last slot of the pool ending at T.
   const int i0 = blockIdx.x * pools_per_wg + grp;
   const bool spec = i0 < spec_pools && T >= kpool * (i0 + 1);
   const int64_t srs = spec ? row0 + T - (int64_t)kpool * (i0 + 1) : 0;
+  const bool subst = live_call && n_live >= 1 && nf == T - 1;  // the stored row is live row T-1
+  const int fc = *(cap > 0 ? pool_start + pbase : tok_off + r);  // (unused when cap == 0)
   uint4 skr[KP], sgr[KP];
   // (with no such rows the loads read ape's kpool rows)
   const int sallv = load_rows(spec ? k : ape, spec ? gate : ape,
-                              spec ? valid : (const uint8_t*)ape, srs, skr, sgr);
-  const int fc = *(cap > 0 ? pool_start + pbase : new_from + r);  // (unused when cap == 0)
+                              spec ? valid : (const uint8_t*)ape, srs, skr, sgr,
+                              subst && i0 == 0);
+  if (live_call) {
+    uint4 kout = kst;
+    if (la.store_ln) {  // (all lanes: the group sums need every lane of the group)
+      float x[8], sw[8], sb[8];
+      bf16x8_to_f32(kst, x);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        sw[c] = la.sln_w[c0 + c];
+        sb[c] = la.sln_b[c0 + c];
+      }
+      kout = layer_norm8_bf16<LPP>(x, sw, sb, eps);
+    }
+    if (blockIdx.x == 0 && grp == 0 && nf < region) {
+      const int64_t row = row0 + nf;
+      *(uint4*)(k + row * D + c0) = kout;
+      *(uint4*)(gate + row * D + c0) = gst;
+      if (li == 0) valid[row] = 1;
+    }
+    if (blockIdx.x == 0 && t == 0) {
+      la.q_req[r] = r;
+      la.q_pos[r] = n_live - 1;
+      la.new_from[r] = nf;
+    }
+    if (subst && i0 == 0) {
+      skr[KP - 1] = kout;
+      sgr[KP - 1] = gst;
+    }
+  }
   const bool cached = cap > 0 && fc >= 0 && fc < nf;
-  const int f = cached ? fc : first_valid_row(valid, row0, T, &s_first);
+  int f = cached ? fc : first_valid_row(valid, row0, T, &s_first);
+  if (subst && !cached) f = f >= 0 ? min(f, T - 1) : T - 1;  // (row T-1 is valid now)
   int P = f < 0 ? 0 : (T - f) / kpool;
   if (P > cap) P = cap;
   if (blockIdx.x == 0 && t == 0) n_pools[r] = P;
@@ -340,17 +381,19 @@ dsa_status check_compress_args(int B, int D, int kpool, int max_cap, const int32
 }
 
 // One launch: B rows of compression workgroups, then ga.nwg gate workgroups.
+// k, gate and valid are written only by a live call (la.k_new set).
 dsa_status launch_compress(const uint16_t* k, const uint16_t* gate, const uint16_t* ape,
                            const uint8_t* valid, const int32_t* tok_off, const int32_t* pool_off,
-                           const int32_t* seq_len, const float* ln_w, const float* ln_b, float eps, int B, int D,
-                           int kpool, int max_cap, const int32_t* new_from, int max_new,
-                           uint16_t* keys, int32_t* pool_start, uint8_t* pool_valid,
-                           int32_t* n_pools, const GateArgs& ga, hipStream_t stream,
-                           const char* who) {
+                           const int32_t* seq_len, const float* ln_w, const float* ln_b,
+                           float eps, int B, int D, int kpool, int max_cap,
+                           const int32_t* new_from, int max_new, uint16_t* keys,
+                           int32_t* pool_start, uint8_t* pool_valid, int32_t* n_pools,
+                           const GateArgs& ga, hipStream_t stream, const char* who,
+                           const LiveArgs& la = LiveArgs{}) {
   const int lpp = D / 8;
   const int groups = 256 / lpp;
   int ppw, nx, spec = 0;
-  if (new_from) {
+  if (new_from || la.k_new) {
     const int touch = (max_new + kpool - 1) / kpool;  // pools one request can touch
     ppw = groups;
     nx = (touch + ppw - 1) / ppw;
@@ -365,12 +408,12 @@ dsa_status launch_compress(const uint16_t* k, const uint16_t* gate, const uint16
   if (dsa::trace_enabled())
     fprintf(stderr,
             "[dsa] %s B=%d D=%d kpool=%d max_cap=%d inc=%d gate_wg=%d grid=(%d,%d)\n", who, B,
-            D, kpool, max_cap, new_from != nullptr, ga.nwg, grid.x, grid.y);
+            D, kpool, max_cap, new_from != nullptr || la.k_new != nullptr, ga.nwg, grid.x, grid.y);
 #define DSA_LAUNCH_KP(LPP, KP)                                                                 \
   kpool_compress_kernel<LPP, KP><<<grid, 256, 0, stream>>>(                                     \
-      k, gate, ape, valid, tok_off, pool_off, seq_len ? seq_len : tok_off, seq_len != nullptr, ln_w, \
-      ln_b, eps, new_from, ppw, spec, keys, \
-      pool_start, pool_valid, n_pools, B, ga)
+      const_cast<uint16_t*>(k), const_cast<uint16_t*>(gate), ape, const_cast<uint8_t*>(valid),  \
+      tok_off, pool_off, seq_len ? seq_len : tok_off, seq_len != nullptr, ln_w, ln_b, eps,      \
+      new_from, ppw, spec, keys, pool_start, pool_valid, n_pools, B, ga, la)
 #define DSA_LAUNCH_KP_D(KP)            \
   switch (lpp) {                       \
     case 4: DSA_LAUNCH_KP(4, KP); break;   \
@@ -476,4 +519,48 @@ DSA_EXPORT dsa_status dsa_gate_compress(const float* hidden, const float* W, int
   return launch_compress(k, gate, ape, valid, tok_off, pool_off, seq_len, ln_w, ln_b, eps, B, D,
                          kpool, max_cap, new_from, max_new, keys, pool_start, pool_valid,
                          n_pools, ga, stream, "dsa_gate_compress");
+}
+
+DSA_EXPORT dsa_status dsa_gate_compress_live(
+    const float* hidden, const float* W, int M, int K, int N, float* gate_part,
+    size_t gate_part_bytes, uint16_t* k, uint16_t* gate, const uint16_t* ape, uint8_t* valid,
+    const int32_t* tok_off, const int32_t* pool_off, const int32_t* seq_len,
+    const uint16_t* k_new, const uint16_t* gate_new, const float* ln_w, const float* ln_b,
+    int normed_rows, float eps, int B, int D, int kpool, int max_cap, uint16_t* keys,
+    int32_t* pool_start, uint8_t* pool_valid, int32_t* n_pools, int32_t* q_req, int32_t* q_pos,
+    int32_t* new_from, hipStream_t stream) {
+  DSA_REQUIRE(N >= 1 && N <= DSA_MAX_INDEX_HEADS, DSA_ERR_INVALID_ARG,
+              "dsa_gate_compress_live: N=%d outside [1,%d]", N, DSA_MAX_INDEX_HEADS);
+  DSA_REQUIRE(M >= 0 && K >= 1, DSA_ERR_INVALID_ARG, "dsa_gate_compress_live: M=%d K=%d", M, K);
+  const dsa_status st = check_compress_args(B, D, kpool, max_cap, nullptr, 1, eps, ln_w, ln_b);
+  if (st != DSA_OK) return st;
+  DSA_REQUIRE(ln_w != nullptr, DSA_ERR_INVALID_ARG,
+              "dsa_gate_compress_live: ln_w / ln_b are required (normed_rows selects where the "
+              "LayerNorm applies)");
+  const size_t need = dsa_gate_compress_workspace_size(M, K, N);
+  DSA_REQUIRE(M == 0 || (gate_part && gate_part_bytes >= need), DSA_ERR_INVALID_ARG,
+              "dsa_gate_compress_live: gate partials %zu bytes, need %zu", gate_part_bytes, need);
+  DSA_REQUIRE(M == 0 || (hidden && W), DSA_ERR_INVALID_ARG,
+              "dsa_gate_compress_live: NULL tensor pointer");
+  DSA_REQUIRE(B == 0 || (k && gate && ape && valid && tok_off && pool_off && seq_len && k_new &&
+                         gate_new && keys && pool_start && pool_valid && n_pools && q_req &&
+                         q_pos && new_from),
+              DSA_ERR_INVALID_ARG, "dsa_gate_compress_live: NULL tensor pointer");
+  const LiveArgs la{k_new, gate_new, normed_rows != 0, ln_w, ln_b, q_req, q_pos, new_from};
+  const float* pw = normed_rows ? nullptr : ln_w;  // LayerNorm after pooling
+  const float* pb = normed_rows ? nullptr : ln_b;
+  const int ns = gate_slices(M, K);
+  if (M > 0 && ns == 1) {  // dense head-gate: the partials buffer receives w
+    const dsa_status g = dsa_head_gate(hidden, W, gate_part, M, K, N, nullptr, 0, stream);
+    if (g != DSA_OK) return g;
+    if (B == 0) return DSA_OK;
+    return launch_compress(k, gate, ape, valid, tok_off, pool_off, seq_len, pw, pb, eps, B, D,
+                           kpool, max_cap, nullptr, 1, keys, pool_start, pool_valid, n_pools,
+                           GateArgs{}, stream, "dsa_gate_compress_live", la);
+  }
+  GateArgs ga{hidden, W, gate_part, M, K, N, ns, M > 0 ? ns * ((M + kGateRows - 1) / kGateRows) : 0};
+  if (B == 0 && ga.nwg == 0) return DSA_OK;
+  return launch_compress(k, gate, ape, valid, tok_off, pool_off, seq_len, pw, pb, eps, B, D,
+                         kpool, max_cap, nullptr, 1, keys, pool_start, pool_valid, n_pools, ga,
+                         stream, "dsa_gate_compress_live", la);
 }

@@ -52,6 +52,9 @@ _SIGS = {
                                _F, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P]),
     "dsa_write_geom": (_I, [_P, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P]),
     "dsa_indexer_store": (_I, [_P, _P, _P, _P, _P, _P, _F, _I, _I, _P, _P, _P, _P]),
+    "dsa_gate_compress_live": (_I, [_P, _P, _I, _I, _I, _P, _Z, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                    _P, _P, _I, _F, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
+                                    _P]),
     "dsa_index_scores_gated": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                                     _I, _P, _P, _P]),
     "dsa_topk_expand": (_I, [_P, _P, _I, _I, _I, _P, _P, _P, _I, _I, _I, _P, _P, _P]),
@@ -332,3 +335,24 @@ def dsa_select_tail(valid, tok_off, pool_start, pool_off, n_pools, q_req, q_pos,
         _dev(pool_off, _I32, "pool_off"), _dev(n_pools, _I32, "n_pools"), _dev(q_req, _I32, "q_req"),
         _dev(q_pos, _I32, "q_pos"), Q, kpool, select_k, out_width, _dev(tok, _I32, "tok"),
         _stream(stream)))
+
+
+def dsa_gate_compress_live(hidden, W, gate_part, k, gate, ape, valid, tok_off, pool_off, seq_len,
+                           k_new, gate_new, ln_w, ln_b, normed_rows: bool, eps: float, kpool: int,
+                           max_cap: int, keys, pool_start, pool_valid, n_pools, q_req, q_pos,
+                           new_from, stream=None) -> None:
+    M, K = hidden.shape
+    N = W.shape[1]
+    B = tok_off.numel() - 1
+    D = k.shape[1]
+    gp, gb = _ws(gate_part)
+    _check(lib().dsa_gate_compress_live(
+        _dev(hidden, torch.float32, "hidden"), _dev(W, torch.float32, "W"), M, K, N, gp, gb,
+        _dev(k, _BF, "k"), _dev(gate, _BF, "gate"), _dev(ape, _BF, "ape"), _dev(valid, _U8, "valid"),
+        _dev(tok_off, _I32, "tok_off"), _dev(pool_off, _I32, "pool_off"),
+        _dev(seq_len, _I32, "seq_len"), _dev(k_new, _BF, "k_new"), _dev(gate_new, _BF, "gate_new"),
+        _dev(ln_w, torch.float32, "ln_w"), _dev(ln_b, torch.float32, "ln_b"), int(bool(normed_rows)),
+        float(eps), B, D, kpool, max_cap, _dev(keys, _BF, "keys"),
+        _dev(pool_start, _I32, "pool_start"), _dev(pool_valid, _U8, "pool_valid"),
+        _dev(n_pools, _I32, "n_pools"), _dev(q_req, _I32, "q_req"), _dev(q_pos, _I32, "q_pos"),
+        _dev(new_from, _I32, "new_from"), _stream(stream)))

@@ -160,12 +160,31 @@ class DsaStep:
         dsa.dsa_indexer_store(k_new, gate_new, x.new_from, x.tok_off, x.k, x.gate, x.valid,
                               ln_w=lw, ln_b=lb, eps=self.spec.eps, stream=self.stream)
 
-    def run_live(self, k_new, gate_new, paged=None, slot=None):
+    def gate_compress_live(self, k_new, gate_new):
+        """Geometry, row store, head-gate and incremental compression in one launch."""
+        x = self.x
+        dsa.dsa_gate_compress_live(x.hidden, x.W, self.gate_part, x.k, x.gate, x.ape, x.valid,
+                                   x.tok_off, x.pool_off, self.seq_len, k_new, gate_new, x.ln_w,
+                                   x.ln_b, not self.post_ln, self.spec.eps, self.spec.kpool,
+                                   self.max_cap, self.keys, self.pool_start, self.pool_valid,
+                                   self.n_pools, x.q_req, x.q_pos, x.new_from, stream=self.stream)
+
+    def run_live(self, k_new, gate_new, paged=None, slot=None, fused: bool = False):
         """A whole decode step from the live lengths: geometry, the row store,
-        then the fused step over cached pools."""
-        self.write_geom(paged, slot)
-        self.store(k_new, gate_new)
-        self.run_fused(incremental=True, paged=paged)
+        then the fused step over cached pools.  fused: the first three in the
+        compression launch (dsa_gate_compress_live; no slot is written)."""
+        if fused:
+            self.gate_compress_live(k_new, gate_new)
+        else:
+            self.write_geom(paged, slot)
+            self.store(k_new, gate_new)
+            self.gate_compress(incremental=True)
+        self.index_scores_gated()
+        self.topk_expand()
+        if paged is None:
+            self.mla()
+        else:
+            self.mla_paged(paged)
 
     def run(self, incremental: bool = False):
         self.head_gate()

@@ -17,7 +17,7 @@ NUL = ctypes.c_void_p(None)
 
 def test_exports_every_declared_function():
     names = dsa.header_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     import subprocess
     out = subprocess.run(["nm", "-D", "--defined-only", dsa.LIB_PATH], capture_output=True, text=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
@@ -221,3 +221,15 @@ def test_cache_write_errors():
     assert store(pos=NUL) == INV
     assert store(B=-1) == INV
     assert store(B=0) == dsa.DSA_OK
+
+    def live(ln_w=FAKE, ln_b=FAKE, kpool=4, seq_len=FAKE, N=16, part_bytes=32 * 16 * 16 * 4):
+        return L.dsa_gate_compress_live(FAKE, FAKE, 16, 4096, N, FAKE, part_bytes, FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, FAKE, seq_len, FAKE, FAKE, ln_w, ln_b, 0, 1e-5,
+                                        2, 128, kpool, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        NUL)
+    assert live(ln_w=NUL, ln_b=NUL) == INV          # the LayerNorm is required here
+    assert live(ln_w=NUL) == INV
+    assert live(kpool=9) == INV
+    assert live(seq_len=NUL) == INV
+    assert live(N=17) == INV
+    assert live(part_bytes=4) == INV

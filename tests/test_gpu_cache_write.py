@@ -133,12 +133,14 @@ def test_write_geom():
         assert np.array_equal(_np(out[n]), want[n]), n
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("post_ln", [True, False])
-def test_live_decode_graph(post_ln):
+def test_live_decode_graph(post_ln, fused):
     """One captured graph per variant: write_geom -> indexer_store -> the fused
-    step over cached pools with the paged attention.  Between replays the
-    host only writes the new live lengths and the staged rows into device
-    buffers; each replay is checked against the oracle at its lengths."""
+    step over cached pools with the paged attention (fused: the first three
+    as one dsa_gate_compress_live launch).  Between replays the host only
+    writes the new live lengths and the staged rows into device buffers; each
+    replay is checked against the oracle at its lengths."""
     _need_gpu()
     from sparse_attention_fp32_amd.pipeline import DsaStep
     spec = W.spec_by_name("medium_live")
@@ -161,7 +163,7 @@ def test_live_decode_graph(post_ln):
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        st.run_live(k_new, gate_new, paged=pc, slot=slot)
+        st.run_live(k_new, gate_new, paged=pc, slot=slot, fused=fused)
     torch.cuda.synchronize()
 
     k, gate, valid = xn["k"].copy(), xn["gate"].copy(), xn["valid"].copy()
@@ -176,13 +178,15 @@ def test_live_decode_graph(post_ln):
         st.seq_len.copy_(torch.from_numpy(seq))
         k_new.copy_(kn)
         gate_new.copy_(gn)
-        _say(f"live decode post_ln={post_ln} step {step}: lengths {seq.tolist()}")
+        _say(f"live decode post_ln={post_ln} fused={fused} step {step}: lengths {seq.tolist()}")
         g.replay()
         torch.cuda.synchronize()
 
         geo = O.write_geom(seq, table, pc.page_rows)
-        for name, t in (("q_req", xg.q_req), ("q_pos", xg.q_pos), ("new_from", xg.new_from),
-                        ("slot", slot)):
+        outs = [("q_req", xg.q_req), ("q_pos", xg.q_pos), ("new_from", xg.new_from)]
+        if not fused:
+            outs.append(("slot", slot))
+        for name, t in outs:
             assert np.array_equal(_np(t), geo[name]), (step, name)
         stored = O.indexer_store(k, gate, valid, xn["tok_off"], geo["new_from"], kn.numpy(),
                                  gn.numpy(), ln[0], ln[1], spec.eps)
@@ -210,3 +214,45 @@ def test_live_decode_graph(post_ln):
             if nd == 0:
                 assert np.array_equal(tok_g[q], ref["tok"][q]), (step, q)
                 PT.check_mla(out_g, lse_g, ref["out_f64"], ref["lse"], rows=[q])
+
+
+@pytest.mark.parametrize("post_ln", [True, False])
+def test_live_call_equals_three_calls(post_ln):
+    """dsa_gate_compress_live leaves every buffer bit-equal to write_geom +
+    indexer_store + gate_compress, step after step, including steps that
+    complete a pool and an empty request that receives its first row."""
+    _need_gpu()
+    from sparse_attention_fp32_amd.pipeline import DsaStep
+    spec = W.spec_by_name("medium_live")
+    B, D = spec.B, spec.index_dim
+    x = W.make_inputs(spec, seed=0)
+    steps = []
+    seq0 = np.array([901, 0, 1990], dtype=np.int32)
+    for _ in range(2):
+        st = DsaStep(x.to("cuda"))
+        st.post_ln = post_ln
+        st.seq_len = torch.from_numpy(seq0).cuda()
+        st.write_geom()
+        st.gate_compress(incremental=False)
+        steps.append(st)
+    rng = np.random.default_rng(44)
+    seq = seq0.copy()
+    for step in range(9):
+        seq = seq + 1
+        kn, gn = _bf16_rows(rng, (B, D)).cuda(), _bf16_rows(rng, (B, D)).cuda()
+        _say(f"live call vs three calls post_ln={post_ln} step {step}: {seq.tolist()}")
+        for i, st in enumerate(steps):
+            st.seq_len.copy_(torch.from_numpy(seq))
+            if i == 0:
+                st.write_geom()
+                st.store(kn, gn)
+                st.gate_compress(incremental=True)
+            else:
+                st.gate_compress_live(kn, gn)
+        a, b = steps
+        for name in ("k", "gate", "valid", "q_req", "q_pos", "new_from"):
+            assert np.array_equal(_np(getattr(a.x, name)).view(np.uint8),
+                                  _np(getattr(b.x, name)).view(np.uint8)), (step, name)
+        for name in ("keys", "pool_start", "pool_valid", "n_pools", "gate_part"):
+            assert np.array_equal(_np(getattr(a, name)).view(np.uint8),
+                                  _np(getattr(b, name)).view(np.uint8)), (step, name)
