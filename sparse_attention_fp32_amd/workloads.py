@@ -130,6 +130,18 @@ def spec_by_name(name: str, seed: int = 0) -> Spec:
                     index_dim=128, hidden=1024, select_k=100, out_width=403, mla_heads=64,
                     q_req=[0, 0, 1, 2, 2], q_pos=[999, 480, 516, 2052, 62],
                     always_select_tail=True)
+    if name == "medium_pairs":   # 32 queries x 1100 ids: seven attention chunks of 160 ids,
+        # the last one short; a third of the queries sit mid-context (fewer candidates)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 106])))
+        lengths = [2600, 1900, 3100]
+        q_req = [0] * 11 + [1] * 10 + [2] * 11
+        q_pos = []
+        for r in q_req:
+            n = lengths[r]
+            q_pos.append(n - 1 if len(q_pos) % 3 else int(rng.integers(n // 3, n - 1)))
+        return Spec(name, lengths=lengths, pads=[0, 11, 40], kpool=4, index_heads=16,
+                    index_dim=128, hidden=512, select_k=275, out_width=1100, mla_heads=64,
+                    q_req=q_req, q_pos=q_pos)
     if name == "medium_live":    # live lengths inside larger regions, one query per request
         return Spec(name, lengths=[1000, 517, 2053], pads=[3, 0, 61], kpool=4, index_heads=16,
                     index_dim=128, hidden=1024, select_k=100, out_width=403, mla_heads=64,
@@ -142,7 +154,7 @@ def spec_by_name(name: str, seed: int = 0) -> Spec:
 
 
 WORKLOADS = ("tiny", "decode32k", "longctx", "prefill4k", "mixed64")
-PARITY_SHAPES = ("tiny", "medium", "medium_fp8", "medium_tail")
+PARITY_SHAPES = ("tiny", "medium", "medium_fp8", "medium_tail", "medium_pairs")
 
 
 @dataclasses.dataclass
