@@ -23,7 +23,8 @@ The JSON line also carries, for the call that takes the most time, its
 algorithmic bytes per launch over its average launch time (a graph of 32
 back-to-back calls of that kind, replayed between HIP events on the launch
 stream),
-against the 8 TB/s HBM peak; and the CPU oracle's throughput on a bounded
+against the 8 TB/s HBM peak and against the lane (a plain coalesced read of
+1 GiB, dsa_lane_read, timed in the same run); and the CPU oracle's throughput on a bounded
 sample of the same workload (rank 0 only).
 """
 from __future__ import annotations
@@ -338,6 +339,23 @@ def main():
     live["indexer_store_us"] = round(call_us["indexer_store"], 2)
     live["gate_compress_live_us"] = round(call_us["gate_compress_live"], 2)
 
+    # the lane: a plain coalesced 16-byte-per-lane read of 1 GiB on this part
+    lane_bytes = 1 << 30
+    lane_buf = torch.empty(lane_bytes, dtype=torch.uint8, device=dev)
+    lane_buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        dsa.dsa_lane_read(lane_buf, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dsa.dsa_lane_read(lane_buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    lane_gbs = lane_bytes / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+    del lane_buf
+
     xn0 = {"q_req": sets[0].q_req.cpu().numpy()}
     nb = algorithmic_bytes(spec, xn0, steps[0].n_pools.cpu().numpy(), steps[0].tok.cpu().numpy())
     step_bytes = sum(nb[k] for k in STAGES)
@@ -346,7 +364,8 @@ def main():
     traffic = stored_traffic(dom, spec.name)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "algorithmic_bytes": int(nb[dom]), "avg_launch_us": round(stage_us[dom], 2)}
+                "algorithmic_bytes": int(nb[dom]), "avg_launch_us": round(stage_us[dom], 2),
+                "lane_GBps": round(lane_gbs, 1), "frac_of_lane": round(ach / lane_gbs, 4)}
 
     cpu = None
     if not a.no_cpu_baseline:

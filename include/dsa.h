@@ -407,6 +407,20 @@ dsa_status dsa_topk_expand(const float* scores, const uint8_t* cand, int Q, int 
                            const int32_t* q_req, int kpool, int out_width, int flags,
                            int32_t* sel, int32_t* tok, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Measurement: the HBM read lane   [stkernel pull request #290, its
+ *     measurement ledger: a bandwidth-bound kernel is compared with the rate
+ *     of a plain streaming kernel on the same part, and counts as at the
+ *     bandwidth floor at 90 % of it or more]
+ *
+ * dsa_lane_read: reads `bytes` bytes at src (device memory, 16-byte aligned)
+ * once with coalesced 16-byte loads; writes at most one word to sink (device,
+ * 4 bytes) and only for a value no ordinary fill produces.  Its duration over
+ * `bytes` is the lane.  Errors: INVALID_ARG for bytes not a multiple of 16 or
+ * NULL pointers with bytes > 0.
+ * ------------------------------------------------------------------------- */
+dsa_status dsa_lane_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -51,6 +51,7 @@ _SIGS = {
     "dsa_gate_compress": (_I, [_P, _P, _I, _I, _I, _P, _Z, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                _F, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P]),
     "dsa_write_geom": (_I, [_P, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P]),
+    "dsa_lane_read": (_I, [_P, _Z, _P, _P]),
     "dsa_indexer_store": (_I, [_P, _P, _P, _P, _P, _P, _F, _I, _I, _P, _P, _P, _P]),
     "dsa_gate_compress_live": (_I, [_P, _P, _I, _I, _I, _P, _Z, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     _P, _P, _I, _F, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
@@ -356,3 +357,11 @@ def dsa_gate_compress_live(hidden, W, gate_part, k, gate, ape, valid, tok_off, p
         _dev(pool_start, _I32, "pool_start"), _dev(pool_valid, _U8, "pool_valid"),
         _dev(n_pools, _I32, "n_pools"), _dev(q_req, _I32, "q_req"), _dev(q_pos, _I32, "q_pos"),
         _dev(new_from, _I32, "new_from"), _stream(stream)))
+
+
+def dsa_lane_read(src, sink, stream=None) -> None:
+    """The HBM read lane: one coalesced read of src (a contiguous GPU tensor)."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    _check(lib().dsa_lane_read(_P(src.data_ptr()), src.numel() * src.element_size(),
+                               _dev(sink, (torch.int32, torch.uint32), "sink"), _stream(stream)))

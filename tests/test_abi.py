@@ -17,7 +17,7 @@ NUL = ctypes.c_void_p(None)
 
 def test_exports_every_declared_function():
     names = dsa.header_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     import subprocess
     out = subprocess.run(["nm", "-D", "--defined-only", dsa.LIB_PATH], capture_output=True, text=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
@@ -233,3 +233,10 @@ def test_cache_write_errors():
     assert live(seq_len=NUL) == INV
     assert live(N=17) == INV
     assert live(part_bytes=4) == INV
+
+
+def test_lane_read_errors():
+    L = dsa.lib()
+    assert L.dsa_lane_read(FAKE, 17, FAKE, NUL) == INV
+    assert L.dsa_lane_read(NUL, 16, FAKE, NUL) == INV
+    assert L.dsa_lane_read(NUL, 0, NUL, NUL) == dsa.DSA_OK
