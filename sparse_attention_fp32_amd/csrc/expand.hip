@@ -36,7 +36,7 @@ DSA_EXPORT dsa_status dsa_expand_selection(const int32_t* sel, const int32_t* po
   DSA_REQUIRE((flags & ~1) == 0, DSA_ERR_INVALID_ARG, "dsa_expand_selection: unknown flags 0x%x",
               flags);
   DSA_REQUIRE((flags & 1) == 0, DSA_ERR_UNSUPPORTED,
-              "dsa_expand_selection: always_select_tail is not built");
+              "dsa_expand_selection: flag bit 0 is reserved (dsa_select_tail writes the tail)");
   DSA_REQUIRE(kpool >= 1 && kpool <= DSA_MAX_KPOOL, DSA_ERR_INVALID_ARG,
               "dsa_expand_selection: kpool=%d outside [1,%d]", kpool, DSA_MAX_KPOOL);
   DSA_REQUIRE(select_k >= 1, DSA_ERR_INVALID_ARG, "dsa_expand_selection: select_k=%d < 1",

@@ -404,7 +404,7 @@ DSA_EXPORT dsa_status dsa_topk_expand(const float* scores, const uint8_t* cand, 
   DSA_REQUIRE((flags & ~1) == 0, DSA_ERR_INVALID_ARG, "dsa_topk_expand: unknown flags 0x%x",
               flags);
   DSA_REQUIRE((flags & 1) == 0, DSA_ERR_UNSUPPORTED,
-              "dsa_topk_expand: always_select_tail is not built");
+              "dsa_topk_expand: flag bit 0 is reserved (dsa_select_tail writes the tail)");
   DSA_REQUIRE(kpool >= 1 && kpool <= DSA_MAX_KPOOL, DSA_ERR_INVALID_ARG,
               "dsa_topk_expand: kpool=%d outside [1,%d]", kpool, DSA_MAX_KPOOL);
   DSA_REQUIRE((long long)out_width >= (long long)select_k * kpool, DSA_ERR_INVALID_ARG,

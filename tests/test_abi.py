@@ -162,7 +162,7 @@ def test_fused_call_errors():
     assert te(out_width=15) == INV
     assert te(select_k=0) == INV
     assert te(kpool=9) == INV
-    assert te(flags=1) == UNS
+    assert te(flags=1) == UNS          # bit 0 reserved: dsa_select_tail writes the tail
     assert te(tok=NUL) == INV
 
 
