@@ -29,6 +29,12 @@ Readings of points the pages leave open (each repeated where it is used):
 * fp8 latent rows are OCP E4M3FN codes times one f32 scale per row.
 * a paged latent cache is a pool of equal pages; a [B, max_blocks] block
   table names the page of each request's block of page_rows logical rows.
+* a request's region may hold more rows than its live length; only the live
+  rows exist for the step.  A decode step's query sits at the newest live row,
+  and the step writes that row (its indexer row stored at a device-side
+  position and marked valid).
+* k_norm may instead be applied to each row when it is stored (the per-token
+  k_normed buffer); the pooled row then gets no LayerNorm.
 """
 from __future__ import annotations
 
