@@ -19,6 +19,9 @@
  *  - Every tensor pointer is a DEVICE pointer owned by the caller.  Arrays are
  *    dense, row-major, with the element types named in each comment; bf16
  *    values travel as uint16_t bit patterns, fp8 as uint8_t codes.
+ *  - Every tensor pointer (workspaces included) is 16-byte aligned, as
+ *    hipMalloc's and torch's allocations are; the kernels use 16-byte vector
+ *    accesses.  A misaligned pointer is INVALID_ARG.
  *  - The library never allocates, frees, synchronizes, or reads device memory
  *    on the host.  Each call validates its host arguments first and, if they
  *    are bad, returns an error before launching anything; otherwise it
@@ -79,11 +82,13 @@ const char* dsa_last_error(void);
  * M >= 0 (M = 0 is a no-op).  For M <= 16 (decode) every row gets its own
  * workgroup that spreads K over 1024 threads and adds the partial sums in a
  * fixed order, so the result is deterministic and the same bits for a row
- * whatever the batch.  For M > 16 one workgroup per 16 rows walks K.  No
+ * whatever the batch.  For M > 16 one workgroup per 16 rows splits K over
+ * 16 waves (fp32 MFMA when K % 16 == 0) and adds the waves' partial sums in
+ * a fixed order, so those rows are deterministic too.  No
  * workspace is needed at present (dsa_head_gate_workspace_size returns 0; ws
  * may be NULL).
- * Errors: INVALID_ARG for N outside [1,16], K < 1, M < 0, or a NULL pointer
- * with M > 0.
+ * Errors: INVALID_ARG for N outside [1,16], K < 1, M < 0, or a NULL or
+ * misaligned pointer with M > 0.
  * ------------------------------------------------------------------------- */
 size_t dsa_head_gate_workspace_size(int M, int K, int N);
 dsa_status dsa_head_gate(const float* hidden, const float* W, float* w, int M, int K, int N,

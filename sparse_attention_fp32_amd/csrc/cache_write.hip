@@ -96,6 +96,7 @@ DSA_EXPORT dsa_status dsa_write_geom(const int32_t* seq_len, int B, const int32_
                 bt_stride, page_rows, n_pages);
   if (B == 0) return DSA_OK;
   DSA_REQUIRE(seq_len && q_pos, DSA_ERR_INVALID_ARG, "dsa_write_geom: NULL tensor pointer");
+  DSA_REQUIRE_ALIGNED("dsa_write_geom", seq_len, block_table, q_req, q_pos, new_from, slot);
   write_geom_kernel<<<(B + 255) / 256, 256, 0, stream>>>(seq_len, B, block_table, bt_stride,
                                                           page_rows, n_pages, q_req, q_pos,
                                                           new_from, slot);
@@ -116,6 +117,8 @@ DSA_EXPORT dsa_status dsa_indexer_store(const uint16_t* k_new, const uint16_t* g
   if (B == 0) return DSA_OK;
   DSA_REQUIRE(k_new && gate_new && pos && tok_off && k && gate && valid, DSA_ERR_INVALID_ARG,
               "dsa_indexer_store: NULL tensor pointer");
+  DSA_REQUIRE_ALIGNED("dsa_indexer_store", k_new, gate_new, pos, tok_off, ln_w, ln_b, k, gate,
+                      valid);
   const int lpp = D / 8, per_wg = 256 / lpp;
   const dim3 grid((B + per_wg - 1) / per_wg);
 #define DSA_LAUNCH_STORE(LPP)                                                                  \

@@ -3,6 +3,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
+#include <stdint.h>
 #include <stdio.h>
 
 #include "dsa.h"
@@ -17,9 +18,22 @@ void clear_error();
 dsa_status check_launch(const char* what);
 bool trace_enabled();
 
+// True when every non-NULL pointer is 16-byte aligned (the kernels' vector
+// loads and stores need it).
+inline bool aligned16() { return true; }
+template <typename P, typename... R>
+inline bool aligned16(P p, R... rest) {
+  return ((uintptr_t)(const void*)p & 15u) == 0 && aligned16(rest...);
+}
+
 }  // namespace dsa
 
 #define DSA_REQUIRE(cond, code, ...)                  \
   do {                                                \
     if (!(cond)) return ::dsa::set_error(code, __VA_ARGS__); \
   } while (0)
+
+// INVALID_ARG unless every listed (non-NULL) tensor pointer is 16-byte aligned.
+#define DSA_REQUIRE_ALIGNED(who, ...)                                               \
+  DSA_REQUIRE(::dsa::aligned16(__VA_ARGS__), DSA_ERR_INVALID_ARG,                   \
+              "%s: a tensor pointer is not 16-byte aligned", who)

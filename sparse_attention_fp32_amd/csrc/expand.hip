@@ -48,6 +48,7 @@ DSA_EXPORT dsa_status dsa_expand_selection(const int32_t* sel, const int32_t* po
   if (Q == 0) return DSA_OK;
   DSA_REQUIRE(sel && pool_start && pool_off && q_req && tok, DSA_ERR_INVALID_ARG,
               "dsa_expand_selection: NULL tensor pointer");
+  DSA_REQUIRE_ALIGNED("dsa_expand_selection", sel, pool_start, pool_off, q_req, tok);
   dim3 grid((out_width + 255) / 256, Q);
   expand_kernel<<<grid, 256, 0, stream>>>(sel, pool_start, pool_off, q_req, select_k, kpool,
                                           out_width, tok);
@@ -110,6 +111,8 @@ DSA_EXPORT dsa_status dsa_select_tail(const uint8_t* valid, const int32_t* tok_o
   if (Q == 0 || kpool == 1) return DSA_OK;  // kpool 1: no tail slots
   DSA_REQUIRE(valid && tok_off && pool_start && pool_off && n_pools && q_req && q_pos && tok,
               DSA_ERR_INVALID_ARG, "dsa_select_tail: NULL tensor pointer");
+  DSA_REQUIRE_ALIGNED("dsa_select_tail", valid, tok_off, pool_start, pool_off, n_pools, q_req,
+                      q_pos, tok);
   tail_kernel<<<(Q + 63) / 64, 64, 0, stream>>>(valid, tok_off, pool_start, pool_off, n_pools,
                                                 q_req, q_pos, Q, kpool, select_k, out_width, tok);
   return dsa::check_launch("dsa_select_tail");

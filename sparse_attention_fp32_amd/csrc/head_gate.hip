@@ -9,11 +9,16 @@
 // reduce-scatter over the wave (17 ALU-latency lane exchanges leave lane l with
 // output j(l)),
 // then the 16 waves' sums added in wave order.  Deterministic, and the same
-// bits for a row whatever the batch.  Above 16 rows each workgroup owns 16 rows
-// and walks K through LDS tiles.
+// bits for a row whatever the batch.  Above 16 rows (prefill) each workgroup
+// owns 16 rows: a [16,K] x [K,16] product on fp32 MFMA (v_mfma_f32_16x16x4_f32,
+// fp32 products and sums) with the 16 waves splitting K and their 16x16
+// partials added in wave order; K not a multiple of 16 takes a plain LDS-tiled
+// loop.
 //
-// HBM-bound work (2 FLOP per 4-byte element of hidden), so this is plain fp32
-// VALU arithmetic, not MFMA.
+// Either way the work is HBM-bound (2 FLOP per 4-byte element of hidden): at
+// decode it is plain fp32 VALU arithmetic; at prefill the MFMA form only
+// replaces 16 VALU FMAs per element with one quarter of an MFMA, so that the
+// loop is nothing but loads in flight.
 #include "dsa_device.hpp"
 #include "dsa_host.hpp"
 
@@ -148,6 +153,64 @@ __global__ __launch_bounds__(256) void head_gate_rows_kernel(const float* __rest
   if (gm < M && n < N) w[(size_t)gm * N + n] = acc;
 }
 
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+
+constexpr int kGateWaves = 16;  // waves over K per workgroup (MFMA path)
+
+// 16 rows per workgroup (M > 16, K % 16 == 0).  MFMA 16x16x4 f32: lane l holds
+// A[l % 16][l / 16] = hidden[m0 + l % 16][k], B[l / 16][l % 16] = W[k][l % 16],
+// and D[4 (l / 16) + r][l % 16] in acc[r].  A float4 of a hidden row feeds four
+// MFMAs: for c < 4 the K index of lane group j is k0 + 4 j + c.  Wave wv takes
+// the 16-wide K steps [s0, s1).
+template <int U>  // K steps per loop pass, all loads of a pass in flight
+__global__ __launch_bounds__(kGateWaves * 64) void head_gate_mfma_kernel(
+    const float* __restrict__ hidden, const float* __restrict__ W, float* __restrict__ w, int M,
+    int K, int N) {
+  __shared__ f32x4_v s_red[kGateWaves][64];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int i = lane & 15, j = lane >> 4;
+  const int m0 = blockIdx.x * 16;
+  const float* hrow = hidden + (size_t)min(m0 + i, M - 1) * K;
+  const int nsteps = K / 16;
+  const int s0 = nsteps * wv / kGateWaves, s1 = nsteps * (wv + 1) / kGateWaves;
+  const int ncol = i < N ? i : N - 1;
+  const float bmask = i < N ? 1.f : 0.f;
+  f32x4_v acc = {0.f, 0.f, 0.f, 0.f};
+  for (int sb = s0; sb < s1; sb += U) {
+    float4 h[U];
+    float b[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int st = min(sb + u, s1 - 1);  // (steps past s1 are loaded and not used)
+      const int k0 = st * 16;
+      h[u] = *(const float4*)(hrow + k0 + 4 * j);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) b[u][c] = W[(size_t)(k0 + 4 * j + c) * N + ncol];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (sb + u < s1) {
+        const float hv[4] = {h[u].x, h[u].y, h[u].z, h[u].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(hv[c], b[u][c] * bmask, acc, 0, 0, 0);
+      }
+    }
+  }
+  s_red[wv][lane] = acc;
+  __syncthreads();
+  if (wv == 0) {
+    f32x4_v v = s_red[0][lane];
+#pragma unroll
+    for (int x = 1; x < kGateWaves; ++x) v += s_red[x][lane];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = m0 + 4 * j + r;
+      if (m < M && i < N) w[(size_t)m * N + i] = v[r];
+    }
+  }
+}
+
 }  // namespace
 
 DSA_EXPORT size_t dsa_head_gate_workspace_size(int M, int K, int N) {
@@ -167,12 +230,16 @@ DSA_EXPORT dsa_status dsa_head_gate(const float* hidden, const float* W, float* 
   DSA_REQUIRE(M >= 0, DSA_ERR_INVALID_ARG, "dsa_head_gate: M=%d < 0", M);
   if (M == 0) return DSA_OK;
   DSA_REQUIRE(hidden && W && w, DSA_ERR_INVALID_ARG, "dsa_head_gate: NULL tensor pointer");
+  DSA_REQUIRE_ALIGNED("dsa_head_gate", hidden, W, w, ws);
   if (dsa::trace_enabled()) fprintf(stderr, "[dsa] head_gate M=%d K=%d N=%d\n", M, K, N);
   if (M <= kRows)
     if (N == 16)
       head_gate_row_kernel<true><<<M, kRowThreads, 0, stream>>>(hidden, W, w, K, N);
     else
       head_gate_row_kernel<false><<<M, kRowThreads, 0, stream>>>(hidden, W, w, K, N);
+  else if (K % 16 == 0)
+    head_gate_mfma_kernel<8><<<(M + kRows - 1) / kRows, kGateWaves * 64, 0, stream>>>(hidden, W, w,
+                                                                                   M, K, N);
   else
     head_gate_rows_kernel<<<(M + kRows - 1) / kRows, 256, 0, stream>>>(hidden, W, w, M, K, N);
   return dsa::check_launch("dsa_head_gate");

@@ -158,6 +158,8 @@ dsa_status launch_scores(const uint16_t* qi, const float* w, int nslices, float*
   DSA_REQUIRE(qi && w && keys && pool_start && pool_valid && pool_off && n_pools && q_req &&
                   q_pos && scores && cand,
               DSA_ERR_INVALID_ARG, "%s: NULL tensor pointer", who);
+  DSA_REQUIRE_ALIGNED(who, qi, w, w_out, keys, pool_start, pool_valid, pool_off, n_pools, q_req,
+                      q_pos, scores, cand);
   dim3 grid((pstride + kPoolsPerWG - 1) / kPoolsPerWG, Q);
   DSA_REQUIRE(grid.y <= 65535u, DSA_ERR_UNSUPPORTED, "%s: Q=%d above 65535", who, Q);
   if (dsa::trace_enabled())

@@ -462,6 +462,8 @@ DSA_EXPORT dsa_status dsa_kpool_compress(const uint16_t* k, const uint16_t* gate
   DSA_REQUIRE(k && gate && ape && valid && tok_off && pool_off && keys && pool_start &&
                   pool_valid && n_pools,
               DSA_ERR_INVALID_ARG, "dsa_kpool_compress: NULL tensor pointer");
+  DSA_REQUIRE_ALIGNED("dsa_kpool_compress", k, gate, ape, valid, tok_off, pool_off, seq_len, ln_w,
+                      ln_b, new_from, keys, pool_start, pool_valid, n_pools);
   return launch_compress(k, gate, ape, valid, tok_off, pool_off, seq_len, ln_w, ln_b, eps, B, D,
                          kpool, max_cap, new_from, max_new, keys, pool_start, pool_valid,
                          n_pools, GateArgs{}, stream, "dsa_kpool_compress");
@@ -503,6 +505,9 @@ DSA_EXPORT dsa_status dsa_gate_compress(const float* hidden, const float* W, int
   DSA_REQUIRE(B == 0 || (k && gate && ape && valid && tok_off && pool_off && keys &&
                          pool_start && pool_valid && n_pools),
               DSA_ERR_INVALID_ARG, "dsa_gate_compress: NULL tensor pointer");
+  DSA_REQUIRE_ALIGNED("dsa_gate_compress", hidden, W, gate_part, k, gate, ape, valid, tok_off,
+                      pool_off, seq_len, ln_w, ln_b, new_from, keys, pool_start, pool_valid,
+                      n_pools);
   const int ns = gate_slices(M, K);
   if (M > 0 && ns == 1) {  // dense head-gate: the partials buffer receives w
     const dsa_status g = dsa_head_gate(hidden, W, gate_part, M, K, N, nullptr, 0, stream);
@@ -546,6 +551,9 @@ DSA_EXPORT dsa_status dsa_gate_compress_live(
                          gate_new && keys && pool_start && pool_valid && n_pools && q_req &&
                          q_pos && new_from),
               DSA_ERR_INVALID_ARG, "dsa_gate_compress_live: NULL tensor pointer");
+  DSA_REQUIRE_ALIGNED("dsa_gate_compress_live", hidden, W, gate_part, k, gate, ape, valid, tok_off,
+                      pool_off, seq_len, k_new, gate_new, ln_w, ln_b, keys, pool_start, pool_valid,
+                      n_pools, q_req, q_pos, new_from);
   const LiveArgs la{k_new, gate_new, normed_rows != 0, ln_w, ln_b, q_req, q_pos, new_from};
   const float* pw = normed_rows ? nullptr : ln_w;  // LayerNorm after pooling
   const float* pb = normed_rows ? nullptr : ln_b;

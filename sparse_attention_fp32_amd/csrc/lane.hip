@@ -48,6 +48,7 @@ DSA_EXPORT dsa_status dsa_lane_read(const void* src, size_t bytes, uint32_t* sin
               bytes);
   if (bytes == 0) return DSA_OK;
   DSA_REQUIRE(src && sink, DSA_ERR_INVALID_ARG, "dsa_lane_read: NULL pointer");
+  DSA_REQUIRE_ALIGNED("dsa_lane_read", src, sink);
   lane_read_kernel<<<kLaneWG, 256, 0, stream>>>((const uint4*)src, bytes / 16, sink);
   return dsa::check_launch("dsa_lane_read");
 }

@@ -539,6 +539,8 @@ dsa_status launch_mla(const uint16_t* q, const void* ckv, const float* ckv_scale
   DSA_REQUIRE(q && ckv && (paged ? cm.block_table != nullptr : cm.kv_off != nullptr) && q_req &&
                   tok && out,
               DSA_ERR_INVALID_ARG, "%s: NULL tensor pointer", who);
+  DSA_REQUIRE_ALIGNED(who, q, ckv, ckv_scale, cm.kv_off, cm.block_table, cm.kvidx, q_req, tok, out,
+                      lse, ws);
   const size_t need = dsa_sparse_mla_decode_workspace_size(Q, Hm, L_, out_width, latent_dtype);
   DSA_REQUIRE(ws_bytes >= need && (need == 0 || ws), DSA_ERR_INVALID_ARG,
               "%s: workspace %zu bytes, need %zu", who, ws_bytes, need);

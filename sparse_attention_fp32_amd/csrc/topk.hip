@@ -388,6 +388,7 @@ DSA_EXPORT dsa_status dsa_topk_pools(const float* scores, const uint8_t* cand, i
               "dsa_topk_pools: pstride=%d above %d", pstride, DSA_MAX_TOPK_ROW);
   if (Q == 0) return DSA_OK;
   DSA_REQUIRE(scores && cand && sel, DSA_ERR_INVALID_ARG, "dsa_topk_pools: NULL tensor pointer");
+  DSA_REQUIRE_ALIGNED("dsa_topk_pools", scores, cand, sel, ws);
   return launch_topk<false>(scores, cand, Q, pstride, select_k, sel, ExpandArgs{}, stream);
 }
 
@@ -413,6 +414,7 @@ DSA_EXPORT dsa_status dsa_topk_expand(const float* scores, const uint8_t* cand, 
   if (Q == 0) return DSA_OK;
   DSA_REQUIRE(scores && cand && sel && pool_start && pool_off && q_req && tok,
               DSA_ERR_INVALID_ARG, "dsa_topk_expand: NULL tensor pointer");
+  DSA_REQUIRE_ALIGNED("dsa_topk_expand", scores, cand, pool_start, pool_off, q_req, sel, tok);
   return launch_topk<true>(scores, cand, Q, pstride, select_k, sel,
                            ExpandArgs{pool_start, pool_off, q_req, kpool, out_width, tok}, stream);
 }

@@ -331,6 +331,13 @@ def make_paged_cache(x: Inputs, page_rows: int, seed: int = 0, spare_pages: int 
                       page_rows=page_rows)
 
 
+def gate_operands(M: int, K: int, N: int, seed: int = 0):
+    """hidden [M,K] and W [K,N] (f32) drawn as make_inputs draws them, for
+    head-gate shapes outside the named workloads."""
+    s = _Streams(seed, "cpu")
+    return s.normal((M, K)), s.normal((K, N), std=1.0 / math.sqrt(K))
+
+
 def random_selection(spec: Spec, seed: int = 0, holes: float = 0.1) -> torch.Tensor:
     """A selection row per query for running the attention stage on its own:
     distinct request-local ids drawn uniformly from the query's request, in

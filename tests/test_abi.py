@@ -13,6 +13,11 @@ pytestmark = pytest.mark.skipif(not os.path.exists(dsa.LIB_PATH), reason="libdsa
 INV, UNS = dsa.DSA_ERR_INVALID_ARG, dsa.DSA_ERR_UNSUPPORTED
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case fails validation first
 NUL = ctypes.c_void_p(None)
+MIS = ctypes.c_void_p(0x1004)    # a pointer that is not 16-byte aligned
+
+
+def _misaligned(code):
+    return code == INV and "16-byte aligned" in dsa.last_error()
 
 
 def test_exports_every_declared_function():
@@ -39,6 +44,7 @@ def test_head_gate_errors():
     assert L.dsa_head_gate(FAKE, FAKE, FAKE, 4, 0, 16, NUL, 0, NUL) == INV
     assert L.dsa_head_gate(FAKE, FAKE, FAKE, -1, 16, 16, NUL, 0, NUL) == INV
     assert L.dsa_head_gate(NUL, FAKE, FAKE, 4, 4096, 16, FAKE, 1 << 20, NUL) == INV
+    assert _misaligned(L.dsa_head_gate(FAKE, MIS, FAKE, 40, 4096, 16, NUL, 0, NUL))
     # no workspace is needed on either path
     assert dsa.head_gate_workspace_size(16, 4096, 16) == 0
     assert dsa.head_gate_workspace_size(4096, 4096, 16) == 0
@@ -63,6 +69,7 @@ def test_kpool_compress_errors():
     assert _compress(max_cap=-1) == INV
     assert _compress(new_from=FAKE, max_new=0) == INV
     assert _compress(k=NUL) == INV
+    assert _misaligned(_compress(k=MIS))
     assert _compress(ln_w=NUL) == INV             # both LayerNorm vectors, or neither
     assert "both" in dsa.last_error()
     assert _compress(B=0) == dsa.DSA_OK
@@ -80,6 +87,7 @@ def test_index_scores_errors():
     assert call(pstride=0) == INV
     assert call(Q=-2) == INV
     assert call(qi=NUL) == INV
+    assert _misaligned(call(qi=MIS))
     assert call(Q=0) == dsa.DSA_OK
 
 
@@ -89,6 +97,7 @@ def test_topk_errors():
     assert L.dsa_topk_pools(FAKE, FAKE, 4, 0, 8, FAKE, NUL, 0, NUL) == INV
     assert L.dsa_topk_pools(FAKE, FAKE, 4, dsa.MAX_TOPK_ROW + 1, 8, FAKE, NUL, 0, NUL) == UNS
     assert L.dsa_topk_pools(NUL, FAKE, 4, 100, 8, FAKE, NUL, 0, NUL) == INV
+    assert _misaligned(L.dsa_topk_pools(FAKE, MIS, 4, 100, 8, FAKE, NUL, 0, NUL))
     assert dsa.topk_pools_workspace_size(16, 8192, 512) == 0
 
 
@@ -104,6 +113,7 @@ def test_expand_errors():
     assert call(flags=1) == UNS          # always_select_tail: not built
     assert call(flags=2) == INV
     assert call(sel=NUL) == INV
+    assert _misaligned(call(sel=MIS))
 
 
 def test_sparse_mla_errors():
@@ -122,6 +132,8 @@ def test_sparse_mla_errors():
     assert need > 0
     assert call(ws=FAKE, wsb=need - 1) == INV
     assert call(q=NUL, ws=FAKE, wsb=need) == INV
+    assert _misaligned(call(q=MIS, ws=FAKE, wsb=need))
+    assert _misaligned(call(ws=MIS, wsb=need))
     assert call(Q=0) == dsa.DSA_OK
 
 
@@ -146,6 +158,7 @@ def test_fused_call_errors():
     assert "need" in dsa.last_error()
     assert gc(kpool=9) == INV
     assert gc(hidden=NUL) == INV
+    assert _misaligned(gc(hidden=MIS))
     assert gc(M=0, B=0) == dsa.DSA_OK
 
     def sg(nslices=32, H=16, Q=3):
@@ -154,6 +167,8 @@ def test_fused_call_errors():
     assert sg(nslices=0) == INV
     assert sg(nslices=65) == INV
     assert sg(H=17) == INV
+    assert _misaligned(L.dsa_index_scores_gated(FAKE, MIS, 32, NUL, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                FAKE, FAKE, 3, 16, 128, 4, 100, FAKE, FAKE, NUL))
     assert sg(Q=0) == dsa.DSA_OK
 
     def te(select_k=4, kpool=4, out_width=16, flags=0, tok=FAKE):
@@ -164,6 +179,7 @@ def test_fused_call_errors():
     assert te(kpool=9) == INV
     assert te(flags=1) == UNS          # bit 0 reserved: dsa_select_tail writes the tail
     assert te(tok=NUL) == INV
+    assert _misaligned(te(tok=MIS))
 
 
 def test_select_tail_errors():
@@ -178,6 +194,7 @@ def test_select_tail_errors():
     assert call(select_k=0) == INV
     assert call(Q=-1) == INV
     assert call(tok=NUL) == INV
+    assert _misaligned(call(tok=MIS))
     assert call(Q=0) == dsa.DSA_OK
     assert call(kpool=1, out_width=2) == dsa.DSA_OK   # kpool 1 has no tail slots
 
@@ -196,6 +213,7 @@ def test_sparse_mla_paged_errors():
     assert call(n_pages=0) == INV
     assert call(n_pages=1 << 20, page_rows=4096) == UNS     # 2^32 rows
     assert call(bt=NUL) == INV
+    assert _misaligned(call(bt=MIS))
     assert call(wsb=need - 1) == INV
     assert call(Q=0) == dsa.DSA_OK
 
@@ -210,6 +228,7 @@ def test_cache_write_errors():
     assert "block table" in dsa.last_error()
     assert geom(slot=FAKE, bt=FAKE, bt_stride=4, page_rows=0, n_pages=3) == INV
     assert geom(seq_len=NUL) == INV
+    assert _misaligned(geom(seq_len=MIS))
     assert geom(B=0) == dsa.DSA_OK
 
     def store(B=2, D=128, ln_w=NUL, ln_b=NUL, pos=FAKE, eps=1e-5):
@@ -219,6 +238,7 @@ def test_cache_write_errors():
     assert store(ln_w=FAKE) == INV
     assert store(eps=-1.0) == INV
     assert store(pos=NUL) == INV
+    assert _misaligned(store(pos=MIS))
     assert store(B=-1) == INV
     assert store(B=0) == dsa.DSA_OK
 
@@ -231,6 +251,7 @@ def test_cache_write_errors():
     assert live(ln_w=NUL) == INV
     assert live(kpool=9) == INV
     assert live(seq_len=NUL) == INV
+    assert _misaligned(live(seq_len=MIS))
     assert live(N=17) == INV
     assert live(part_bytes=4) == INV
 
@@ -239,4 +260,5 @@ def test_lane_read_errors():
     L = dsa.lib()
     assert L.dsa_lane_read(FAKE, 17, FAKE, NUL) == INV
     assert L.dsa_lane_read(NUL, 16, FAKE, NUL) == INV
+    assert _misaligned(L.dsa_lane_read(MIS, 16, FAKE, NUL))
     assert L.dsa_lane_read(NUL, 0, NUL, NUL) == dsa.DSA_OK

@@ -70,6 +70,26 @@ def test_head_gate_repeat_keeps_workspace_clean(case):
     assert int(st.ws_gate[:4].view(torch.int32).item() if st.ws_gate.numel() >= 4 else 0) == 0
 
 
+# (M, K, N): row path at its upper bound, MFMA path with ragged row tiles, waves
+# left without K steps, N < 16 and N = 1, and the LDS path (K % 16 != 0)
+GATE_SHAPES = [(16, 4096, 16), (17, 16, 16), (33, 48, 7), (100, 4096, 16), (63, 2064, 1),
+               (40, 1000, 16), (20, 4104, 5)]
+
+
+@pytest.mark.parametrize("M,K,N", GATE_SHAPES)
+def test_head_gate_shapes(M, K, N):
+    _need_gpu()
+    from sparse_attention_fp32_amd import dsa
+    _say(f"head_gate shape M={M} K={K} N={N}")
+    h, Wm = W.gate_operands(M, K, N, seed=M * 7 + N)
+    w = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    _poison(w)
+    ws = torch.zeros(max(1, dsa.head_gate_workspace_size(M, K, N)), dtype=torch.uint8,
+                     device="cuda")
+    dsa.dsa_head_gate(h.cuda(), Wm.cuda(), w, ws)
+    PT.check_gate(_np(w), O.head_gate(h.numpy(), Wm.numpy()))
+
+
 def test_kpool_compress(case):
     spec, xn, ref, xg = case
     _say(f"kpool_compress {spec.name}")
