@@ -41,17 +41,6 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// OCP fp8 E4M3FN code -> bf16 bits, exact (every E4M3 value, subnormals
-// included, is a bf16 value).  Normal codes move their exponent from bias 7 to
-// bias 127; subnormal codes m * 2^-9 are formed as 2^-6 * (1 + m/8) - 2^-6.
-__device__ __forceinline__ uint32_t fp8e4m3_to_bf16(uint32_t code) {
-  uint32_t em = code & 0x7fu;
-  bool sub = em < 8u;
-  uint32_t bits = (em << 20) + ((sub ? 121u : 120u) << 23);
-  float f = __uint_as_float(bits) - (sub ? 0.015625f : 0.0f);
-  return (__float_as_uint(f) >> 16) | ((code & 0x80u) << 8);
-}
-
 // Order-preserving map of a finite float to an unsigned key (larger float ->
 // larger key); -0 is mapped like +0.
 __device__ __forceinline__ uint32_t float_order_key(float f) {

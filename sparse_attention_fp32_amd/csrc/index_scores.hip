@@ -23,7 +23,8 @@ namespace {
 using namespace dsa;
 
 constexpr int kTiles = 4;                  // 16-pool tiles per wave
-constexpr int kPoolsPerWG = 4 * kTiles * 16;  // 4 waves
+constexpr int kPoolsPerWG = 4 * kTiles * 16;  // 4 waves (= 256, one slot per thread)
+static_assert(kPoolsPerWG == 256, "the sentinel-only path gives each thread one slot");
 
 constexpr int kMaxGateSlices = 64;  // 16 slice groups x 4 per thread
 
@@ -55,7 +56,19 @@ __global__ __launch_bounds__(256) void index_scores_kernel(
   const int P = n_pools[r];
   const int64_t base = pool_off[r];
   const int qp = q_pos[q];
-  const int tile0 = blockIdx.x * kPoolsPerWG + wave * (kTiles * 16);
+  const int wg0 = blockIdx.x * kPoolsPerWG;
+  const int tile0 = wg0 + wave * (kTiles * 16);
+  // A workgroup past the request's last pool (ragged batches: the row is as
+  // long as the longest request's) writes its slots' sentinels and leaves,
+  // unless it is the one that stores w.
+  if (wg0 >= P && !(GATED && w_out && blockIdx.x == 0)) {
+    const int p = wg0 + (int)threadIdx.x;  // kPoolsPerWG == blockDim.x
+    if (p < pstride) {
+      scores[(int64_t)q * pstride + p] = -INFINITY;
+      cand[(int64_t)q * pstride + p] = 0;
+    }
+    return;
+  }
 
   // Key rows: the long-latency HBM stream.  Every load is issued, unconditional
   // and together: pool indices are clamped to the request's last pool (a

@@ -41,23 +41,76 @@ namespace {
 
 using namespace dsa;
 
-// First valid row of a request (request-local), or -1.  The whole workgroup
-// scans 4 KiB windows (16 bytes per thread, all loads issued together with
-// clamped addresses) and stops at the first window holding a valid byte.
+// First valid row of a request (request-local), or -1.
+//
+// The request's bytes valid[row0, row0 + T) are read as the 16-byte chunks of
+// the array that hold them (the array starts 16-byte aligned).  Bytes of a
+// chunk outside the request are masked off; the chunk holding the request's
+// last byte is read byte by byte with clamped addresses, and lanes past it
+// read kScanPad, so no access passes the request's end (the array may end
+// there).  Rounds of 256 * U chunks, all loads of a round in flight: a first
+// round of 4 KiB (a request that starts valid is found at once), then 16 KiB
+// rounds (wider rounds cost the kernel a wave of occupancy at kpool 4), so
+// left padding of 64 Ki rows costs five round trips rather than sixteen.
+__device__ uint4 kScanPad;
+__device__ __forceinline__ uint64_t nz_bytes(uint32_t lo, uint32_t hi) {
+  // bit 8i+7 set for each nonzero byte i of the 8 bytes lo | hi << 32
+  const uint32_t a = (((lo & 0x7f7f7f7fu) + 0x7f7f7f7fu) | lo) & 0x80808080u;
+  const uint32_t b = (((hi & 0x7f7f7f7fu) + 0x7f7f7f7fu) | hi) & 0x80808080u;
+  return a | (uint64_t)b << 32;
+}
+__device__ __forceinline__ uint64_t bytes_below(int n) {  // bytes [0, n) of 8
+  return n <= 0 ? 0ull : n >= 8 ? ~0ull : (1ull << (8 * n)) - 1;
+}
+
+template <int U>
+__device__ int scan_round(const uint4* __restrict__ vc, int64_t jb, int64_t j1,
+                          uint4 last, int64_t row0, int64_t end) {
+  const int t = threadIdx.x;
+  uint4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t j = jb + u * 256 + t;
+    v[u] = *(j < j1 ? vc + j : &kScanPad);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t j = jb + u * 256 + t;
+    if (j > j1) break;
+    const uint4 c = j == j1 ? last : v[u];
+    const int lo = (int)max(row0 - 16 * j, (int64_t)0), hi = (int)min(end - 16 * j, (int64_t)16);
+    const uint64_t m0 = nz_bytes(c.x, c.y) & bytes_below(hi) & ~bytes_below(lo);
+    const uint64_t m1 = nz_bytes(c.z, c.w) & bytes_below(hi - 8) & ~bytes_below(lo - 8);
+    if (m0 | m1) {
+      const int i = m0 ? __builtin_ctzll(m0) >> 3 : 8 + (__builtin_ctzll(m1) >> 3);
+      return (int)(16 * j + i - row0);
+    }
+  }
+  return INT_MAX;
+}
+
 __device__ int first_valid_row(const uint8_t* __restrict__ valid, int64_t row0, int T,
                                int* s_first) {
   const int t = threadIdx.x;
   if (t == 0) *s_first = INT_MAX;
   __syncthreads();
-  for (int base = 0; base < T; base += 256 * 16) {
-    const int lo = base + t * 16;
-    uint8_t b[16];
+  if (T <= 0) return -1;
+  const int64_t end = row0 + T;
+  const int64_t j0 = row0 >> 4, j1 = (end - 1) >> 4;  // chunks holding the request's bytes
+  uint8_t lb[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) b[i] = valid[row0 + min(lo + i, T - 1)];
-    int found = INT_MAX;
+  for (int i = 0; i < 16; ++i) lb[i] = valid[min(16 * j1 + i, end - 1)];
+  uint32_t lw[4];
 #pragma unroll
-    for (int i = 15; i >= 0; --i)
-      if (lo + i < T && b[i]) found = lo + i;
+  for (int w = 0; w < 4; ++w)
+    lw[w] = lb[4 * w] | lb[4 * w + 1] << 8 | lb[4 * w + 2] << 16 | (uint32_t)lb[4 * w + 3] << 24;
+  const uint4 last = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  const uint4* vc = (const uint4*)valid;
+  for (int64_t jb = j0; jb <= j1;) {
+    const bool first = jb == j0;
+    const int found = first ? scan_round<1>(vc, jb, j1, last, row0, end)
+                            : scan_round<4>(vc, jb, j1, last, row0, end);
+    jb += first ? 256 : 256 * 4;
     if (found != INT_MAX) atomicMin(s_first, found);
     __syncthreads();
     const int cur = *s_first;

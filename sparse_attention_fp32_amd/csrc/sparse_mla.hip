@@ -25,10 +25,11 @@
 //  * PV: O[32 heads x its 128 dims] += P . C_slice, the B operand read from
 //    the wave's own slice in LDS (16 bytes = 8 dims per row per lane,
 //    regrouped into 8 operands, so each lane owns 8 consecutive output dims).
-// fp8 rows are widened to bf16 exactly in registers; the row scale multiplies
-// the logits and the probabilities instead of the data.  With more than one
-// chunk, per-chunk (max, sum) pairs and unnormalised O (bf16) go to the
-// workspace and mla_combine_kernel merges them in chunk order.
+// fp8 rows are widened to bf16 exactly in registers (the hardware conversion);
+// the row scale multiplies the logits and the probabilities instead of the
+// data.  With more than one chunk, per-chunk (max, sum) pairs and unnormalised
+// O (bf16) go to the workspace and mla_combine_kernel merges them in chunk
+// order.
 //
 // Paged cache (dsa_sparse_mla_decode_paged): the same kernel with the chunk's
 // ids mapped to physical rows in the prologue.  The request's block-table row
@@ -85,17 +86,21 @@ __device__ __forceinline__ uint32_t lo_pair(uint32_t x, uint32_t y) {
 __device__ __forceinline__ uint32_t hi_pair(uint32_t x, uint32_t y) {
   return (x >> 16) | (y & 0xffff0000u);
 }
-// 8 fp8 codes -> 8 bf16 (exact)
+// 8 fp8 codes -> 8 bf16, in byte order, by the hardware conversion with a unit
+// scale: exact (every E4M3 value, subnormals included, is a bf16 value); the
+// NaN codes give NaN.  Word select 0 takes bytes 0-1 of a dword, 1 bytes 2-3.
 __device__ __forceinline__ uint4 widen_fp8x8(uint2 v) {
-  uint32_t o[4];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const uint32_t w = k ? v.y : v.x;
-    o[2 * k] = fp8e4m3_to_bf16(w & 0xffu) | (fp8e4m3_to_bf16((w >> 8) & 0xffu) << 16);
-    o[2 * k + 1] = fp8e4m3_to_bf16((w >> 16) & 0xffu) | (fp8e4m3_to_bf16(w >> 24) << 16);
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false);
+  const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true);
+  const auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false);
+  const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
 }
+
+// Read as the scale of a slot with no id (zero; global memory, so the load
+// stays a plain global load).
+__device__ float kNoScale;
 
 template <bool FP8>
 struct RowSlice;  // registers holding one lane's share of a sub-chunk's rows
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
   // a ring of kPF row sets: sub-chunk s is gathered into slot s mod kPF, kPF
   // sub-chunks ahead of its use; past the last sub-chunk every slot is empty
   RowSlice<FP8> ring[kPF];
-  float rscl[kPF][2];  // row scales of tokens col, 16 + col (wave 0, lanes < 16)
+  float rscl[kPF][2];  // row scales of tokens col, 16 + col (used by wave 0, lanes < 16)
   auto gather = [&](int s, RowSlice<FP8>& cr, float (&scl)[2]) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -236,11 +241,10 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
         else
           ((uint4*)cr.v[tt])[kk] = *(const uint4*)(src + 2 * d);
       }
-      if (FP8 && t < 16) {
-        const float* sp = id >= 0 ? ckv_scale + rowbase + id : (const float*)dummy;
-        const float v = *sp;
-        scl[tt] = id >= 0 ? v : 0.f;
-      }
+      // the row scale (0 for no id) by a pointer select, so that nothing
+      // consumes the loaded value here (a select on it would wait for every
+      // load in flight, the rows just issued included)
+      if (FP8) scl[tt] = *(id >= 0 ? ckv_scale + rowbase + id : &kNoScale);
     }
   };
 #pragma unroll
@@ -443,13 +447,14 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
 
 // Merge the per-chunk partials of one (query, head) in chunk order; a wave per
 // head, 8 dims per lane, four heads per workgroup.  All chunks' loads of a
-// batch are issued before any is used.
+// batch are issued before any is used; the batch is the smallest of 4, 8, 16
+// that holds every chunk (up to 16), so no load repeats a chunk needlessly.
+template <int kBatch>
 __global__ __launch_bounds__(256) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
                                                           int nchunks, int Hm,
                                                           uint16_t* __restrict__ out,
                                                           float* __restrict__ lse) {
-  constexpr int kBatch = 16;
   const int h = blockIdx.x * 4 + (threadIdx.x >> 6), qx = blockIdx.y, lane = threadIdx.x & 63;
   if (h >= Hm) return;
   const int64_t b0 = (int64_t)qx * nchunks * Hm + h;
@@ -569,7 +574,13 @@ dsa_status launch_mla(const uint16_t* q, const void* ckv, const float* ckv_scale
 #undef DSA_LAUNCH_MLA
   dsa_status st = dsa::check_launch(who);
   if (st != DSA_OK || ch.nchunks == 1) return st;
-  mla_combine_kernel<<<dim3((Hm + 3) / 4, Q), 256, 0, stream>>>(part_o, part_ml, ch.nchunks, Hm, out, lse);
+  const dim3 cgrid((Hm + 3) / 4, Q);
+  if (ch.nchunks <= 4)
+    mla_combine_kernel<4><<<cgrid, 256, 0, stream>>>(part_o, part_ml, ch.nchunks, Hm, out, lse);
+  else if (ch.nchunks <= 8)
+    mla_combine_kernel<8><<<cgrid, 256, 0, stream>>>(part_o, part_ml, ch.nchunks, Hm, out, lse);
+  else
+    mla_combine_kernel<16><<<cgrid, 256, 0, stream>>>(part_o, part_ml, ch.nchunks, Hm, out, lse);
   return dsa::check_launch(who);
 }
 

@@ -130,6 +130,50 @@ def test_kpool_compress_incremental(case):
     PT.check_compress(g, ref2)
 
 
+# Left padding that the first-valid-row scan must cross in several rounds, at
+# every alignment of the request's first row: 2 valid rows after 39998 padding
+# rows, a request with no valid row, one of a single row, a first valid row on
+# a 4 KiB boundary, and short requests inside one 16-byte chunk.
+EDGE_PADS = W.Spec("scan_edges", lengths=[40000, 21000, 20, 16, 1, 4100, 7, 33, 5],
+                   pads=[39998, 20485, 19, 16, 0, 4096, 3, 0, 4], kpool=4, index_heads=4,
+                   index_dim=128, hidden=256, select_k=4, out_width=16, mla_heads=8)
+
+
+@pytest.mark.parametrize("live", [False, True])
+def test_kpool_compress_first_valid_edges(live):
+    """Full compression, then the incremental call (whose scan runs where no
+    cached pool gives the first valid row), against the oracle; with live
+    lengths that end the scan inside the padding of some requests."""
+    _need_gpu()
+    spec = EDGE_PADS
+    _say(f"kpool_compress first-valid edges live={live}")
+    x = W.make_inputs(spec, seed=3)
+    xn = x.numpy()
+    xg = x.to("cuda")
+    st = _step(xg)
+    seq = None
+    if live:
+        seq = np.array([39999, 20490, 20, 16, 1, 4096, 5, 33, 4], dtype=np.int32)
+        st.seq_len = torch.from_numpy(seq).cuda()
+    ref = O.kpool_compress(xn["k"], xn["gate"], xn["ape"], xn["valid"], xn["tok_off"],
+                           xn["pool_off"], xn["ln_w"], xn["ln_b"], spec.eps, spec.kpool,
+                           seq_len=seq)
+    ncap = int(xn["pool_off"][-1])
+
+    def got():
+        return {"keys": _np(st.keys).view(np.uint16)[:ncap], "pool_start": _np(st.pool_start)[:ncap],
+                "pool_valid": _np(st.pool_valid)[:ncap], "n_pools": _np(st.n_pools)}
+    for t in (st.keys, st.pool_start, st.pool_valid, st.n_pools):
+        _poison(t)
+    st.compress()
+    PT.check_compress(got(), ref)
+    if live:
+        xg.new_from.copy_(torch.from_numpy(np.maximum(seq - 1, 0)))
+    _poison(st.n_pools)
+    st.compress(incremental=True)
+    PT.check_compress(got(), ref)
+
+
 @pytest.mark.parametrize("fused", [False, True])
 def test_kpool_compress_incremental_multi(case, fused):
     """A step that rewrote the last kpool+1 rows of every request: several
@@ -243,6 +287,32 @@ def test_mla_isolated(case):
     st.mla()
     worst = PT.check_mla(_np(st.out), _np(st.lse), ref["out_f64"], ref["lse"])
     _say(f"MLA worst rel err {worst:.3g}")
+
+
+def test_mla_fp8_every_code():
+    """fp8 latent rows holding every finite E4M3 code (subnormals, both zeros,
+    448) in every lane position: the attention against the oracle's decode of
+    the same codes."""
+    _need_gpu()
+    spec = W.spec_by_name("medium_fp8")
+    _say("sparse_mla fp8 every code")
+    x = W.make_inputs(spec, seed=5)
+    T, L = x.ckv.shape
+    codes = (np.arange(T * L, dtype=np.int64).reshape(T, L) * 7 + np.arange(T)[:, None]) % 256
+    codes[(codes & 0x7F) == 0x7F] = 0          # the two NaN codes
+    x.ckv.copy_(torch.from_numpy(codes.astype(np.uint8)))
+    xn = x.numpy()
+    tok = W.random_selection(spec, seed=5)
+    xg = x.to("cuda")
+    st = _step(xg)
+    st.tok.copy_(tok)
+    _poison(st.out)
+    _poison(st.lse)
+    st.mla()
+    want = O.sparse_mla_decode(xn["q_mla"], xn["ckv"], xn["ckv_scale"], xn["kv_off"], xn["q_req"],
+                               tok.numpy(), spec.sm_scale)
+    worst = PT.check_mla(_np(st.out), _np(st.lse), want["out_f64"], want["lse"])
+    _say(f"MLA fp8 every code worst rel err {worst:.3g}")
 
 
 def test_chain(case):
