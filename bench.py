@@ -9,9 +9,11 @@ calls (gate+compress, gated index scores, top-k+expand, sparse MLA) over one bat
 resident synthetic input: the 32K-context decode batch (16 requests x 32768
 cached rows, one query each) by default.  Eight input sets (each larger than
 the 256 MB last-level cache together with its outputs) are rotated so that
-every step streams its keys and latent rows from HBM.  Each set's calls are
-captured once in a HIP graph; the timed region replays K graphs.  The same
-graphs are also replayed with two batches in flight (two streams), which
+every step streams its keys and latent rows from HBM.  The eight sets' steps
+are captured in sequence in one HIP graph, as a serving loop captures
+consecutive decode steps; the timed region replays it K/8 times (a remainder
+replays single-step graphs), so K steps run.  Single-step graphs (one per
+set) are timed too, and replayed with two batches in flight (two streams), which
 shows how much of the step is fixed latency rather than throughput.  The same
 step through the six separate calls is timed too, for comparison, and the
 step with the attention reading a paged copy of the latent cache (64-row pages
@@ -211,6 +213,36 @@ def main():
         torch.cuda.synchronize()
         return graphs
 
+    def capture_seq(fn):
+        """One graph over every set's step, in set order."""
+        for st in steps:
+            fn(st)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for st in steps:
+                fn(st)
+        torch.cuda.synchronize()
+        return g
+
+    def timed_seq(gseq, singles, n, warm):
+        """n steps: n // len(singles) replays of the sequence graph, then the
+        remainder as single-step graphs."""
+        k = len(singles)
+        for _ in range(max(1, warm // k)):
+            gseq.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n // k):
+            gseq.replay()
+        for i in range(n % k):
+            singles[i].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1), time.perf_counter() - t0
+
     def timed(graphs, n, warm):
         for i in range(warm):
             graphs[i % len(graphs)].replay()
@@ -226,8 +258,10 @@ def main():
 
     # the step: the fused decode calls over cached pools
     graphs = capture(lambda st: st.run_fused(incremental=True))
-    ms, wall = timed(graphs, a.steps, a.warmup)
+    gseq = capture_seq(lambda st: st.run_fused(incremental=True))
+    ms, wall = timed_seq(gseq, graphs, a.steps, a.warmup)
     ms_per_step = ms / a.steps
+    ms1, _ = timed(graphs, a.steps, a.warmup)  # the same steps as single-step graphs
     qps = spec.Q * a.steps / (ms / 1e3)
     # the same step graphs with two batches in flight: set i replays on side
     # stream i mod 2 (default priority), bracketed by events on the launch stream
@@ -393,8 +427,10 @@ def main():
                    "latent_dtype": "fp8_e4m3" if spec.latent_fp8 else "bf16",
                    "pools": "cached; the step recompresses the pool of its newest row",
                    "input_sets": a.sets,
-                   "graph": "one HIP graph per set: the fused decode calls (gate+compress, "
-                            "gated index scores, top-k+expand, sparse MLA)"},
+                   "graph": "one HIP graph of eight consecutive steps (one per input set), "
+                            "each the fused decode calls (gate+compress, gated index scores, "
+                            "top-k+expand, sparse MLA)"},
+        "single_step_graph_us": round(ms1 / a.steps * 1e3, 2),
         "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": int(step_bytes),
         "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
