@@ -332,16 +332,20 @@ def index_scores(qi, w, keys, pool_start, pool_valid, pool_off, n_pools, q_req, 
 # ---------------------------------------------------------------------------
 
 
-def topk_pools(scores, cand, select_k_: int, queries: Optional[Iterable[int]] = None):
+def topk_pools(scores, cand, select_k_: int, queries: Optional[Iterable[int]] = None,
+               row_len=None):
     """[Q, select_k] pool ids: the k_eff = min(select_k, #candidates)
     candidates ranked first by (score descending, pool id ascending), listed in
     ascending pool id; the remaining slots are -1.  Selection is a set (the
-    attention is set membership), so the ascending list is its canonical form."""
+    attention is set membership), so the ascending list is its canonical form.
+    row_len [Q] (optional): only the first row_len[q] entries of row q count
+    (clamped to [0, row width])."""
     Q = scores.shape[0]
     sel = np.full((Q, select_k_), -1, dtype=np.int32)
     qs = range(Q) if queries is None else queries
     for q in qs:
-        ids = np.flatnonzero(cand[q])
+        n = scores.shape[1] if row_len is None else min(max(int(row_len[q]), 0), scores.shape[1])
+        ids = np.flatnonzero(cand[q][:n])
         if len(ids) == 0:
             continue
         s = scores[q, ids].astype(np.float64)

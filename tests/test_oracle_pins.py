@@ -367,6 +367,26 @@ def test_topk_brute_force_with_ties():
         assert np.all(sel[len(expect):] == -1)
 
 
+def test_topk_row_len_brute_force():
+    """A row length keeps only the row's leading entries: brute force over the
+    cut row, with lengths of 0, inside the row, the width and past it."""
+    rng = np.random.default_rng(23)
+    for trial in range(200):
+        P = int(rng.integers(1, 30))
+        kk = int(rng.integers(1, 10))
+        Q = 4
+        s = rng.choice(np.float32([-1.0, 0.0, 0.25, 2.0, 5.0]), size=(Q, P)).astype(np.float32)
+        c = (rng.random((Q, P)) < 0.8).astype(np.uint8)
+        lens = np.array([0, int(rng.integers(0, P + 1)), P, P + 7], dtype=np.int32)
+        sel = O.topk_pools(s, c, kk, row_len=lens)
+        for q in range(Q):
+            n = min(int(lens[q]), P)
+            cands = [(float(s[q, p]), p) for p in range(n) if c[q, p]]
+            expect = sorted(p for _, p in sorted(cands, key=lambda t: (-t[0], t[1]))[:kk])
+            assert list(sel[q, :len(expect)]) == expect
+            assert np.all(sel[q, len(expect):] == -1)
+
+
 def test_topk_no_candidates_all_minus_one():
     sel = O.topk_pools(np.full((2, 5), -np.inf, np.float32), np.zeros((2, 5), np.uint8), 3)
     assert np.all(sel == -1)
