@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 2
+#define DSA_ABI_VERSION 3
 
 typedef int dsa_status;
 #define DSA_OK 0
@@ -179,13 +179,16 @@ dsa_status dsa_index_scores(const uint16_t* qi, const float* w, const uint16_t* 
  * (fp32 keys compared as ordered integers), so the result is a pure function
  * of the scores.
  * scores [Q, pstride] f32, cand [Q, pstride] u8, sel [Q, select_k] i32.
+ * row_len [Q] i32 or NULL: only entries p < row_len[q] of row q count
+ * (clamped to [0, pstride]; NULL means pstride), for rows shorter than the
+ * batch's widest.
  * No workspace is needed at present (size 0; ws may be NULL).
  * Errors: INVALID_ARG for select_k < 1, pstride < 1, Q < 0, NULL pointers;
  * UNSUPPORTED for pstride > DSA_MAX_TOPK_ROW.
  * ------------------------------------------------------------------------- */
 size_t dsa_topk_pools_workspace_size(int Q, int pstride, int select_k);
-dsa_status dsa_topk_pools(const float* scores, const uint8_t* cand, int Q, int pstride,
-                          int select_k, int32_t* sel, void* ws, size_t ws_bytes,
+dsa_status dsa_topk_pools(const float* scores, const uint8_t* cand, const int32_t* row_len, int Q,
+                          int pstride, int select_k, int32_t* sel, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
@@ -407,10 +410,11 @@ dsa_status dsa_index_scores_gated(const uint16_t* qi, const float* gate_part, in
                                   const int32_t* n_pools, const int32_t* q_req,
                                   const int32_t* q_pos, int Q, int H, int D, int kpool,
                                   int pstride, float* scores, uint8_t* cand, hipStream_t stream);
-dsa_status dsa_topk_expand(const float* scores, const uint8_t* cand, int Q, int pstride,
-                           int select_k, const int32_t* pool_start, const int32_t* pool_off,
-                           const int32_t* q_req, int kpool, int out_width, int flags,
-                           int32_t* sel, int32_t* tok, hipStream_t stream);
+dsa_status dsa_topk_expand(const float* scores, const uint8_t* cand, const int32_t* row_len,
+                           int Q, int pstride, int select_k, const int32_t* pool_start,
+                           const int32_t* pool_off, const int32_t* q_req, int kpool,
+                           int out_width, int flags, int32_t* sel, int32_t* tok,
+                           hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Measurement: the HBM read lane   [stkernel pull request #290, its

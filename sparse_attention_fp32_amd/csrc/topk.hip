@@ -74,6 +74,7 @@ __device__ __forceinline__ void wave0_offsets(const int* __restrict__ cnt, int* 
 template <int E, bool EXPAND>
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores,
                                                         const uint8_t* __restrict__ cand,
+                                                        const int32_t* __restrict__ row_len,
                                                         int pstride, int select_k,
                                                         int32_t* __restrict__ sel, ExpandArgs ex) {
   __shared__ int hist[kWaves][256];
@@ -92,7 +93,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   const uint8_t* crow = cand + (int64_t)q * pstride;
   int32_t* out = sel + (int64_t)q * select_k;
 
-  // loads (ids clamped into the row), then masked
+  // loads (ids clamped into the row), then masked; the row's length loads
+  // beside them (without row_len it reads a score word and does not use it)
   float sv[E];
   uint8_t cv[E];
 #pragma unroll
@@ -101,6 +103,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     sv[e] = srow[id];
     cv[e] = crow[id];
   }
+  const int len_word = *(row_len ? row_len + q : (const int32_t*)srow);
   // fused expansion: start rows of this request's pool slots, loaded without a
   // branch (ids clamped to the request's slots; a request with no slot reads
   // q_req instead, and none of its pools can be selected)
@@ -115,6 +118,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
 #pragma unroll
     for (int e = 0; e < E; ++e) ps[e] = src[min(t + kThreads * e, last)];
   }
+  const int lenq = row_len ? min(max(len_word, 0), pstride) : pstride;  // entries that count
   uint32_t key[E];
   uint32_t kmx = 0u;
   int nc = 0;
@@ -125,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     // (which would end in a wait for every outstanding load)
     uint32_t u = __float_as_uint(sv[e]), cb = cv[e];
     asm volatile("" : "+v"(u), "+v"(cb));
-    const bool c = (t + kThreads * e < pstride) & (cb != 0u);
+    const bool c = (t + kThreads * e < lenq) & (cb != 0u);
     key[e] = c ? float_order_key(__uint_as_float(u)) : 0u;
     kmx = max(kmx, key[e]);
     nc += __popcll(ballot(c));
@@ -350,14 +354,16 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
 }
 
 template <bool EXPAND>
-dsa_status launch_topk(const float* scores, const uint8_t* cand, int Q, int pstride, int select_k,
+dsa_status launch_topk(const float* scores, const uint8_t* cand, const int32_t* row_len, int Q,
+                       int pstride, int select_k,
                        int32_t* sel, const ExpandArgs& ex, hipStream_t stream) {
   const int need = (pstride + kThreads - 1) / kThreads;
   if (dsa::trace_enabled())
     fprintf(stderr, "[dsa] topk_pools Q=%d pstride=%d select_k=%d E=%d expand=%d\n", Q, pstride,
             select_k, need, (int)EXPAND);
 #define DSA_LAUNCH_TK(E) \
-  topk_kernel<E, EXPAND><<<Q, kThreads, 0, stream>>>(scores, cand, pstride, select_k, sel, ex)
+  topk_kernel<E, EXPAND><<<Q, kThreads, 0, stream>>>(scores, cand, row_len, pstride, select_k, \
+                                                      sel, ex)
   if (need <= 1) DSA_LAUNCH_TK(1);
   else if (need <= 2) DSA_LAUNCH_TK(2);
   else if (need <= 4) DSA_LAUNCH_TK(4);
@@ -376,8 +382,9 @@ DSA_EXPORT size_t dsa_topk_pools_workspace_size(int Q, int pstride, int select_k
   return 0;
 }
 
-DSA_EXPORT dsa_status dsa_topk_pools(const float* scores, const uint8_t* cand, int Q, int pstride,
-                                     int select_k, int32_t* sel, void* ws, size_t ws_bytes,
+DSA_EXPORT dsa_status dsa_topk_pools(const float* scores, const uint8_t* cand,
+                                     const int32_t* row_len, int Q, int pstride, int select_k,
+                                     int32_t* sel, void* ws, size_t ws_bytes,
                                      hipStream_t stream) {
   (void)ws;
   (void)ws_bytes;
@@ -388,12 +395,14 @@ DSA_EXPORT dsa_status dsa_topk_pools(const float* scores, const uint8_t* cand, i
               "dsa_topk_pools: pstride=%d above %d", pstride, DSA_MAX_TOPK_ROW);
   if (Q == 0) return DSA_OK;
   DSA_REQUIRE(scores && cand && sel, DSA_ERR_INVALID_ARG, "dsa_topk_pools: NULL tensor pointer");
-  DSA_REQUIRE_ALIGNED("dsa_topk_pools", scores, cand, sel, ws);
-  return launch_topk<false>(scores, cand, Q, pstride, select_k, sel, ExpandArgs{}, stream);
+  DSA_REQUIRE_ALIGNED("dsa_topk_pools", scores, cand, row_len, sel, ws);
+  return launch_topk<false>(scores, cand, row_len, Q, pstride, select_k, sel, ExpandArgs{},
+                            stream);
 }
 
-DSA_EXPORT dsa_status dsa_topk_expand(const float* scores, const uint8_t* cand, int Q,
-                                      int pstride, int select_k, const int32_t* pool_start,
+DSA_EXPORT dsa_status dsa_topk_expand(const float* scores, const uint8_t* cand,
+                                      const int32_t* row_len, int Q, int pstride, int select_k,
+                                      const int32_t* pool_start,
                                       const int32_t* pool_off, const int32_t* q_req, int kpool,
                                       int out_width, int flags, int32_t* sel, int32_t* tok,
                                       hipStream_t stream) {
@@ -414,7 +423,8 @@ DSA_EXPORT dsa_status dsa_topk_expand(const float* scores, const uint8_t* cand, 
   if (Q == 0) return DSA_OK;
   DSA_REQUIRE(scores && cand && sel && pool_start && pool_off && q_req && tok,
               DSA_ERR_INVALID_ARG, "dsa_topk_expand: NULL tensor pointer");
-  DSA_REQUIRE_ALIGNED("dsa_topk_expand", scores, cand, pool_start, pool_off, q_req, sel, tok);
-  return launch_topk<true>(scores, cand, Q, pstride, select_k, sel,
+  DSA_REQUIRE_ALIGNED("dsa_topk_expand", scores, cand, row_len, pool_start, pool_off, q_req, sel,
+                      tok);
+  return launch_topk<true>(scores, cand, row_len, Q, pstride, select_k, sel,
                            ExpandArgs{pool_start, pool_off, q_req, kpool, out_width, tok}, stream);
 }

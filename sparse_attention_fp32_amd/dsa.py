@@ -39,7 +39,7 @@ _SIGS = {
                                 _I, _P, _P, _P, _P, _P]),
     "dsa_index_scores": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
     "dsa_topk_pools_workspace_size": (_Z, [_I, _I, _I]),
-    "dsa_topk_pools": (_I, [_P, _P, _I, _I, _I, _P, _P, _Z, _P]),
+    "dsa_topk_pools": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _Z, _P]),
     "dsa_expand_selection": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "dsa_sparse_mla_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "dsa_sparse_mla_decode": (_I, [_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P,
@@ -58,7 +58,7 @@ _SIGS = {
                                     _P]),
     "dsa_index_scores_gated": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                                     _I, _P, _P, _P]),
-    "dsa_topk_expand": (_I, [_P, _P, _I, _I, _I, _P, _P, _P, _I, _I, _I, _P, _P, _P]),
+    "dsa_topk_expand": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _I, _I, _I, _P, _P, _P]),
     "dsa_select_tail": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
 }
 
@@ -191,12 +191,14 @@ def dsa_index_scores(qi, w, keys, pool_start, pool_valid, pool_off, n_pools, q_r
         _dev(cand, _U8, "cand"), _stream(stream)))
 
 
-def dsa_topk_pools(scores, cand, sel, ws=None, stream=None) -> None:
+def dsa_topk_pools(scores, cand, sel, ws=None, stream=None, row_len=None) -> None:
+    """row_len: [Q] i32 (only the first row_len[q] entries of row q count) or None."""
     Q, pstride = scores.shape
     select_k = sel.shape[1]
     wp, wb = _ws(ws)
-    _check(lib().dsa_topk_pools(_dev(scores, torch.float32, "scores"), _dev(cand, _U8, "cand"), Q,
-                                pstride, select_k, _dev(sel, _I32, "sel"), wp, wb, _stream(stream)))
+    _check(lib().dsa_topk_pools(_dev(scores, torch.float32, "scores"), _dev(cand, _U8, "cand"),
+                                _dev(row_len, _I32, "row_len", allow_none=True), Q, pstride,
+                                select_k, _dev(sel, _I32, "sel"), wp, wb, _stream(stream)))
 
 
 def dsa_expand_selection(sel, pool_start, pool_off, q_req, kpool: int, tok, flags: int = 0,
@@ -317,12 +319,13 @@ def dsa_index_scores_gated(qi, gate_part, nslices: int, w, keys, pool_start, poo
 
 
 def dsa_topk_expand(scores, cand, pool_start, pool_off, q_req, kpool: int, sel, tok, flags: int = 0,
-                    stream=None) -> None:
+                    stream=None, row_len=None) -> None:
     Q, pstride = scores.shape
     select_k = sel.shape[1]
     out_width = tok.shape[1]
     _check(lib().dsa_topk_expand(
-        _dev(scores, torch.float32, "scores"), _dev(cand, _U8, "cand"), Q, pstride, select_k,
+        _dev(scores, torch.float32, "scores"), _dev(cand, _U8, "cand"),
+        _dev(row_len, _I32, "row_len", allow_none=True), Q, pstride, select_k,
         _dev(pool_start, _I32, "pool_start"), _dev(pool_off, _I32, "pool_off"),
         _dev(q_req, _I32, "q_req"), kpool, out_width, flags, _dev(sel, _I32, "sel"),
         _dev(tok, _I32, "tok"), _stream(stream)))

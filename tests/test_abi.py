@@ -29,7 +29,7 @@ def test_exports_every_declared_function():
     for n in names:
         assert n in exported, n
         getattr(dsa.lib(), n)
-    assert dsa.abi_version() == 2
+    assert dsa.abi_version() == 3
 
 
 def _code(fn, *args):
@@ -93,11 +93,12 @@ def test_index_scores_errors():
 
 def test_topk_errors():
     L = dsa.lib()
-    assert L.dsa_topk_pools(FAKE, FAKE, 4, 100, 0, FAKE, NUL, 0, NUL) == INV
-    assert L.dsa_topk_pools(FAKE, FAKE, 4, 0, 8, FAKE, NUL, 0, NUL) == INV
-    assert L.dsa_topk_pools(FAKE, FAKE, 4, dsa.MAX_TOPK_ROW + 1, 8, FAKE, NUL, 0, NUL) == UNS
-    assert L.dsa_topk_pools(NUL, FAKE, 4, 100, 8, FAKE, NUL, 0, NUL) == INV
-    assert _misaligned(L.dsa_topk_pools(FAKE, MIS, 4, 100, 8, FAKE, NUL, 0, NUL))
+    assert L.dsa_topk_pools(FAKE, FAKE, NUL, 4, 100, 0, FAKE, NUL, 0, NUL) == INV
+    assert L.dsa_topk_pools(FAKE, FAKE, NUL, 4, 0, 8, FAKE, NUL, 0, NUL) == INV
+    assert L.dsa_topk_pools(FAKE, FAKE, NUL, 4, dsa.MAX_TOPK_ROW + 1, 8, FAKE, NUL, 0, NUL) == UNS
+    assert L.dsa_topk_pools(NUL, FAKE, NUL, 4, 100, 8, FAKE, NUL, 0, NUL) == INV
+    assert _misaligned(L.dsa_topk_pools(FAKE, MIS, NUL, 4, 100, 8, FAKE, NUL, 0, NUL))
+    assert _misaligned(L.dsa_topk_pools(FAKE, FAKE, MIS, 4, 100, 8, FAKE, NUL, 0, NUL))
     assert dsa.topk_pools_workspace_size(16, 8192, 512) == 0
 
 
@@ -172,8 +173,8 @@ def test_fused_call_errors():
     assert sg(Q=0) == dsa.DSA_OK
 
     def te(select_k=4, kpool=4, out_width=16, flags=0, tok=FAKE):
-        return L.dsa_topk_expand(FAKE, FAKE, 2, 100, select_k, FAKE, FAKE, FAKE, kpool, out_width,
-                                 flags, FAKE, tok, NUL)
+        return L.dsa_topk_expand(FAKE, FAKE, NUL, 2, 100, select_k, FAKE, FAKE, FAKE, kpool,
+                                 out_width, flags, FAKE, tok, NUL)
     assert te(out_width=15) == INV
     assert te(select_k=0) == INV
     assert te(kpool=9) == INV

@@ -101,3 +101,41 @@ def test_topk_exact(P, k, kind):
     dsa.dsa_topk_pools(sg, cg, out)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), ref)
+
+
+ROW_LEN_CASES = [(P, k, kind) for P in (30, 2047, 8192, 16384) for k in (1, 64, 512)
+                 for kind in ("normal", "ties")] + [(4096, 2049, "wide"), (8192, 3000, "ties")]
+
+
+@pytest.mark.parametrize("P,k,kind", ROW_LEN_CASES)
+@pytest.mark.parametrize("fused", [False, True])
+def test_topk_row_len(P, k, kind, fused):
+    """Rows cut by row_len (0, negative, inside the row, the width, past it):
+    only the leading entries count, in both calls."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rng, s, c = _case_rows(P, k, kind)
+    Q = s.shape[0]
+    lens = np.array([0, P, int(rng.integers(1, P + 1)), -5, P + 100,
+                     int(rng.integers(0, P + 1))], dtype=np.int32)[:Q]
+    ref_sel = O.topk_pools(s, c, k, row_len=lens)
+    sg, cg = torch.from_numpy(s).cuda(), torch.from_numpy(c).cuda()
+    lg = torch.from_numpy(lens).cuda()
+    sel = torch.full((Q, k), 12345, dtype=torch.int32, device="cuda")
+    if not fused:
+        dsa.dsa_topk_pools(sg, cg, sel, row_len=lg)
+        torch.cuda.synchronize()
+        assert np.array_equal(sel.cpu().numpy(), ref_sel)
+        return
+    kpool = 2
+    out_width = k * kpool + 1
+    pool_off = np.arange(Q + 1, dtype=np.int32) * P
+    pool_start = np.concatenate([7 + kpool * np.arange(P)] * Q).astype(np.int32)
+    q_req = np.arange(Q, dtype=np.int32)
+    ref_tok = O.expand_selection(ref_sel, pool_start, pool_off, q_req, kpool, out_width)
+    tok = torch.full((Q, out_width), 12345, dtype=torch.int32, device="cuda")
+    dsa.dsa_topk_expand(sg, cg, torch.from_numpy(pool_start).cuda(), torch.from_numpy(pool_off).cuda(),
+                        torch.from_numpy(q_req).cuda(), kpool, sel, tok, row_len=lg)
+    torch.cuda.synchronize()
+    assert np.array_equal(sel.cpu().numpy(), ref_sel)
+    assert np.array_equal(tok.cpu().numpy(), ref_tok)
