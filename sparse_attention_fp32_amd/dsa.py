@@ -194,6 +194,8 @@ def dsa_index_scores(qi, w, keys, pool_start, pool_valid, pool_off, n_pools, q_r
 def dsa_topk_pools(scores, cand, sel, ws=None, stream=None, row_len=None) -> None:
     """row_len: [Q] i32 (only the first row_len[q] entries of row q count) or None."""
     Q, pstride = scores.shape
+    if row_len is not None and row_len.numel() < Q:
+        raise ValueError(f"row_len holds {row_len.numel()} entries, need {Q}")
     select_k = sel.shape[1]
     wp, wb = _ws(ws)
     _check(lib().dsa_topk_pools(_dev(scores, torch.float32, "scores"), _dev(cand, _U8, "cand"),
@@ -321,6 +323,8 @@ def dsa_index_scores_gated(qi, gate_part, nslices: int, w, keys, pool_start, poo
 def dsa_topk_expand(scores, cand, pool_start, pool_off, q_req, kpool: int, sel, tok, flags: int = 0,
                     stream=None, row_len=None) -> None:
     Q, pstride = scores.shape
+    if row_len is not None and row_len.numel() < Q:
+        raise ValueError(f"row_len holds {row_len.numel()} entries, need {Q}")
     select_k = sel.shape[1]
     out_width = tok.shape[1]
     _check(lib().dsa_topk_expand(
