@@ -26,7 +26,7 @@ constexpr int kTiles = 4;                  // 16-pool tiles per wave
 constexpr int kPoolsPerWG = 4 * kTiles * 16;  // 4 waves (= 256, one slot per thread)
 static_assert(kPoolsPerWG == 256, "the sentinel-only path gives each thread one slot");
 
-constexpr int kMaxGateSlices = 64;  // 4 slice groups x 16 per lane
+constexpr int kMaxGateSlices = 64;  // 16 slice groups x 4 per thread
 
 template <int KS, bool GATED>  // D / 32 k-steps; w given as head-gate partials
 __global__ __launch_bounds__(256) void index_scores_kernel(
@@ -41,16 +41,15 @@ __global__ __launch_bounds__(256) void index_scores_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   // Head-gate partials first (gated variant): the oldest loads, so the
-  // reduction below waits for them alone while the key rows stream in.  Every
-  // wave loads all of them: lane (head h = lane % 16, group g = lane / 16)
-  // takes slices g, g+4, g+8, ...
-  float gp[kMaxGateSlices / 4];
+  // reduction below waits for them alone while the key rows stream in.
+  float gp[4];
   if (GATED) {
     const int Q = gridDim.y;
+    const int h = threadIdx.x & 15, g = threadIdx.x >> 4;
 #pragma unroll
-    for (int i = 0; i < kMaxGateSlices / 4; ++i) {
-      const int sl = min(grp + 4 * i, nslices - 1);
-      gp[i] = w[((int64_t)sl * Q + q) * H + min(col, H - 1)];
+    for (int i = 0; i < 4; ++i) {
+      const int sl = min(g + 16 * i, nslices - 1);
+      gp[i] = w[((int64_t)sl * Q + q) * H + min(h, H - 1)];
     }
   }
   const int r = q_req[q];
@@ -98,21 +97,26 @@ __global__ __launch_bounds__(256) void index_scores_kernel(
   for (int kk = 0; kk < KS; ++kk) a[kk] = as_bf16x8(*(const uint4*)(qrow + kk * 32));
   float wr[4];
   if (GATED) {
-    // w[q, h] = sum over slices of part[sl][q][h], inside each wave (no
-    // barrier): group g adds its slices in order, then the four group sums
-    // are added as (g0 + g1) + (g2 + g3) -- the same bits in every lane, wave
-    // and workgroup, since a + b == b + a exactly.
+    // w[q, h] = sum over slices of part[sl][q][h]: thread (group g, head h)
+    // adds slices g, g+16, g+32, g+48; the 16 group sums go in group order.
+    __shared__ float s_red[16][16];
+    __shared__ float s_w[16];
+    const int t = threadIdx.x, h = t & 15, g = t >> 4;
     float acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < kMaxGateSlices / 4; ++i) acc += grp + 4 * i < nslices ? gp[i] : 0.f;
-    acc += xor16(acc);
-    acc += xor32(acc);
+    for (int i = 0; i < 4; ++i) acc += g + 16 * i < nslices ? gp[i] : 0.f;
+    s_red[g][h] = acc;
+    __syncthreads();
+    if (t < 16) {
+      float sum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float v = __shfl(acc, grp * 4 + i);  // head grp*4 + i
-      wr[i] = grp * 4 + i < H ? v : 0.f;
+      for (int j = 0; j < 16; ++j) sum += s_red[j][t];
+      s_w[t] = sum;
+      if (w_out && blockIdx.x == 0 && t < H) w_out[(int64_t)q * H + t] = sum;
     }
-    if (w_out && blockIdx.x == 0 && wave == 0 && lane < H) w_out[(int64_t)q * H + lane] = acc;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wr[i] = grp * 4 + i < H ? s_w[grp * 4 + i] : 0.f;
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
