@@ -42,11 +42,12 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t 
 }
 
 // Order-preserving map of a finite float to an unsigned key (larger float ->
-// larger key); -0 is mapped like +0.
+// larger key): 2^31 plus the value's magnitude bits, negated for a negative
+// value, so -0 and +0 share the key 2^31 and no finite value (nor -inf) maps
+// to 0.
 __device__ __forceinline__ uint32_t float_order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(f), m = u & 0x7fffffffu;
+  return (u & 0x80000000u) ? 0x80000000u - m : 0x80000000u + m;
 }
 
 // ---- cross-lane primitives at ALU latency (DPP and gfx950 permlane swaps) ----

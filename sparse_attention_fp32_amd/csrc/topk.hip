@@ -3,8 +3,8 @@
 // One 1024-thread workgroup per score row; thread t holds ids t + 1024*e
 // (e < E), so every load instruction is fully coalesced and the order (e, t)
 // is ascending id order.  Scores become order-preserving integer keys (a
-// finite float maps to an unsigned key that sorts like the float; -0 like +0;
-// non-candidates are key 0 and never counted), so no floating-point
+// finite float maps to a nonzero unsigned key that sorts like the float; -0
+// like +0; non-candidates are key 0 and never counted), so no floating-point
 // comparison decides the selection.
 //  1. Candidate count and largest key (wave ballots / DPP max, one barrier).
 //  2. Octave of every key below the largest (difference of the top 9 key bits
@@ -32,7 +32,7 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kStage = 2048;  // largest select_k whose output is staged in LDS
 
-__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 // number of set bits of m below this lane
 __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -99,7 +99,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   uint8_t cv[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int id = min(t + kThreads * e, pstride - 1);
+    // (unsigned, so the address is a 32-bit offset from the row's base)
+    const unsigned id = min((unsigned)(t + kThreads * e), (unsigned)(pstride - 1));
     sv[e] = srow[id];
     cv[e] = crow[id];
   }
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     const bool c = (t + kThreads * e < lenq) & (cb != 0u);
     key[e] = c ? float_order_key(__uint_as_float(u)) : 0u;
     kmx = max(kmx, key[e]);
-    nc += __popcll(ballot(c));
+    nc += __popcll(ballot(key[e] != 0u));  // (no candidate's key is 0)
   }
   kmx = wave_max_u32(kmx);
   if (lane == 0) {
