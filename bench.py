@@ -179,7 +179,7 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}))
         return
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1",
                           "n_gpus": a.gpus}))
         sys.exit(2)
     if not torch.cuda.is_available():

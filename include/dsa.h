@@ -52,7 +52,7 @@ extern "C" {
 typedef int dsa_status;
 #define DSA_OK 0
 #define DSA_ERR_INVALID_ARG 1 /* an argument breaks the documented contract */
-#define DSA_ERR_UNSUPPORTED 2 /* a legal shape this build has no kernel for */
+#define DSA_ERR_UNSUPPORTED 2 /* a legal shape the library has no kernel for */
 #define DSA_ERR_LAUNCH 3      /* the HIP runtime refused a launch */
 
 /* latent cache element types for dsa_sparse_mla_decode */

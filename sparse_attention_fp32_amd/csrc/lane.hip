@@ -2,7 +2,7 @@
 // achievable streaming rate a kernel's bandwidth is compared with.
 //
 // stkernel pull request #290 (its measurement ledger): a bandwidth-bound
-// kernel is judged against the rate of a plain streaming kernel on the same
+// kernel is measured against the rate of a plain streaming kernel on the same
 // part -- "the lane" -- and one at 90 % of it or more counts as at the
 // bandwidth floor.  The 8 TB/s figure is the part's peak; the lane is what a
 // kernel can reach.
