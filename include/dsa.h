@@ -136,7 +136,8 @@ dsa_status dsa_head_gate(const float* hidden, const float* W, float* w, int M, i
  * new_from = NULL recomputes every slot.
  * Errors: INVALID_ARG for kpool outside [1, 8] (never truncated), B < 0, NULL
  * pointers, exactly one of ln_w / ln_b NULL, max_cap < 0, max_new < 1 with
- * new_from; UNSUPPORTED for D not in {32, 64, 128, 256}.
+ * new_from; UNSUPPORTED for D not in {32, 64, 128, 256} or more than 65535
+ * requests.
  * ------------------------------------------------------------------------- */
 dsa_status dsa_kpool_compress(const uint16_t* k, const uint16_t* gate, const uint16_t* ape,
                               const uint8_t* valid, const int32_t* tok_off, const int32_t* pool_off,
@@ -161,7 +162,8 @@ dsa_status dsa_kpool_compress(const uint16_t* k, const uint16_t* gate, const uin
  * q_pos [Q] i32; scores [Q, pstride] f32; cand [Q, pstride] u8.
  * pstride >= every cap_r.
  * Errors: INVALID_ARG for H outside [1, 16], kpool outside [1, 8], pstride < 1,
- * Q < 0, NULL pointers; UNSUPPORTED for D not in {32, 64, 128, 256}.
+ * Q < 0, NULL pointers; UNSUPPORTED for D not in {32, 64, 128, 256} or
+ * Q > 65535.
  * ------------------------------------------------------------------------- */
 dsa_status dsa_index_scores(const uint16_t* qi, const float* w, const uint16_t* keys,
                             const int32_t* pool_start, const uint8_t* pool_valid,
@@ -203,7 +205,7 @@ dsa_status dsa_topk_pools(const float* scores, const uint8_t* cand, const int32_
  * always_select_tail slots are written by dsa_select_tail afterwards).
  * Errors: INVALID_ARG for out_width < select_k * kpool (the page's
  * topk-multiple-of-kpool rule), kpool outside [1, 8], select_k < 1, unknown
- * flag bits, NULL pointers; UNSUPPORTED for flag bit 0.
+ * flag bits, NULL pointers; UNSUPPORTED for flag bit 0 or Q > 65535.
  * ------------------------------------------------------------------------- */
 dsa_status dsa_expand_selection(const int32_t* sel, const int32_t* pool_start,
                                 const int32_t* pool_off, const int32_t* q_req, int Q, int select_k,
@@ -256,7 +258,7 @@ dsa_status dsa_select_tail(const uint8_t* valid, const int32_t* tok_off, const i
  * Errors: UNSUPPORTED for L != 512 (the latent width is fixed, as the page's
  * validate() demands); INVALID_ARG for Hm < 1, out_width < 1, Q < 0, an
  * unknown latent_dtype, fp8 without ckv_scale, NULL pointers, or ws_bytes
- * below the size.
+ * below the size; UNSUPPORTED for Q > 65535.
  * ------------------------------------------------------------------------- */
 size_t dsa_sparse_mla_decode_workspace_size(int Q, int Hm, int L, int out_width,
                                             int latent_dtype);

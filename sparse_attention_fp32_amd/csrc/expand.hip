@@ -49,6 +49,7 @@ DSA_EXPORT dsa_status dsa_expand_selection(const int32_t* sel, const int32_t* po
   DSA_REQUIRE(sel && pool_start && pool_off && q_req && tok, DSA_ERR_INVALID_ARG,
               "dsa_expand_selection: NULL tensor pointer");
   DSA_REQUIRE_ALIGNED("dsa_expand_selection", sel, pool_start, pool_off, q_req, tok);
+  DSA_REQUIRE(Q <= 65535, DSA_ERR_UNSUPPORTED, "dsa_expand_selection: Q=%d above 65535", Q);
   dim3 grid((out_width + 255) / 256, Q);
   expand_kernel<<<grid, 256, 0, stream>>>(sel, pool_start, pool_off, q_req, select_k, kpool,
                                           out_width, tok);

@@ -457,6 +457,9 @@ dsa_status launch_compress(const uint16_t* k, const uint16_t* gate, const uint16
   }
   if (nx < 1) nx = 1;  // n_pools is written even with no slots
   const int gate_rows = (ga.nwg + nx - 1) / nx;
+  DSA_REQUIRE((long long)B + gate_rows <= 65535, DSA_ERR_UNSUPPORTED,
+              "%s: B=%d requests (+%d head-gate rows) above the 65535-row launch grid", who, B,
+              gate_rows);
   dim3 grid(nx, B + gate_rows);
   if (dsa::trace_enabled())
     fprintf(stderr,

@@ -70,6 +70,7 @@ def test_kpool_compress_errors():
     assert _compress(new_from=FAKE, max_new=0) == INV
     assert _compress(k=NUL) == INV
     assert _misaligned(_compress(k=MIS))
+    assert _compress(B=70000, max_cap=4) == UNS      # beyond the launch grid
     assert _compress(ln_w=NUL) == INV             # both LayerNorm vectors, or neither
     assert "both" in dsa.last_error()
     assert _compress(B=0) == dsa.DSA_OK
@@ -115,6 +116,7 @@ def test_expand_errors():
     assert call(flags=2) == INV
     assert call(sel=NUL) == INV
     assert _misaligned(call(sel=MIS))
+    assert L.dsa_expand_selection(FAKE, FAKE, FAKE, FAKE, 70000, 4, 4, 16, 0, FAKE, NUL) == UNS
 
 
 def test_sparse_mla_errors():
