@@ -225,23 +225,34 @@ def main():
         torch.cuda.synchronize()
         return g
 
-    def timed_seq(gseq, singles, n, warm):
+    def timed_seq(gseq, singles, n, warm, segments=5):
         """n steps: n // len(singles) replays of the sequence graph, then the
-        remainder as single-step graphs."""
+        remainder as single-step graphs.  Events also split the replays into
+        `segments` runs of equal replay count; returns the total time, the
+        wall time and the median per-step time of the segments (us)."""
         k = len(singles)
         for _ in range(max(1, warm // k)):
             gseq.replay()
         torch.cuda.synchronize()
+        reps = n // k
+        nseg = max(1, min(segments, reps))
+        bounds = [reps * i // nseg for i in range(nseg + 1)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(nseg + 1)]
+        e1 = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(n // k):
+        ev[0].record()
+        for i in range(reps):
             gseq.replay()
+            if i + 1 in bounds[1:]:
+                ev[bounds.index(i + 1)].record()
         for i in range(n % k):
             singles[i].replay()
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1), time.perf_counter() - t0
+        seg = sorted(ev[j].elapsed_time(ev[j + 1]) / ((bounds[j + 1] - bounds[j]) * k) * 1e3
+                     for j in range(nseg) if bounds[j + 1] > bounds[j])
+        med = seg[len(seg) // 2] if seg else None
+        return ev[0].elapsed_time(e1), time.perf_counter() - t0, med
 
     def timed(graphs, n, warm):
         for i in range(warm):
@@ -259,7 +270,7 @@ def main():
     # the step: the fused decode calls over cached pools
     graphs = capture(lambda st: st.run_fused(incremental=True))
     gseq = capture_seq(lambda st: st.run_fused(incremental=True))
-    ms, wall = timed_seq(gseq, graphs, a.steps, a.warmup)
+    ms, wall, seg_med_us = timed_seq(gseq, graphs, a.steps, a.warmup)
     ms_per_step = ms / a.steps
     ms1, _ = timed(graphs, a.steps, a.warmup)  # the same steps as single-step graphs
     qps = spec.Q * a.steps / (ms / 1e3)
@@ -431,6 +442,7 @@ def main():
                             "each the fused decode calls (gate+compress, gated index scores, "
                             "top-k+expand, sparse MLA)"},
         "single_step_graph_us": round(ms1 / a.steps * 1e3, 2),
+        "median_of_5_segments_us": None if seg_med_us is None else round(seg_med_us, 2),
         "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": int(step_bytes),
         "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
