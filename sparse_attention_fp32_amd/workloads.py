@@ -146,6 +146,15 @@ def spec_by_name(name: str, seed: int = 0) -> Spec:
         return Spec(name, lengths=[1000, 517, 2053], pads=[3, 0, 61], kpool=4, index_heads=16,
                     index_dim=128, hidden=1024, select_k=100, out_width=403, mla_heads=64,
                     always_select_tail=True, live=[901, 398, 1990])
+    if name == "medium_prefill":  # causal prefill of two sequences and a request with no
+        # full pool: many queries per request (the index scores' query-block form), one
+        # block of 16 queries spanning all three requests, a short last block, and a
+        # query before its sequence's first valid row
+        q_req = [0] * 683 + [1] * 3 + [2] * 411
+        q_pos = [3] + list(range(9, 4100, 6)) + [69, 68, 67] + list(range(0, 2051, 5))
+        return Spec(name, lengths=[4100, 70, 2051], pads=[9, 67, 0], kpool=4, index_heads=16,
+                    index_dim=128, hidden=512, select_k=32, out_width=128, mla_heads=64,
+                    q_req=q_req, q_pos=q_pos)
     if name == "medium_fp8":
         return Spec(name, lengths=[777, 1500, 96, 2500], pads=[0, 17, 95, 5], kpool=8,
                     index_heads=12, index_dim=64, hidden=768, select_k=40, out_width=330,
@@ -154,7 +163,7 @@ def spec_by_name(name: str, seed: int = 0) -> Spec:
 
 
 WORKLOADS = ("tiny", "decode32k", "longctx", "prefill4k", "mixed64")
-PARITY_SHAPES = ("tiny", "medium", "medium_fp8", "medium_tail", "medium_pairs")
+PARITY_SHAPES = ("tiny", "medium", "medium_fp8", "medium_tail", "medium_pairs", "medium_prefill")
 
 
 @dataclasses.dataclass

@@ -400,6 +400,29 @@ def test_fused_index_scores_isolated(case):
     _say(f"gated scores worst rel diff {worst:.3g}")
 
 
+@pytest.mark.parametrize("ns", [1, 7, 16, 17, 32, 33, 64])
+def test_gated_scores_slice_counts(case, ns):
+    """The gated scores for every count of head-gate slices the library
+    takes (up to 64, uneven slices): the partials are the oracle's head-gate
+    over each slice of K, so they add up to the oracle's w."""
+    spec, xn, ref, xg = case
+    _say(f"index_scores_gated {spec.name} with {ns} slices")
+    from sparse_attention_fp32_amd import dsa
+    st = _step(xg)
+    _load_oracle_front(st, ref)
+    parts = [O.head_gate(xn["hidden"][:, c], xn["W"][c])
+             for c in np.array_split(np.arange(xn["hidden"].shape[1]), ns)]
+    part = torch.from_numpy(np.stack(parts).astype(np.float32).reshape(-1)).cuda()
+    for t in (st.scores, st.cand, st.w):
+        _poison(t)
+    x = st.x
+    dsa.dsa_index_scores_gated(x.qi, part, ns, st.w, st.keys, st.pool_start, st.pool_valid,
+                               x.pool_off, st.n_pools, x.q_req, x.q_pos, spec.kpool, st.scores,
+                               st.cand)
+    PT.check_gate(_np(st.w), ref["w"])
+    PT.check_scores(_np(st.scores), _np(st.cand), ref["scores"], ref["cand"])
+
+
 def test_fused_topk_expand_isolated(case):
     spec, xn, ref, xg = case
     _say(f"topk_expand {spec.name}")
