@@ -15,6 +15,11 @@
 // arrive as split-K partials of the head-gate (one per 128-wide K slice); each
 // workgroup adds them in slice order while its key rows load, and the first
 // workgroup of each query stores the sum as w.
+//
+// Prefill-sized batches (many queries of one sequence scanning the same keys)
+// take the query-block form below: the keys of a 256-pool block stay in
+// registers while the workgroup walks 8 consecutive queries, so the call is a
+// dense [Q*H x D] x [D x P] contraction instead of Q separate key streams.
 #include "dsa_device.hpp"
 #include "dsa_host.hpp"
 
