@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(
 // so both forms give the same bits.  A wave whose 64 pools hold no candidate
 // for the query (every pool past the request's end, invalid, or after the
 // query's position) skips its MFMAs.
-template <int KS, bool GATED, int NS>  // NS: most head-gate slices (16, 32 or 64)
+template <int KS, bool GATED, int NS>  // NS: most head-gate slices (1, 16, 32 or 64)
 __global__ __launch_bounds__(256) void index_scores_qblock_kernel(
     const uint16_t* __restrict__ qi, const float* __restrict__ w,
     const uint16_t* __restrict__ keys, const int32_t* __restrict__ pool_start,
@@ -423,6 +423,8 @@ dsa_status launch_scores(const uint16_t* qi, const float* w, int nslices, float*
 #define DSA_LAUNCH_QB_NS(KS)            \
   if (nslices == 0)                     \
     DSA_LAUNCH_QB(KS, false, 1);        \
+  else if (nslices == 1)                \
+    DSA_LAUNCH_QB(KS, true, 1);         \
   else if (nslices <= 16)               \
     DSA_LAUNCH_QB(KS, true, 16);        \
   else if (nslices <= 32)               \
