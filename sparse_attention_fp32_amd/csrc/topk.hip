@@ -1,11 +1,11 @@
 // a4: pool top-k with lowest-id tie-breaking, emitted in ascending pool id.
 //
-// One 1024-thread workgroup per score row; thread t holds ids t + 1024*e
-// (e < E), so every load instruction is fully coalesced and the order (e, t)
-// is ascending id order.  Scores become order-preserving integer keys (a
-// finite float maps to a nonzero unsigned key that sorts like the float; -0
-// like +0; non-candidates are key 0 and never counted), so no floating-point
-// comparison decides the selection.
+// One workgroup per score row (1024 threads, or 256 for rows of at most 1024
+// pools); thread t holds ids t + NT*e (e < E), so every load instruction is
+// fully coalesced and the order (e, t) is ascending id order.  Scores become
+// order-preserving integer keys (a finite float maps to a nonzero unsigned
+// key that sorts like the float; -0 like +0; non-candidates are key 0 and
+// never counted), so no floating-point comparison decides the selection.
 //  1. Candidate count and largest key (wave ballots / DPP max, one barrier).
 //  2. Octave of every key below the largest (difference of the top 9 key bits
 //     = sign and exponent, capped at 15), counted in packed 8-bit register
@@ -28,8 +28,11 @@ namespace {
 
 using namespace dsa;
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
+// Rows of more than kShortRow pools take 1024-thread workgroups; shorter rows
+// (prefill: thousands of rows of at most a thousand pools) take 256 threads,
+// so that several rows share a compute unit and fewer waves meet at each
+// barrier.
+constexpr int kShortRow = 1024;
 constexpr int kStage = 2048;  // largest select_k whose output is staged in LDS
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
@@ -48,11 +51,11 @@ struct ExpandArgs {
 };
 
 // Exclusive prefix, in (e, wave) order, of the per-(e, wave) counts in cnt
-// (E * kWaves entries), written to off; run by wave 0 alone.
-template <int E>
+// (E * NW entries), written to off; run by wave 0 alone.
+template <int E, int NW>
 __device__ __forceinline__ void wave0_offsets(const int* __restrict__ cnt, int* __restrict__ off,
                                               int lane) {
-  constexpr int kN = E * kWaves;
+  constexpr int kN = E * NW;
   constexpr int kPer = (kN + 63) / 64;
   int c[kPer];
   int sum = 0;
@@ -71,12 +74,14 @@ __device__ __forceinline__ void wave0_offsets(const int* __restrict__ cnt, int* 
   }
 }
 
-template <int E, bool EXPAND>
-__global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores,
+template <int NT, int E, bool EXPAND>  // NT threads per row, E ids per thread
+__global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores,
                                                         const uint8_t* __restrict__ cand,
                                                         const int32_t* __restrict__ row_len,
                                                         int pstride, int select_k,
                                                         int32_t* __restrict__ sel, ExpandArgs ex) {
+  constexpr int kThreads = NT, kWaves = NT / 64;
+  static_assert(NT >= 256, "the radix bins are summed by one thread each");
   __shared__ int hist[kWaves][256];
   __shared__ int s_tot[256];
   __shared__ uint32_t s_max[kWaves];
@@ -299,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
       if (lane == 0) s_ecnt[e * kWaves + wv] = __popcll(beq[e]);
     }
     __syncthreads();
-    if (wv == 0) wave0_offsets<E>(s_ecnt, s_eoff, lane);
+    if (wv == 0) wave0_offsets<E, kWaves>(s_ecnt, s_eoff, lane);
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < E; ++e)
@@ -314,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     if (lane == 0) s_ecnt[e * kWaves + wv] = __popcll(bk[e]);
   }
   __syncthreads();
-  if (wv == 0) wave0_offsets<E>(s_ecnt, s_eoff, lane);
+  if (wv == 0) wave0_offsets<E, kWaves>(s_ecnt, s_eoff, lane);
   __syncthreads();
   if (select_k <= kStage) {
     // positions into LDS, then every output row written in order by all threads
@@ -358,18 +363,25 @@ template <bool EXPAND>
 dsa_status launch_topk(const float* scores, const uint8_t* cand, const int32_t* row_len, int Q,
                        int pstride, int select_k,
                        int32_t* sel, const ExpandArgs& ex, hipStream_t stream) {
-  const int need = (pstride + kThreads - 1) / kThreads;
+  const int nt = pstride <= kShortRow ? 256 : 1024;
+  const int need = (pstride + nt - 1) / nt;
   if (dsa::trace_enabled())
-    fprintf(stderr, "[dsa] topk_pools Q=%d pstride=%d select_k=%d E=%d expand=%d\n", Q, pstride,
-            select_k, need, (int)EXPAND);
-#define DSA_LAUNCH_TK(E) \
-  topk_kernel<E, EXPAND><<<Q, kThreads, 0, stream>>>(scores, cand, row_len, pstride, select_k, \
-                                                      sel, ex)
-  if (need <= 1) DSA_LAUNCH_TK(1);
-  else if (need <= 2) DSA_LAUNCH_TK(2);
-  else if (need <= 4) DSA_LAUNCH_TK(4);
-  else if (need <= 8) DSA_LAUNCH_TK(8);
-  else DSA_LAUNCH_TK(16);
+    fprintf(stderr, "[dsa] topk_pools Q=%d pstride=%d select_k=%d threads=%d E=%d expand=%d\n", Q,
+            pstride, select_k, nt, need, (int)EXPAND);
+#define DSA_LAUNCH_TK(NT, E)                                                                     \
+  topk_kernel<NT, E, EXPAND><<<Q, NT, 0, stream>>>(scores, cand, row_len, pstride, select_k, sel, \
+                                                   ex)
+  if (nt == 256) {
+    if (need <= 1) DSA_LAUNCH_TK(256, 1);
+    else if (need <= 2) DSA_LAUNCH_TK(256, 2);
+    else DSA_LAUNCH_TK(256, 4);
+  } else {
+    if (need <= 1) DSA_LAUNCH_TK(1024, 1);
+    else if (need <= 2) DSA_LAUNCH_TK(1024, 2);
+    else if (need <= 4) DSA_LAUNCH_TK(1024, 4);
+    else if (need <= 8) DSA_LAUNCH_TK(1024, 8);
+    else DSA_LAUNCH_TK(1024, 16);
+  }
 #undef DSA_LAUNCH_TK
   return dsa::check_launch(EXPAND ? "dsa_topk_expand" : "dsa_topk_pools");
 }
