@@ -282,6 +282,8 @@ __global__ __launch_bounds__(256) void index_scores_qblock_kernel(
           scores[(int64_t)(qb0 + j) * pstride + p] = -INFINITY;
           cand[(int64_t)(qb0 + j) * pstride + p] = 0;
         }
+      // the qi rows' DMA into LDS lands before the workgroup gives its LDS up
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       return;
     }
   }
