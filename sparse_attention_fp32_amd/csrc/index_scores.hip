@@ -30,7 +30,7 @@ using namespace dsa;
 constexpr int kTiles = 4;                  // 16-pool tiles per wave
 constexpr int kPoolsPerWG = 4 * kTiles * 16;  // 4 waves (= 256, one slot per thread)
 static_assert(kPoolsPerWG == 256, "the sentinel-only path gives each thread one slot");
-static_assert(kTiles == 4, "the query-block stores give each lane group one tile");
+static_assert(kTiles == 4, "the score stores give each lane group one tile");
 
 constexpr int kMaxGateSlices = 64;  // 16 slice groups x 4 per thread
 constexpr int kQB = 8;              // queries per workgroup in the query-block form
@@ -142,6 +142,11 @@ __global__ __launch_bounds__(256) void index_scores_kernel(
     }
   }
 
+  // after the head sum every lane of column col holds tile tt's score for
+  // pool tile0 + 16tt + col; lane (col, grp) keeps tile grp's, so each wave
+  // stores its 64 pools with one score and one flag instruction
+  float so = -INFINITY;
+  bool co = false;
 #pragma unroll
   for (int tt = 0; tt < kTiles; ++tt) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -156,10 +161,15 @@ __global__ __launch_bounds__(256) void index_scores_kernel(
     if (s == 0.f) s = 0.f;  // store -0 as +0
     const int p = tile0 + tt * 16 + col;
     const bool c = p < P && pv[tt] != 0 && ps[tt] + kpool - 1 <= qp;
-    if (p < pstride) {
-      if (grp == 0) scores[(int64_t)q * pstride + p] = c ? s : -INFINITY;
-      if (grp == 1) cand[(int64_t)q * pstride + p] = (uint8_t)c;
+    if (grp == tt) {
+      so = c ? s : -INFINITY;
+      co = c;
     }
+  }
+  const int p = tile0 + lane;
+  if (p < pstride) {
+    scores[(int64_t)q * pstride + p] = so;
+    cand[(int64_t)q * pstride + p] = (uint8_t)co;
   }
 }
 
