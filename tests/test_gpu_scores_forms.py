@@ -3,8 +3,9 @@ prefill) at every key width it is built for and at narrow head counts,
 against the oracle: plain weights and head-gate partials of several slice
 counts.  Each shape has at least 256 queries and enough 8-query blocks times
 256-pool blocks (>= 256) for the library to take that form; the queries of
-one request are followed by two of a request without a full pool and then by
-another request's, so some blocks span requests."""
+one request are followed by eighteen of a request with at most one full pool
+(one 8-query block entirely its own) and then by another request's, so some
+blocks span requests."""
 import math
 import sys
 
@@ -31,9 +32,11 @@ def _say(msg):
 def _spec(name, H, D, kpool):
     rng = np.random.default_rng(H * 1000 + D + kpool)
     lengths, pads = [2600, 33, 1500], [7, 30, 0]
-    q_req = [0] * 700 + [1] * 2 + [2] * 401
-    q_pos = sorted(int(x) for x in rng.integers(0, 2600, size=700)) + [32, 31] + \
-        list(range(0, 1500, 3))[:401]
+    # queries 704..711 all belong to request 1, which has no full pool for
+    # kpool >= 4 (a block of its own); 696..703 and 712..719 span requests
+    q_req = [0] * 700 + [1] * 18 + [2] * 385
+    q_pos = sorted(int(x) for x in rng.integers(0, 2600, size=700)) + \
+        list(range(32, 14, -1)) + list(range(0, 1500, 3))[:385]
     return W.Spec(name, lengths=lengths, pads=pads, kpool=kpool, index_heads=H, index_dim=D,
                   hidden=256, select_k=8, out_width=8 * kpool, mla_heads=8, q_req=q_req,
                   q_pos=q_pos)
