@@ -161,9 +161,10 @@ dsa_status dsa_kpool_compress(const uint16_t* k, const uint16_t* gate, const uin
  * pool_valid, pool_off, n_pools as written by dsa_kpool_compress; q_req,
  * q_pos [Q] i32; scores [Q, pstride] f32; cand [Q, pstride] u8.
  * pstride >= every cap_r.
- * Performance: with Q >= 256 (prefill) the call reads each 256-pool block of
- * keys once per 8 consecutive queries, so queries of one request should be
- * consecutive in q_req; any order gives the same bits, only slower.
+ * Performance: with Q >= 256 and at least 256 (8-query block, 256-pool block)
+ * pairs (prefill-sized calls) the call reads each 256-pool block of keys once
+ * per 8 consecutive queries, so queries of one request should be consecutive
+ * in q_req; any order gives the same bits, only slower.
  * Errors: INVALID_ARG for H outside [1, 16], kpool outside [1, 8], pstride < 1,
  * Q < 0, NULL pointers; UNSUPPORTED for D not in {32, 64, 128, 256} or
  * Q > 65535.
