@@ -64,22 +64,25 @@ STAGE_SOURCE = {"head_gate": "head_gate.hip", "kpool_compress": "kpool_compress.
 
 def algorithmic_bytes(spec: W.Spec, xn: dict, n_pools: np.ndarray, tok: np.ndarray) -> dict:
     """Bytes each call must move at least once (inputs read once, outputs
-    written once), for the cached-pool decode step."""
+    written once), for the cached-pool decode step.  A pooled key or latent
+    row that several queries of one request use (prefill) counts once."""
     Q, H, D, Hm, L = spec.Q, spec.index_heads, spec.index_dim, spec.mla_heads, spec.latent
     kp = spec.kpool
-    req = np.asarray(xn["q_req"])
-    P_q = n_pools[req].astype(np.int64)               # pools scanned per query
+    req = np.asarray(xn["q_req"]).astype(np.int64)
+    P_r = int(n_pools[np.unique(req)].astype(np.int64).sum())  # pools of the requests queried
     pst = spec.pstride()
     touched = len(spec.lengths)                        # one pool per request
     lat_row = L * (1 if spec.latent_fp8 else 2) + (4 if spec.latent_fp8 else 0)
-    n_sel = int((tok >= 0).sum())
+    sel = tok >= 0                                     # distinct (request, row) pairs selected
+    n_sel = int(np.unique(req[:, None].repeat(tok.shape[1], 1)[sel] * (1 << 32)
+                          + tok[sel].astype(np.int64)).size)
     b = {
         "head_gate": 4 * (Q * spec.hidden + spec.hidden * H + Q * H),
         # kpool rows of k and gate per touched pool, ape, LN params, key + meta out,
         # the valid flags of each pool, offsets
         "kpool_compress": touched * (2 * kp * D * 2 + kp + D * 2 + 5) + kp * D * 2 + 8 * D
         + 4 * (2 * (spec.B + 1) + 2 * spec.B),
-        "index_scores": int(P_q.sum()) * (D * 2 + 5) + Q * H * (D * 2 + 4) + Q * pst * 5 + 12 * Q,
+        "index_scores": P_r * (D * 2 + 5) + Q * H * (D * 2 + 4) + Q * pst * 5 + 12 * Q,
         "topk_pools": Q * pst * 5 + Q * spec.select_k * 4,
         "expand_selection": Q * spec.select_k * 8 + Q * spec.out_width * 4 + 8 * Q,
         "sparse_mla_decode": n_sel * lat_row + Q * Hm * L * 2 * 2 + Q * spec.out_width * 4
