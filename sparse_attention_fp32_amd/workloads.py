@@ -25,7 +25,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
-from typing import List, Optional
+from typing import List, Optional, Tuple
 
 import numpy as np
 import torch
@@ -52,6 +52,8 @@ class Spec:
     eps: float = 1e-5
     always_select_tail: bool = False  # out_width then holds select_k*kpool + kpool-1 ids
     live: Optional[List[int]] = None  # live lengths inside the regions (None: the whole regions)
+    holes: Optional[List[Tuple[int, int]]] = None  # (request, local row) with valid = 0 after
+    #                                                the padding (validity holes)
 
     @property
     def B(self) -> int:
@@ -143,9 +145,11 @@ def spec_by_name(name: str, seed: int = 0) -> Spec:
                     index_dim=128, hidden=512, select_k=275, out_width=1100, mla_heads=64,
                     q_req=q_req, q_pos=q_pos)
     if name == "medium_live":    # live lengths inside larger regions, one query per request
+        # (with holes inside the live rows: a mid-request pool, and the tail of request 2)
         return Spec(name, lengths=[1000, 517, 2053], pads=[3, 0, 61], kpool=4, index_heads=16,
                     index_dim=128, hidden=1024, select_k=100, out_width=403, mla_heads=64,
-                    always_select_tail=True, live=[901, 398, 1990])
+                    always_select_tail=True, live=[901, 398, 1990],
+                    holes=[(0, 500), (1, 200), (2, 1989)])
     if name == "medium_prefill":  # causal prefill of two sequences and a request with no
         # full pool: many queries per request (the index scores' query-block form), one
         # block of 16 queries spanning all three requests, a short last block, and a
@@ -155,6 +159,14 @@ def spec_by_name(name: str, seed: int = 0) -> Spec:
         return Spec(name, lengths=[4100, 70, 2051], pads=[9, 67, 0], kpool=4, index_heads=16,
                     index_dim=128, hidden=512, select_k=32, out_width=128, mla_heads=64,
                     q_req=q_req, q_pos=q_pos)
+    if name == "medium_holes":   # validity holes after the first valid row: one just after
+        # it and two mid-request (those pools are not candidates), a hole inside two
+        # queries' tails, and a request whose only full pool holds a hole (no candidate)
+        return Spec(name, lengths=[1000, 517, 2053, 7], pads=[3, 0, 61, 2], kpool=4,
+                    index_heads=16, index_dim=128, hidden=1024, select_k=100, out_width=403,
+                    mla_heads=64, q_req=[0, 0, 1, 2, 2, 3], q_pos=[999, 206, 514, 2051, 700, 6],
+                    always_select_tail=True,
+                    holes=[(0, 4), (0, 205), (0, 403), (1, 513), (2, 1000), (2, 2050), (3, 4)])
     if name == "medium_fp8":
         return Spec(name, lengths=[777, 1500, 96, 2500], pads=[0, 17, 95, 5], kpool=8,
                     index_heads=12, index_dim=64, hidden=768, select_k=40, out_width=330,
@@ -163,7 +175,8 @@ def spec_by_name(name: str, seed: int = 0) -> Spec:
 
 
 WORKLOADS = ("tiny", "decode32k", "longctx", "prefill4k", "mixed64")
-PARITY_SHAPES = ("tiny", "medium", "medium_fp8", "medium_tail", "medium_pairs", "medium_prefill")
+PARITY_SHAPES = ("tiny", "medium", "medium_fp8", "medium_tail", "medium_pairs", "medium_prefill",
+                 "medium_holes")
 
 
 @dataclasses.dataclass
@@ -266,6 +279,9 @@ def make_inputs(spec: Spec, seed: int = 0, device: str = "cpu") -> Inputs:
     for r, p in enumerate(spec.pads):
         if p:
             valid[int(offs[r]):int(offs[r]) + p] = 0
+    for r, row in spec.holes or ():
+        assert 0 <= row < spec.lengths[r], (r, row)
+        valid[int(offs[r]) + row] = 0
 
     qi = _bf16_bits(s.normal((Q, H, D)))
     q_mla = _bf16_bits(s.normal((Q, Hm, L)))

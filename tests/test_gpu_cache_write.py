@@ -206,14 +206,9 @@ def test_live_decode_graph(post_ln, fused):
               "pool_valid": _np(st.pool_valid)[:ncap], "n_pools": _np(st.n_pools)}
         PT.check_compress(gk, ref)
         PT.check_gate(_np(st.w), ref["w"])
-        sel_g, tok_g = _np(st.sel), _np(st.tok)
-        out_g, lse_g = _np(st.out), _np(st.lse)
-        for q in range(B):
-            ok, nd = PT.boundary_ok(sel_g[q], ref["sel"][q], ref["scores"][q], PT.CHAIN_GAP_REL)
-            assert ok, f"step {step} selection row {q}: {nd} pools differ away from the boundary"
-            if nd == 0:
-                assert np.array_equal(tok_g[q], ref["tok"][q]), (step, q)
-                PT.check_mla(out_g, lse_g, ref["out_f64"], ref["lse"], rows=[q])
+        nd = PT.check_chained_rows(_np(st.sel), _np(st.tok), _np(st.out), _np(st.lse), ref,
+                                   PT.oracle_expect(xo, spec, ref["pool_start"]))
+        _say(f"live decode step {step}: boundary swaps {nd}")
 
 
 @pytest.mark.parametrize("post_ln", [True, False])

@@ -60,15 +60,8 @@ def test_fullsize(name):
         g = {"keys": _np(st.keys).view(np.uint16)[:ncap], "pool_start": _np(st.pool_start)[:ncap],
              "pool_valid": _np(st.pool_valid)[:ncap], "n_pools": _np(st.n_pools)}
         flips = PT.check_compress(g, ref, requests=reqs, pool_off=xn["pool_off"])
-        sel_g, tok_g, out_g, lse_g = _np(st.sel), _np(st.tok), _np(st.out), _np(st.lse)
-        ndiff = 0
-        for q in sample:
-            ok, nd = PT.boundary_ok(sel_g[q], ref["sel"][q], ref["scores"][q], PT.CHAIN_GAP_REL)
-            assert ok, f"{label} selection q={q}: {nd} pools differ away from the boundary"
-            ndiff += nd
-            if nd == 0:
-                assert np.array_equal(tok_g[q], ref["tok"][q])
-                PT.check_mla(out_g, lse_g, ref["out_f64"], ref["lse"], rows=[q])
+        ndiff = PT.check_chained_rows(_np(st.sel), _np(st.tok), _np(st.out), _np(st.lse), ref,
+                                      PT.oracle_expect(xn, spec, ref["pool_start"]), rows=sample)
         _say(f"fullsize {name}: {label} ok; key ulp flips in sample {flips}, boundary swaps {ndiff}")
 
     # the fused decode calls the bench times: full compression, then the cached-pool step

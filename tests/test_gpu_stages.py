@@ -321,14 +321,9 @@ def test_chain(case):
     st = _step(xg)
     st.run()
     PT.check_gate(_np(st.w), ref["w"])
-    s_g = _np(st.scores)
-    sel_g, tok_g = _np(st.sel), _np(st.tok)
-    for q in range(spec.Q):
-        ok, nd = PT.boundary_ok(sel_g[q], ref["sel"][q], ref["scores"][q], PT.CHAIN_GAP_REL)
-        assert ok, f"chained selection row {q}: {nd} pools differ away from the boundary"
-        if nd == 0:
-            assert np.array_equal(tok_g[q], ref["tok"][q])
-            PT.check_mla(_np(st.out), _np(st.lse), ref["out_f64"], ref["lse"], rows=[q])
+    nd = PT.check_chained_rows(_np(st.sel), _np(st.tok), _np(st.out), _np(st.lse), ref,
+                               PT.oracle_expect(xn, spec, ref["pool_start"]))
+    _say(f"chain {spec.name}: boundary swaps {nd}")
 
 
 def test_determinism_and_duplicate_rows(case):
@@ -445,13 +440,9 @@ def test_fused_chain(case):
         _poison(t)
     st.run_fused()
     PT.check_gate(_np(st.w), ref["w"])
-    sel_g, tok_g = _np(st.sel), _np(st.tok)
-    for q in range(spec.Q):
-        ok, nd = PT.boundary_ok(sel_g[q], ref["sel"][q], ref["scores"][q], PT.CHAIN_GAP_REL)
-        assert ok, f"fused selection row {q}: {nd} pools differ away from the boundary"
-        if nd == 0:
-            assert np.array_equal(tok_g[q], ref["tok"][q])
-            PT.check_mla(_np(st.out), _np(st.lse), ref["out_f64"], ref["lse"], rows=[q])
+    nd = PT.check_chained_rows(_np(st.sel), _np(st.tok), _np(st.out), _np(st.lse), ref,
+                               PT.oracle_expect(xn, spec, ref["pool_start"]))
+    _say(f"fused chain {spec.name}: boundary swaps {nd}")
     # the cached-pool step after it gives the same outputs (nothing changed)
     a = [_np(t).copy() for t in (st.w, st.scores, st.sel, st.tok, st.out, st.lse)]
     st.run_fused(incremental=True)
