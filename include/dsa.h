@@ -302,6 +302,35 @@ dsa_status dsa_sparse_mla_decode_paged(const uint16_t* q, const void* ckv, const
                                        float* lse, int32_t* kvidx, void* ws, size_t ws_bytes,
                                        hipStream_t stream);
 
+/* -------------------------------------------------------------------------
+ * dsa_sparse_mla_decode_noalloc -- dsa_sparse_mla_decode without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, kernels, results (bit for bit) and errors as
+ * dsa_sparse_mla_decode, except ws / ws_bytes: the per-chunk partials go to a
+ * fixed array of DSA_MLA_SCRATCH_BYTES inside the library, one per GPU,
+ * allocated when the library's code is loaded on that GPU and held until the
+ * process ends.  The call itself allocates and frees nothing.  Its device
+ * address is looked up (hipGetSymbolAddress) on the first call on each device,
+ * with that device current.
+ * Every call on one GPU shares that GPU's array, and the array keeps what the
+ * last call wrote (nothing in it needs to start at zero): calls that overlap
+ * on one GPU (two streams, two threads) race and give wrong results.
+ * Errors: those of dsa_sparse_mla_decode; UNSUPPORTED when
+ * dsa_sparse_mla_decode_workspace_size(Q, Hm, L, out_width, latent_dtype)
+ * exceeds DSA_MLA_SCRATCH_BYTES (nothing is launched); INVALID_ARG when the
+ * stream belongs to a device other than the current one; LAUNCH when the
+ * array's address cannot be found.
+ * ------------------------------------------------------------------------- */
+#define DSA_MLA_SCRATCH_BYTES (32u << 20)
+dsa_status dsa_sparse_mla_decode_noalloc(const uint16_t* q, const void* ckv,
+                                         const float* ckv_scale, int latent_dtype,
+                                         const int32_t* kv_off, const int32_t* q_req,
+                                         const int32_t* tok, int Q, int Hm, int L, int out_width,
+                                         float sm_scale, uint16_t* out, float* lse,
+                                         hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * The cache-write side of a decode step   [Atlas page, Glm5NextDsaKernels:
  *     write_geom (the step's selector geometry derived on the device from

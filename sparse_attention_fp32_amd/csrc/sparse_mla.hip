@@ -40,8 +40,16 @@
 // numbers to the table row, so no id can address memory outside them.
 #include <limits.h>
 
+#include <mutex>
+
 #include "dsa_device.hpp"
 #include "dsa_host.hpp"
+
+// Workspace of dsa_sparse_mla_decode_noalloc: a fixed array in device memory,
+// one per GPU the library runs on, held until the process ends.  In host code
+// its name is only a host-side stand-in: kernels receive the device address
+// that hipGetSymbolAddress returns for the current device (scratch_address).
+static __device__ __align__(256) uint8_t scratch[DSA_MLA_SCRATCH_BYTES];
 
 namespace {
 
@@ -517,10 +525,44 @@ DSA_EXPORT size_t dsa_sparse_mla_decode_workspace_size(int Q, int Hm, int L_, in
 
 namespace {
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];  // device address of `scratch` per device (null: not yet)
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.  The stream must belong to the
+// current device: the address is that device's.
+dsa_status scratch_address(hipStream_t stream, void** addr, const char* who) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  DSA_REQUIRE(e == hipSuccess && dev >= 0 && dev < kMaxDevices, DSA_ERR_LAUNCH,
+              "%s: hipGetDevice: %s (device %d)", who, hipGetErrorString(e), dev);
+  if (stream) {
+    int sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    DSA_REQUIRE(e == hipSuccess, DSA_ERR_INVALID_ARG, "%s: hipStreamGetDevice: %s", who,
+                hipGetErrorString(e));
+    DSA_REQUIRE(sdev == dev, DSA_ERR_INVALID_ARG,
+                "%s: the stream belongs to device %d, the current device is %d", who, sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    DSA_REQUIRE(e == hipSuccess && p, DSA_ERR_LAUNCH, "%s: hipGetSymbolAddress(scratch): %s",
+                who, hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return DSA_OK;
+}
+
+
 dsa_status launch_mla(const uint16_t* q, const void* ckv, const float* ckv_scale, int latent_dtype,
                       const CacheMap& cm, bool paged, const int32_t* q_req, const int32_t* tok,
                       int Q, int Hm, int L_, int out_width, float sm_scale, uint16_t* out,
-                      float* lse, void* ws, size_t ws_bytes, hipStream_t stream, const char* who) {
+                      float* lse, void* ws, size_t ws_bytes, hipStream_t stream, const char* who,
+                      bool use_scratch = false) {
   DSA_REQUIRE(L_ == L, DSA_ERR_UNSUPPORTED,
               "%s: latent width L=%d, the kernels read exactly %d (a NoPE cache row is "
               "kv_lora_rank wide)",
@@ -547,6 +589,18 @@ dsa_status launch_mla(const uint16_t* q, const void* ckv, const float* ckv_scale
   DSA_REQUIRE_ALIGNED(who, q, ckv, ckv_scale, cm.kv_off, cm.block_table, cm.kvidx, q_req, tok, out,
                       lse, ws);
   const size_t need = dsa_sparse_mla_decode_workspace_size(Q, Hm, L_, out_width, latent_dtype);
+  if (use_scratch) {  // the library's fixed array instead of a workspace argument
+    DSA_REQUIRE(need <= (size_t)DSA_MLA_SCRATCH_BYTES, DSA_ERR_UNSUPPORTED,
+                "%s: Q=%d Hm=%d out_width=%d need %zu bytes of workspace, above the library's "
+                "fixed %zu (use dsa_sparse_mla_decode with a workspace)",
+                who, Q, Hm, out_width, need, (size_t)DSA_MLA_SCRATCH_BYTES);
+    ws = nullptr;
+    ws_bytes = need;
+    if (need > 0) {
+      const dsa_status st = scratch_address(stream, &ws, who);
+      if (st != DSA_OK) return st;
+    }
+  }
   DSA_REQUIRE(ws_bytes >= need && (need == 0 || ws), DSA_ERR_INVALID_ARG,
               "%s: workspace %zu bytes, need %zu", who, ws_bytes, need);
   const Chunking ch = mla_chunking(Q, Hm, out_width);
@@ -596,6 +650,19 @@ DSA_EXPORT dsa_status dsa_sparse_mla_decode(const uint16_t* q, const void* ckv,
   CacheMap cm{kv_off, nullptr, 0, 0, 0, nullptr};
   return launch_mla(q, ckv, ckv_scale, latent_dtype, cm, false, q_req, tok, Q, Hm, L_, out_width,
                     sm_scale, out, lse, ws, ws_bytes, stream, "dsa_sparse_mla_decode");
+}
+
+
+DSA_EXPORT dsa_status dsa_sparse_mla_decode_noalloc(const uint16_t* q, const void* ckv,
+                                                    const float* ckv_scale, int latent_dtype,
+                                                    const int32_t* kv_off, const int32_t* q_req,
+                                                    const int32_t* tok, int Q, int Hm, int L_,
+                                                    int out_width, float sm_scale, uint16_t* out,
+                                                    float* lse, hipStream_t stream) {
+  CacheMap cm{kv_off, nullptr, 0, 0, 0, nullptr};
+  return launch_mla(q, ckv, ckv_scale, latent_dtype, cm, false, q_req, tok, Q, Hm, L_, out_width,
+                    sm_scale, out, lse, nullptr, 0, stream, "dsa_sparse_mla_decode_noalloc",
+                    /*use_scratch=*/true);
 }
 
 DSA_EXPORT dsa_status dsa_sparse_mla_decode_paged(

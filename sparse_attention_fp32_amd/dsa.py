@@ -22,6 +22,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "dsa.h")
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_LAUNCH = 0, 1, 2, 3
 LATENT_BF16, LATENT_FP8_E4M3 = 0, 1
 MAX_KPOOL, KV_LORA, MAX_INDEX_HEADS, MAX_TOPK_ROW = 8, 512, 16, 16384
+MLA_SCRATCH_BYTES = 32 << 20
 
 _lib = None
 
@@ -46,6 +47,8 @@ _SIGS = {
                                    _Z, _P]),
     "dsa_sparse_mla_decode_paged": (_I, [_P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _I, _I, _I, _I,
                                          _F, _P, _P, _P, _P, _Z, _P]),
+    "dsa_sparse_mla_decode_noalloc": (_I, [_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _F, _P,
+                                           _P, _P]),
     "dsa_gate_split_count": (_I, [_I, _I, _I]),
     "dsa_gate_compress_workspace_size": (_Z, [_I, _I, _I]),
     "dsa_gate_compress": (_I, [_P, _P, _I, _I, _I, _P, _Z, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -226,6 +229,22 @@ def dsa_sparse_mla_decode(q, ckv, ckv_scale, kv_off, q_req, tok, sm_scale: float
         _dev(kv_off, _I32, "kv_off"), _dev(q_req, _I32, "q_req"), _dev(tok, _I32, "tok"), Q, Hm, L,
         out_width, float(sm_scale), _dev(out, _BF, "out"), _dev(lse, torch.float32, "lse", allow_none=True),
         wp, wb, _stream(stream)))
+
+
+def dsa_sparse_mla_decode_noalloc(q, ckv, ckv_scale, kv_off, q_req, tok, sm_scale: float, out,
+                                  lse=None, stream=None) -> None:
+    """dsa_sparse_mla_decode with the library's fixed per-GPU workspace (no
+    workspace argument; the call allocates nothing)."""
+    Q, Hm, L = q.shape
+    out_width = tok.shape[1]
+    fp8 = ckv.dtype in (torch.uint8, torch.float8_e4m3fn)
+    dt = LATENT_FP8_E4M3 if fp8 else LATENT_BF16
+    _check(lib().dsa_sparse_mla_decode_noalloc(
+        _dev(q, _BF, "q"), _dev(ckv, (torch.uint8, torch.float8_e4m3fn) if fp8 else _BF, "ckv"),
+        _dev(ckv_scale, torch.float32, "ckv_scale", allow_none=not fp8), dt,
+        _dev(kv_off, _I32, "kv_off"), _dev(q_req, _I32, "q_req"), _dev(tok, _I32, "tok"), Q, Hm, L,
+        out_width, float(sm_scale), _dev(out, _BF, "out"), _dev(lse, torch.float32, "lse", allow_none=True),
+        _stream(stream)))
 
 
 def dsa_sparse_mla_decode_paged(q, ckv, ckv_scale, block_table, page_rows: int, q_req, tok,

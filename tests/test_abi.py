@@ -22,7 +22,7 @@ def _misaligned(code):
 
 def test_exports_every_declared_function():
     names = dsa.header_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     import subprocess
     out = subprocess.run(["nm", "-D", "--defined-only", dsa.LIB_PATH], capture_output=True, text=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
@@ -265,3 +265,18 @@ def test_lane_read_errors():
     assert L.dsa_lane_read(NUL, 16, FAKE, NUL) == INV
     assert _misaligned(L.dsa_lane_read(MIS, 16, FAKE, NUL))
     assert L.dsa_lane_read(NUL, 0, NUL, NUL) == dsa.DSA_OK
+
+
+def test_mla_noalloc_errors():
+    """The allocation-free attention call refuses before it looks for its
+    array or launches: partials beyond the fixed array, and the workspace
+    call's own argument errors."""
+    L = dsa.lib()
+    f = L.dsa_sparse_mla_decode_noalloc
+    assert f(FAKE, FAKE, NUL, 0, FAKE, FAKE, FAKE, 256, 64, 512, 4096, 1.0, FAKE, NUL, NUL) == UNS
+    assert "fixed" in dsa.last_error()
+    assert dsa.sparse_mla_decode_workspace_size(256, 64, 512, 4096, 0) > dsa.MLA_SCRATCH_BYTES
+    assert f(FAKE, FAKE, NUL, 0, FAKE, FAKE, FAKE, 4, 64, 576, 2048, 1.0, FAKE, NUL, NUL) == UNS
+    assert f(FAKE, FAKE, NUL, 0, FAKE, FAKE, FAKE, 4, 0, 512, 2048, 1.0, FAKE, NUL, NUL) == INV
+    assert f(FAKE, FAKE, NUL, 1, FAKE, FAKE, FAKE, 4, 64, 512, 2048, 1.0, FAKE, NUL, NUL) == INV
+    assert f(FAKE, FAKE, NUL, 0, FAKE, FAKE, FAKE, 0, 64, 512, 2048, 1.0, FAKE, NUL, NUL) == dsa.DSA_OK
