@@ -67,8 +67,6 @@ typedef int dsa_status;
 #define DSA_KV_LORA 512
 /* Most indexer heads one head-gate row / index_scores call supports. */
 #define DSA_MAX_INDEX_HEADS 16
-/* Longest score row dsa_topk_pools handles. */
-#define DSA_MAX_TOPK_ROW 16384
 
 int dsa_abi_version(void);
 const char* dsa_last_error(void);
@@ -188,9 +186,11 @@ dsa_status dsa_index_scores(const uint16_t* qi, const float* w, const uint16_t* 
  * row_len [Q] i32 or NULL: only entries p < row_len[q] of row q count
  * (clamped to [0, pstride]; NULL means pstride), for rows shorter than the
  * batch's widest.
+ * Any row length is taken: rows of up to 16384 entries stay in registers,
+ * longer ones are read again from memory on each pass of the select (the
+ * select is tiled over the row).
  * No workspace is needed at present (size 0; ws may be NULL).
- * Errors: INVALID_ARG for select_k < 1, pstride < 1, Q < 0, NULL pointers;
- * UNSUPPORTED for pstride > DSA_MAX_TOPK_ROW.
+ * Errors: INVALID_ARG for select_k < 1, pstride < 1, Q < 0, NULL pointers.
  * ------------------------------------------------------------------------- */
 size_t dsa_topk_pools_workspace_size(int Q, int pstride, int select_k);
 dsa_status dsa_topk_pools(const float* scores, const uint8_t* cand, const int32_t* row_len, int Q,

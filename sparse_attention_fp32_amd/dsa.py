@@ -21,7 +21,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "dsa.h")
 
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_LAUNCH = 0, 1, 2, 3
 LATENT_BF16, LATENT_FP8_E4M3 = 0, 1
-MAX_KPOOL, KV_LORA, MAX_INDEX_HEADS, MAX_TOPK_ROW = 8, 512, 16, 16384
+MAX_KPOOL, KV_LORA, MAX_INDEX_HEADS = 8, 512, 16
 MLA_SCRATCH_BYTES = 32 << 20
 
 _lib = None

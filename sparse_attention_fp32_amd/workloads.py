@@ -18,6 +18,9 @@ kpool pooling, a 512-wide NoPE latent, 64 MLA heads.
 * ``prefill4k``  one causal sequence of 4096 rows with 4096 queries.
 * ``mixed64``    64 requests with log-uniform lengths in [1024, 65536], six of
                  them mostly padding, fp8-e4m3 latent with a per-row scale.
+* ``decode262k`` one request of 262,144 cached rows (the context GLM-5.3 is
+                 advertised at, per the page's MASKED_ATTN_MAX_KEYS note):
+                 65,536 pools in one score row.
 
 ``N(0, v)`` below always names the variance ``v``.
 """
@@ -106,6 +109,9 @@ def spec_by_name(name: str, seed: int = 0) -> Spec:
         return Spec(name, lengths=[131072, 98304, 65537, 40000], pads=pads, kpool=8,
                     index_heads=16, index_dim=128, hidden=4096, select_k=256,
                     out_width=2048, mla_heads=64, gate_var=2.0)
+    if name == "decode262k":   # one request at the 262,144-token context the model advertises
+        return Spec(name, lengths=[262144], pads=[0], kpool=4, index_heads=16, index_dim=128,
+                    hidden=4096, select_k=512, out_width=2048, mla_heads=64)
     if name == "prefill4k":
         return Spec(name, lengths=[4096], pads=[0], kpool=4, index_heads=16, index_dim=128,
                     hidden=4096, select_k=64, out_width=256, mla_heads=64,
@@ -174,7 +180,7 @@ def spec_by_name(name: str, seed: int = 0) -> Spec:
     raise KeyError(name)
 
 
-WORKLOADS = ("tiny", "decode32k", "longctx", "prefill4k", "mixed64")
+WORKLOADS = ("tiny", "decode32k", "longctx", "prefill4k", "mixed64", "decode262k")
 PARITY_SHAPES = ("tiny", "medium", "medium_fp8", "medium_tail", "medium_pairs", "medium_prefill",
                  "medium_holes")
 

@@ -96,7 +96,9 @@ def test_topk_errors():
     L = dsa.lib()
     assert L.dsa_topk_pools(FAKE, FAKE, NUL, 4, 100, 0, FAKE, NUL, 0, NUL) == INV
     assert L.dsa_topk_pools(FAKE, FAKE, NUL, 4, 0, 8, FAKE, NUL, 0, NUL) == INV
-    assert L.dsa_topk_pools(FAKE, FAKE, NUL, 4, dsa.MAX_TOPK_ROW + 1, 8, FAKE, NUL, 0, NUL) == UNS
+    # no row-length cap: a long row passes validation (NULL sel then fails it)
+    assert L.dsa_topk_pools(FAKE, FAKE, NUL, 4, 1 << 20, 8, NUL, NUL, 0, NUL) == INV
+    assert "NULL" in dsa.last_error()
     assert L.dsa_topk_pools(NUL, FAKE, NUL, 4, 100, 8, FAKE, NUL, 0, NUL) == INV
     assert _misaligned(L.dsa_topk_pools(FAKE, MIS, NUL, 4, 100, 8, FAKE, NUL, 0, NUL))
     assert _misaligned(L.dsa_topk_pools(FAKE, FAKE, MIS, 4, 100, 8, FAKE, NUL, 0, NUL))

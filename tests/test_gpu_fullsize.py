@@ -20,6 +20,7 @@ SAMPLES = {
     "longctx": [0, 1, 2, 3],
     "prefill4k": [0, 1, 2, 3, 100, 254, 255, 1000, 2047, 4095],
     "mixed64": None,   # the six mostly-padded requests plus six others
+    "decode262k": [0],
 }
 
 

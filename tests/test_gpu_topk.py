@@ -1,6 +1,8 @@
 """Top-k on adversarial score rows, exact against the oracle: ties, all-equal
 rows, negative rows, rows spanning more than 15 octaves, rows with fewer
-candidates than select_k, and every per-thread register tile size."""
+candidates than select_k, every per-thread register tile size, and rows
+longer than the register tile (up to 65,536 pools, the pools of a 262,144-row
+context at kpool 4)."""
 import zlib
 
 import numpy as np
@@ -37,6 +39,12 @@ CASES += [(8192, 512, "equal"), (8192, 512, "negative"), (4096, 100, "zeros"),
           (16384, 256, "negative"), (1024, 2000, "normal"),
           # budgets above the 2048 staged in LDS take the direct-store path
           (16384, 4000, "normal"), (8192, 3000, "ties"), (4096, 2049, "wide")]
+# rows longer than one register step (16384 pools), read again on each pass:
+# 262,144 rows at kpool 4 give 65,536 pools
+CASES += [(P, k, kind) for P in (16385, 32768, 65536) for k in (1, 512)
+          for kind in ("normal", "ties", "wide")]
+CASES += [(65536, 512, "equal"), (65536, 512, "negative"), (40000, 100, "zeros"),
+          (65536, 2048, "normal"), (65536, 4000, "ties"), (32768, 20000, "wide")]
 
 
 def _seed(*parts):
@@ -103,8 +111,9 @@ def test_topk_exact(P, k, kind):
     assert np.array_equal(out.cpu().numpy(), ref)
 
 
-ROW_LEN_CASES = [(P, k, kind) for P in (30, 2047, 8192, 16384) for k in (1, 64, 512)
-                 for kind in ("normal", "ties")] + [(4096, 2049, "wide"), (8192, 3000, "ties")]
+ROW_LEN_CASES = [(P, k, kind) for P in (30, 2047, 8192, 16384, 65536) for k in (1, 64, 512)
+                 for kind in ("normal", "ties")] + [(4096, 2049, "wide"), (8192, 3000, "ties"),
+                                                    (40000, 3000, "ties")]
 
 
 @pytest.mark.parametrize("P,k,kind", ROW_LEN_CASES)
