@@ -9,15 +9,16 @@ calls (gate+compress, gated index scores, top-k+expand, sparse MLA) over one bat
 resident synthetic input: the 32K-context decode batch (16 requests x 32768
 cached rows, one query each) by default.  Eight input sets (each larger than
 the 256 MB last-level cache together with its outputs) are rotated so that
-every step streams its keys and latent rows from HBM.  The eight sets' steps
-are captured in sequence in one HIP graph, as a serving loop captures
-consecutive decode steps; the timed region replays it K/8 times (a remainder
-replays single-step graphs), so K steps run.  Single-step graphs (one per
-set) are timed too, and replayed with two batches in flight (two streams), which
-shows how much of the step is fixed latency rather than throughput.  The same
-step through the six separate calls is timed too, for comparison, and the
-step with the attention reading a paged copy of the latent cache (64-row pages
-in shuffled order, through a block table), and the whole decode step from
+every step streams its keys and latent rows from HBM.  Each set's step is
+captured in a HIP graph of its own, and the timed region launches one graph
+per step, K steps in all (five equal segments give the median per-step time
+too).  Beside it: the eight sets' steps captured in sequence in one graph (as
+a serving loop captures consecutive decode steps, which spreads the host's
+graph-launch cost), the single-step graphs replayed with two batches in
+flight (two streams, showing how much of the step is fixed latency rather
+than throughput), the same step through the six separate calls, the step with
+the attention reading a paged copy of the latent cache (64-row pages in
+shuffled order, through a block table), and the whole decode step from
 device-side live lengths (geometry, the store of the step's indexer row, the
 fused calls, the paged attention).
 
@@ -27,7 +28,7 @@ back-to-back calls of that kind, replayed between HIP events on the launch
 stream),
 against the 8 TB/s HBM peak and against the lane (a plain coalesced read of
 1 GiB, dsa_lane_read, timed in the same run); and the CPU oracle's throughput on a bounded
-sample of the same workload (rank 0 only).
+sample of the same workload, run on every host core before the GPU is used.
 """
 from __future__ import annotations
 
@@ -49,6 +50,7 @@ from sparse_attention_fp32_amd import workloads as W  # noqa: E402
 from sparse_attention_fp32_amd.pipeline import DsaStep  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
 # the calls of the timed step (the fused decode calls) ...
 STAGES = ("gate_compress", "index_scores_gated", "topk_expand", "sparse_mla_decode")
 # ... and the six separate calls, timed for comparison
@@ -103,24 +105,44 @@ def source_sha(stage: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def stored_traffic(stage: str, workload: str):
-    """HBM bytes per launch measured with rocprofv3 counters, if a summary for
-    this kernel source and workload is stored in profiles/."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.txt")
-    if not os.path.exists(p):
+# kernels behind each call, by name (counters of a call add up over its kernels)
+CALL_KERNELS = {
+    "sparse_mla_decode": (r"sparse_mla_kernel<(true|false), false>", r"mla_combine_kernel"),
+    "index_scores_gated": (r"index_scores(_qblock)?_kernel<\d+, true",),
+    "topk_expand": (r"topk_kernel<\d+, \d+, (true|false), true>",),
+    "index_scores": (r"index_scores(_qblock)?_kernel<\d+, false",),
+    "topk_pools": (r"topk_kernel<\d+, \d+, (true|false), false>",),
+}
+
+
+def stored_counters(stage: str, workload: str):
+    """HBM bytes per launch (FETCH_SIZE and WRITE_SIZE scaled by the copy
+    calibration) and MFMA / VALU busy of a call's kernels, from the rocprofv3
+    summary stored in profiles/counters_<workload>.json, if it was taken on
+    this call's current kernel source.  For each kernel of the call the grid
+    launched most often (the timed step's) counts."""
+    import re
+    p = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
+    if stage not in CALL_KERNELS or not os.path.exists(p):
         return None
-    kv = {}
     with open(p) as f:
-        for line in f:
-            if "=" in line and not line.startswith("#"):
-                k, v = line.strip().split("=", 1)
-                kv[k.strip()] = v.strip()
-    if kv.get("source_sha") != source_sha(stage):
+        rows = json.load(f)["kernels"]
+    cur = source_sha(stage)
+    picked = []
+    for pat in CALL_KERNELS[stage]:
+        cand = [r for r in rows if re.match(pat, r["kernel"])]
+        if not cand:
+            continue
+        r = max(cand, key=lambda r: r.get("dispatches", 0))
+        if r["source_sha"] != cur:
+            return None
+        picked.append(r)
+    if not picked:
         return None
-    try:
-        return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+    main = picked[0]
+    return {"hbm_bytes": sum(r["fetch_bytes"] + r["write_bytes"] for r in picked),
+            "mfma_util_pct": round(main["mfma_util_pct"], 2),
+            "valu_busy_pct": round(main["valu_busy_pct"], 2), "kernel": main["kernel"]}
 
 
 def _cpu_worker(xn, spec, q, core, budget_s, start, results):
@@ -307,26 +329,36 @@ def main():
         med = seg[len(seg) // 2] if seg else None
         return ev[0].elapsed_time(e1), time.perf_counter() - t0, med
 
-    def timed(graphs, n, warm):
+    def timed(graphs, n, warm, segments=1):
+        """n steps, one graph replay each (graphs in rotation); events split
+        them into `segments` runs of equal length.  Returns the total time
+        (ms), the wall time and the median per-step time of the segments (us)."""
         for i in range(warm):
             graphs[i % len(graphs)].replay()
         torch.cuda.synchronize()
+        nseg = max(1, min(segments, n))
+        bounds = [n * i // nseg for i in range(nseg + 1)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(nseg + 1)]
         t0 = time.perf_counter()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        ev[0].record()
         for i in range(n):
             graphs[i % len(graphs)].replay()
-        e1.record()
+            if i + 1 in bounds[1:]:
+                ev[bounds.index(i + 1)].record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1), time.perf_counter() - t0
+        seg = sorted(ev[j].elapsed_time(ev[j + 1]) / (bounds[j + 1] - bounds[j]) * 1e3
+                     for j in range(nseg) if bounds[j + 1] > bounds[j])
+        return ev[0].elapsed_time(ev[-1]), time.perf_counter() - t0, seg[len(seg) // 2]
 
-    # the step: the fused decode calls over cached pools
+    # the step: the fused decode calls over cached pools, one graph launch per
+    # step (the timed figure); the same steps replayed as graphs of eight
+    # consecutive steps are reported beside it
     graphs = capture(lambda st: st.run_fused(incremental=True))
     gseq = capture_seq(lambda st: st.run_fused(incremental=True))
-    ms, wall, seg_med_us = timed_seq(gseq, graphs, a.steps, a.warmup)
+    ms, wall, seg_med_us = timed(graphs, a.steps, a.warmup, segments=5)
     ms_per_step = ms / a.steps
-    ms1, _ = timed(graphs, a.steps, a.warmup)  # the same steps as single-step graphs
     qps = spec.Q * a.steps / (ms / 1e3)
+    ms8, _, seg_med8_us = timed_seq(gseq, graphs, a.steps, a.warmup)
     # the same step graphs with two batches in flight: set i replays on side
     # stream i mod 2 (default priority), bracketed by events on the launch stream
     side = [torch.cuda.Stream(), torch.cuda.Stream()]
@@ -351,7 +383,7 @@ def main():
                   "unit": "queries/s", "us_per_step": round(ms2 / n2 * 1e3, 2)}
     # the same step through the six separate calls, for comparison
     graphs6 = capture(lambda st: st.run(incremental=True))
-    ms6, _ = timed(graphs6, max(1, a.steps // 4), max(1, a.warmup // 4))
+    ms6, _, _ = timed(graphs6, max(1, a.steps // 4), max(1, a.warmup // 4))
     six_us = ms6 / max(1, a.steps // 4) * 1e3
     del graphs6
     # the same step with the attention over a paged copy of the latent cache
@@ -360,7 +392,7 @@ def main():
         for i, st in enumerate(steps):
             st.pc = W.make_paged_cache(sets[i], a.page_rows, seed=i)
         graphs_p = capture(lambda st: st.run_fused(incremental=True, paged=st.pc))
-        ms_p, _ = timed(graphs_p, max(1, a.steps // 4), max(1, a.warmup // 4))
+        ms_p, _, _ = timed(graphs_p, max(1, a.steps // 4), max(1, a.warmup // 4))
         paged = {"page_rows": a.page_rows,
                  "table_cols": int(steps[0].pc.block_table.shape[1]),
                  "step_us": round(ms_p / max(1, a.steps // 4) * 1e3, 2)}
@@ -379,11 +411,11 @@ def main():
         st.slot = torch.empty(spec.B, dtype=torch.int32, device=dev)
     graphs_l = capture(lambda st: st.run_live(st.k_new, st.gate_new, paged=getattr(st, "pc", None),
                                               slot=st.slot if paged is not None else None))
-    ms_l, _ = timed(graphs_l, max(1, a.steps // 4), max(1, a.warmup // 4))
+    ms_l, _, _ = timed(graphs_l, max(1, a.steps // 4), max(1, a.warmup // 4))
     del graphs_l
     graphs_l = capture(lambda st: st.run_live(st.k_new, st.gate_new, paged=getattr(st, "pc", None),
                                               fused=True))
-    ms_lf, _ = timed(graphs_l, max(1, a.steps // 4), max(1, a.warmup // 4))
+    ms_lf, _, _ = timed(graphs_l, max(1, a.steps // 4), max(1, a.warmup // 4))
     del graphs_l
     live = {"step_us": round(ms_l / max(1, a.steps // 4) * 1e3, 2),
             "fused_step_us": round(ms_lf / max(1, a.steps // 4) * 1e3, 2)}
@@ -427,7 +459,7 @@ def main():
     reps = max(1, a.stage_reps // kCallsPerGraph)
     for name, fn in fns.items():
         g = call_graph(fn)
-        ms_c, _ = timed([g], reps, 1)
+        ms_c, _, _ = timed([g], reps, 1)
         call_us[name] = ms_c / (reps * kCallsPerGraph) * 1e3
         del g
     stage_us = {k: call_us[k] for k in STAGES}
@@ -459,11 +491,23 @@ def main():
     step_bytes = sum(nb[k] for k in STAGES)
     dom = max(STAGES, key=lambda n: stage_us[n])
     ach = nb[dom] / (stage_us[dom] * 1e-6) / 1e9
-    traffic = stored_traffic(dom, spec.name)
+    ctr = stored_counters(dom, spec.name)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": None if ctr is None else int(ctr["hbm_bytes"]),
                 "algorithmic_bytes": int(nb[dom]), "avg_launch_us": round(stage_us[dom], 2),
                 "lane_GBps": round(lane_gbs, 1), "frac_of_lane": round(ach / lane_gbs, 4)}
+    if dom == "sparse_mla_decode":
+        # the attention's dense MFMA work over the selected rows (QK and PV)
+        n_tok = int((steps[0].tok >= 0).sum().item())
+        fl = 4.0 * spec.latent * spec.mla_heads * n_tok
+        roofline["mfma"] = {"flops": int(fl), "achieved_TFLOPs": round(fl / (stage_us[dom] * 1e-6) / 1e12, 1),
+                            "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                            "frac": round(fl / (stage_us[dom] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if ctr is not None:
+        roofline["counters"] = {"kernel": ctr["kernel"], "MfmaUtil_pct": ctr["mfma_util_pct"],
+                                "VALUBusy_pct": ctr["valu_busy_pct"],
+                                "source": f"profiles/counters_{spec.name}.json"}
 
     line = {
         "metric": "DSA decode queries/s (gate+indexer+top-k+sparse MLA) and % of HBM peak",
@@ -487,11 +531,17 @@ def main():
                    "latent_dtype": "fp8_e4m3" if spec.latent_fp8 else "bf16",
                    "pools": "cached; the step recompresses the pool of its newest row",
                    "input_sets": a.sets,
-                   "graph": "one HIP graph of eight consecutive steps (one per input set), "
-                            "each the fused decode calls (gate+compress, gated index scores, "
+                   "graph": "one HIP graph per step (the input sets in rotation), each "
+                            "the fused decode calls (gate+compress, gated index scores, "
                             "top-k+expand, sparse MLA)"},
-        "single_step_graph_us": round(ms1 / a.steps * 1e3, 2),
-        "median_of_5_segments_us": None if seg_med_us is None else round(seg_med_us, 2),
+        "median_of_5_segments_us": round(seg_med_us, 2),
+        "eight_step_graph": {"us_per_step": round(ms8 / a.steps * 1e3, 2),
+                             "value": round(spec.Q * a.steps / (ms8 / 1e3), 1),
+                             "unit": "queries/s",
+                             "median_of_5_segments_us": None if seg_med8_us is None
+                             else round(seg_med8_us, 2),
+                             "graph": "the eight input sets' steps captured in sequence "
+                                      "in one graph"},
         "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": int(step_bytes),
         "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
