@@ -413,16 +413,19 @@ dsa_status dsa_gate_compress_live(const float* hidden, const float* W, int M, in
  * dsa_gate_compress_workspace_size(M, K, N) = ns * M * N * 4 bytes.
  *
  * dsa_gate_compress: hidden, W, M, K, N as in dsa_head_gate; gate_part
- * [ns, M, N] f32, part[s][m][n] = sum over k in slice s of hidden[m][k] W[k][n]
- * (contents on entry are ignored); every other argument as in
+ * [M, ns, N] f32, part[m][s][n] = sum over k in slice s of hidden[m][k] W[k][n]
+ * (query-major, so the partials of a run of queries are contiguous; contents
+ * on entry are ignored); every other argument as in
  * dsa_kpool_compress (B = 0 runs the head-gate alone).  Errors: those of
  * dsa_kpool_compress and dsa_head_gate, and INVALID_ARG for gate_part_bytes
  * below the size.
  *
  * dsa_index_scores_gated: as dsa_index_scores, with the head weights given as
  * gate_part and nslices = ns (1 <= ns <= 64): w[q, h] = sum over s of
- * gate_part[s][q][h], added in a fixed order, and stored to w [Q, H] f32
- * unless w is NULL.  M of the gate call must equal Q.
+ * gate_part[q][s][h], added in a fixed order, and stored to w [Q, H] f32
+ * unless w is NULL.  The gate call's rows are the queries: a call on queries
+ * q0 .. q0+Q-1 of a batch passes gate_part + q0*ns*H (and the other per-query
+ * arrays offset alike).
  *
  * dsa_topk_expand: dsa_topk_pools followed by dsa_expand_selection on the same
  * rows (arguments as there; sel and tok both written in full).  Errors: the

@@ -60,12 +60,11 @@ __global__ __launch_bounds__(256) void index_scores_kernel(
   // reduction below waits for them alone while the key rows stream in.
   float gp[4];
   if (GATED) {
-    const int Q = gridDim.y;
     const int h = threadIdx.x & 15, g = threadIdx.x >> 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int sl = min(g + 16 * i, nslices - 1);
-      gp[i] = w[((int64_t)sl * Q + q) * H + min(h, H - 1)];
+      gp[i] = w[((int64_t)q * nslices + sl) * H + min(h, H - 1)];
     }
   }
   const int r = q_req[q];
@@ -218,7 +217,7 @@ __global__ __launch_bounds__(256) void index_scores_qblock_kernel(
   if (GATED) {
 #pragma unroll
     for (int sl = 0; sl < NS; ++sl)
-      gp[sl] = w[((int64_t)min(sl, nslices - 1) * Q + wq) * H + min(wh, H - 1)];
+      gp[sl] = w[((int64_t)wq * nslices + min(sl, nslices - 1)) * H + min(wh, H - 1)];
   } else {
     gp[0] = w[(int64_t)wq * H + min(wh, H - 1)];
   }

@@ -132,11 +132,11 @@ constexpr int kGateRows = 16;    // gate rows per partial workgroup
 struct GateArgs {
   const float* hidden;  // [M, K] f32
   const float* W;       // [K, N] f32
-  float* part;          // [nslices, M, N] f32: part[s] = hidden[:, slice s] @ W[slice s, :]
+  float* part;          // [M, nslices, N] f32: part[m][s] = hidden[m, slice s] @ W[slice s, :]
   int M, K, N, nslices, nwg;  // nwg = nslices * ceil(M / 16); 0 = no gate work
 };
 
-// part[sl][m][n] for the 16 rows of tile mt, K slice sl; k added in order.
+// part[m][sl][n] for the 16 rows of tile mt, K slice sl; k added in order.
 __device__ void gate_partial(const GateArgs& ga, int g) {
   __shared__ __attribute__((aligned(16))) float s_h[kGateRows][kGateSlice + 4];
   __shared__ __attribute__((aligned(16))) float s_w[kGateSlice][16];
@@ -183,7 +183,7 @@ __device__ void gate_partial(const GateArgs& ga, int g) {
     acc = fmaf(h.z, s_w[k + 2][n], acc);
     acc = fmaf(h.w, s_w[k + 3][n], acc);
   }
-  if (m0 + m < M && n < N) ga.part[((int64_t)sl * M + m0 + m) * N + n] = acc;
+  if (m0 + m < M && n < N) ga.part[((int64_t)(m0 + m) * ga.nslices + sl) * N + n] = acc;
 }
 
 // A whole decode step's start in the compression launch (dsa_gate_compress_live):

@@ -370,7 +370,8 @@ def test_fused_gate_compress(case):
         _poison(t)
     st.gate_compress()
     ns = st.nslices
-    part = _np(st.gate_part)[:ns * spec.Q * spec.index_heads].reshape(ns, spec.Q, spec.index_heads)
+    part = _np(st.gate_part)[:ns * spec.Q * spec.index_heads].reshape(
+        spec.Q, ns, spec.index_heads).transpose(1, 0, 2)     # query-major on the device
     if ns > 1:
         PT.check_gate(part, _oracle_gate_partials(xn, ns))
     PT.check_gate(part.astype(np.float64).sum(axis=0), ref["w"])
@@ -385,8 +386,9 @@ def test_fused_index_scores_isolated(case):
     _say(f"index_scores_gated {spec.name}")
     st = _step(xg)
     _load_oracle_front(st, ref)
-    part = _oracle_gate_partials(xn, st.nslices)
-    st.gate_part[:part.size].copy_(torch.from_numpy(part.reshape(-1)))
+    part = _oracle_gate_partials(xn, st.nslices)               # [ns, Q, H]
+    st.gate_part[:part.size].copy_(torch.from_numpy(
+        np.ascontiguousarray(part.transpose(1, 0, 2)).reshape(-1)))   # query-major
     for t in (st.scores, st.cand, st.w):
         _poison(t)
     st.index_scores_gated()
@@ -407,7 +409,8 @@ def test_gated_scores_slice_counts(case, ns):
     _load_oracle_front(st, ref)
     parts = [O.head_gate(xn["hidden"][:, c], xn["W"][c])
              for c in np.array_split(np.arange(xn["hidden"].shape[1]), ns)]
-    part = torch.from_numpy(np.stack(parts).astype(np.float32).reshape(-1)).cuda()
+    part = torch.from_numpy(np.ascontiguousarray(
+        np.stack(parts, axis=1).astype(np.float32)).reshape(-1)).cuda()   # [Q, ns, H]
     for t in (st.scores, st.cand, st.w):
         _poison(t)
     x = st.x
@@ -416,6 +419,37 @@ def test_gated_scores_slice_counts(case, ns):
                                st.cand)
     PT.check_gate(_np(st.w), ref["w"])
     PT.check_scores(_np(st.scores), _np(st.cand), ref["scores"], ref["cand"])
+
+
+def test_gated_scores_query_subrange(case):
+    """The gated scores on a run of queries q0.. of the batch (the per-query
+    arrays, the query-major head-gate partials among them, passed from q0 on)
+    give those queries' rows of the whole call."""
+    spec, xn, ref, xg = case
+    q0 = 4
+    if spec.Q <= q0:
+        pytest.skip("needs more than four queries")
+    _say(f"index_scores_gated {spec.name} on queries {q0}..{spec.Q - 1}")
+    from sparse_attention_fp32_amd import dsa
+    st = _step(xg)
+    _load_oracle_front(st, ref)
+    part = _oracle_gate_partials(xn, st.nslices)               # [ns, Q, H]
+    st.gate_part[:part.size].copy_(torch.from_numpy(
+        np.ascontiguousarray(part.transpose(1, 0, 2)).reshape(-1)))
+    H, ns = spec.index_heads, st.nslices
+    n = spec.Q - q0
+    scores = torch.empty(n, st.pstride, dtype=torch.float32, device="cuda")
+    cand = torch.empty(n, st.pstride, dtype=torch.uint8, device="cuda")
+    w = torch.empty(n, H, dtype=torch.float32, device="cuda")
+    for t in (scores, cand, w):
+        _poison(t)
+    x = st.x
+    sub = st.gate_part[:spec.Q * ns * H].view(spec.Q, ns * H)[q0:]
+    dsa.dsa_index_scores_gated(x.qi[q0:], sub, ns, w, st.keys, st.pool_start, st.pool_valid,
+                               x.pool_off, st.n_pools, x.q_req[q0:], x.q_pos[q0:], spec.kpool,
+                               scores, cand)
+    PT.check_gate(_np(w), ref["w"][q0:])
+    PT.check_scores(_np(scores), _np(cand), ref["scores"][q0:], ref["cand"][q0:])
 
 
 def test_fused_topk_expand_isolated(case):
