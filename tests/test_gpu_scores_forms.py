@@ -81,7 +81,7 @@ def test_query_block_scores(name, H, D, kpool):
     for ns in (1, 3, 40):
         parts = [O.head_gate(xn["hidden"][:, c], xn["W"][c])
                  for c in np.array_split(np.arange(K), ns)]
-        part = torch.from_numpy(np.stack(parts).astype(np.float32).reshape(-1)).cuda()
+        part = torch.from_numpy(np.stack(parts, axis=1).astype(np.float32).reshape(-1)).cuda()  # [Q, ns, H]
         st.scores.view(torch.uint8).fill_(0xFF)
         st.cand.fill_(0xFF)
         st.w.view(torch.uint8).fill_(0xFF)
