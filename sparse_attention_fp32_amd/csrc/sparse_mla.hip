@@ -88,11 +88,12 @@ Chunking mla_chunking(int Q, int Hm, int out_width) {
   return {(nsub + spc - 1) / spc, spc * kSub};
 }
 
+// (low halves of x and y) and (high halves), one v_perm_b32 each
 __device__ __forceinline__ uint32_t lo_pair(uint32_t x, uint32_t y) {
-  return (x & 0xffffu) | (y << 16);
+  return __builtin_amdgcn_perm(y, x, 0x05040100u);
 }
 __device__ __forceinline__ uint32_t hi_pair(uint32_t x, uint32_t y) {
-  return (x >> 16) | (y & 0xffff0000u);
+  return __builtin_amdgcn_perm(y, x, 0x07060302u);
 }
 // 8 fp8 codes -> 8 bf16, in byte order, by the hardware conversion with a unit
 // scale: exact (every E4M3 value, subnormals included, is a bf16 value); the
@@ -234,6 +235,11 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
 
   // a ring of kPF row sets: sub-chunk s is gathered into slot s mod kPF, kPF
   // sub-chunks ahead of its use; past the last sub-chunk every slot is empty
+  // the zero scale's address, loaded once and kept in scalar registers: a
+  // scalar load pending inside the loop would make every LDS wait a full one
+  // (scalar loads return out of order)
+  const float* zscl = &kNoScale;
+  asm volatile("" : "+s"(zscl));
   RowSlice<FP8> ring[kPF];
   float rscl[kPF][2];  // row scales of tokens col, 16 + col (used by wave 0, lanes < 16)
   auto gather = [&](int s, RowSlice<FP8>& cr, float (&scl)[2]) {
@@ -252,7 +258,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
       // the row scale (0 for no id) by a pointer select, so that nothing
       // consumes the loaded value here (a select on it would wait for every
       // load in flight, the rows just issued included)
-      if (FP8) scl[tt] = *(id >= 0 ? ckv_scale + rowbase + id : &kNoScale);
+      if (FP8) scl[tt] = *(id >= 0 ? ckv_scale + rowbase + id : zscl);
     }
   };
 #pragma unroll
@@ -331,20 +337,22 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
       for (int k = 1; k < 8; ++k) mloc = fmaxf(mloc, x[k]);
       mloc = rows_max(mloc);
       const bool move = mloc > m_run + 8.f;
-      const bool any_move = __any(move);
+      // a head's first finite max only sets its reference (its O is still 0)
+      const bool rescale = move && m_run != -INFINITY;
+      const bool any_move = __any(rescale);
       if (any_move) {
-        const float alpha = move ? exp2f(m_run - mloc) : 1.f;  // exp2(-inf) = 0
-        if (move) m_run = mloc;
+        const float alpha = rescale ? __builtin_amdgcn_exp2f(m_run - mloc) : 1.f;
         l_run *= alpha;
         if (grp == 0) s_alpha[w * 16 + col] = alpha;
       }
+      if (move) m_run = mloc;
       if (lane == 0) s_moved[w] = any_move;
       const bool none = m_run == -INFINITY;
       float p[8];
       float psum = 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        p[k] = none ? 0.f : exp2f(x[k] - m_run);
+        p[k] = none ? 0.f : __builtin_amdgcn_exp2f(x[k] - m_run);
         psum += p[k];
       }
       l_run += rows_sum(psum);
