@@ -14,9 +14,9 @@ captured in a HIP graph of its own, and the timed region launches one graph
 per step, K steps in all (five equal segments give the median per-step time
 too).  Beside it: the eight sets' steps captured in sequence in one graph (as
 a serving loop captures consecutive decode steps, which spreads the host's
-graph-launch cost), the single-step graphs replayed with two batches in
-flight (two streams, showing how much of the step is fixed latency rather
-than throughput), the same step through the six separate calls, the step with
+graph-launch cost), the single-step graphs replayed with two and with four
+batches in flight (two or four streams, showing how much of the step is
+fixed latency rather than throughput), the same step through the six separate calls, the step with
 the attention reading a paged copy of the latent cache (64-row pages in
 shuffled order, through a block table), and the whole decode step from
 device-side live lengths (geometry, the store of the step's indexer row, the
@@ -359,28 +359,33 @@ def main():
     ms_per_step = ms / a.steps
     qps = spec.Q * a.steps / (ms / 1e3)
     ms8, _, seg_med8_us = timed_seq(gseq, graphs, a.steps, a.warmup)
-    # the same step graphs with two batches in flight: set i replays on side
-    # stream i mod 2 (default priority), bracketed by events on the launch stream
-    side = [torch.cuda.Stream(), torch.cuda.Stream()]
-    cur = torch.cuda.current_stream()
-    n2 = max(2, a.steps // 2 * 2)
-    for rep2 in range(2):  # (the first pass warms both streams)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(cur)
-        for sd in side:
-            sd.wait_event(e0)
-        for i in range(n2):
-            with torch.cuda.stream(side[i % 2]):
-                graphs[i % len(graphs)].replay()
-        for sd in side:
-            ev = torch.cuda.Event()
-            ev.record(sd)
-            cur.wait_event(ev)
-        e1.record(cur)
-        torch.cuda.synchronize()
-    ms2 = e0.elapsed_time(e1)
-    concurrent = {"streams": 2, "value": round(spec.Q * n2 / (ms2 / 1e3), 1),
-                  "unit": "queries/s", "us_per_step": round(ms2 / n2 * 1e3, 2)}
+    # the same step graphs with two (four) batches in flight: set i replays on
+    # side stream i mod 2 (4), default priority, bracketed by events on the
+    # launch stream; each set always replays on the same stream
+    def in_flight(nstreams):
+        side = [torch.cuda.Stream() for _ in range(nstreams)]
+        cur = torch.cuda.current_stream()
+        n2 = max(nstreams, a.steps // nstreams * nstreams)
+        for rep2 in range(2):  # (the first pass warms the streams)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(cur)
+            for sd in side:
+                sd.wait_event(e0)
+            for i in range(n2):
+                with torch.cuda.stream(side[i % nstreams]):
+                    graphs[i % len(graphs)].replay()
+            for sd in side:
+                ev = torch.cuda.Event()
+                ev.record(sd)
+                cur.wait_event(ev)
+            e1.record(cur)
+            torch.cuda.synchronize()
+        ms2 = e0.elapsed_time(e1)
+        return {"streams": nstreams, "value": round(spec.Q * n2 / (ms2 / 1e3), 1),
+                "unit": "queries/s", "us_per_step": round(ms2 / n2 * 1e3, 2)}
+    # (only when the sets divide evenly, so no set is in flight on two streams)
+    concurrent = in_flight(2) if len(graphs) % 2 == 0 else None
+    concurrent4 = in_flight(4) if len(graphs) % 4 == 0 else None
     # the same step through the six separate calls, for comparison
     graphs6 = capture(lambda st: st.run(incremental=True))
     ms6, _, _ = timed(graphs6, max(1, a.steps // 4), max(1, a.warmup // 4))
@@ -549,6 +554,7 @@ def main():
         "six_call_step_us": round(six_us, 2),
         "call_us": {k: round(call_us[k], 2) for k in CALLS},
         "two_batches_in_flight": concurrent,
+        "four_batches_in_flight": concurrent4,
         "paged": paged,
         "live_step": live,
         "roofline": roofline,
