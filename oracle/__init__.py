@@ -28,6 +28,7 @@ from .dsa_oracle import (  # noqa: F401
     select_tail,
     sparse_mla_decode,
     sparse_mla_decode_paged,
+    latent_rows_f64,
     paged_rows,
     kv_index,
     attend_rows,

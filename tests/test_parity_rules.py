@@ -135,3 +135,59 @@ def test_holes_shape_has_the_cases_it_names():
         r = int(xn["q_req"][q])
         pv = ref["pool_valid"][po[r]:po[r] + ref["n_pools"][r]]
         assert not np.any(ref["cand"][q][:len(pv)][pv == 0])
+
+
+def _online_softmax(xn, spec, tok, rescale=True):
+    """The attention as a lazily rebased online softmax over sub-chunks of 32
+    ids in selection order (reference maximum moved only when a sub-chunk's
+    log2-domain logits exceed it by more than 8), fp64 throughout; with
+    rescale=False a moved reference leaves the earlier output and sum as
+    they were.  Returns bf16 output bits and lse like the library's call."""
+    Q, Hm, L = xn["q_mla"].shape
+    out = np.zeros((Q, Hm, L))
+    lse = np.full((Q, Hm), -np.inf)
+    for q in range(Q):
+        ids = tok[q][tok[q] >= 0]
+        if len(ids) == 0:
+            continue
+        r = int(xn["q_req"][q])
+        lat = O.latent_rows_f64(xn["ckv"], xn["ckv_scale"], int(xn["kv_off"][r]) + ids)
+        x = (O.bf16_bits_to_f64(xn["q_mla"][q]) @ lat.T) * spec.sm_scale / np.log(2.0)
+        m = np.full(Hm, -np.inf)
+        acc = np.zeros((Hm, L))
+        l = np.zeros(Hm)
+        for s0 in range(0, len(ids), 32):
+            xs = x[:, s0:s0 + 32]
+            mloc = xs.max(axis=1)
+            move = mloc > m + 8.0
+            if rescale:
+                a = np.where(move & np.isfinite(m), np.exp2(m - mloc), 1.0)
+                acc *= a[:, None]
+                l *= a
+            m = np.where(move, mloc, m)
+            p = np.exp2(xs - m[:, None])
+            l += p.sum(axis=1)
+            acc += p @ lat[s0:s0 + 32]
+        out[q] = acc / l[:, None]
+        lse[q] = (m + np.log2(l)) * np.log(2.0)
+    return O.f64_to_bf16_bits(out), lse.astype(np.float32)
+
+
+def test_growing_logits_catch_a_missing_rescale():
+    """The GPU growing-logits inputs (tests/test_gpu_mla_rescale.py) separate
+    a correct online softmax from one that skips the rescale when its
+    reference maximum moves: the first passes the attention tolerance, the
+    second fails it."""
+    import test_gpu_mla_rescale as G
+    spec = W.spec_by_name("medium")
+    x = W.make_inputs(spec, seed=11)
+    G._growing_rows(x, spec)
+    tok = G._ascending_selection(spec, seed=11).numpy()
+    xn = x.numpy()
+    want = O.sparse_mla_decode(xn["q_mla"], xn["ckv"], xn["ckv_scale"], xn["kv_off"],
+                               xn["q_req"], tok, spec.sm_scale)
+    good_o, good_l = _online_softmax(xn, spec, tok, rescale=True)
+    PT.check_mla(good_o, good_l, want["out_f64"], want["lse"])
+    bad_o, bad_l = _online_softmax(xn, spec, tok, rescale=False)
+    with pytest.raises(AssertionError):
+        PT.check_mla(bad_o, bad_l, want["out_f64"], want["lse"])
