@@ -115,3 +115,41 @@ def test_mla_growing_logits(name, paged):
     assert frac >= 0.5, frac
     _say(f"growing logits {name} paged={paged}: worst rel err {worst:.3g}, "
          f"rows that move their reference: {frac:.0%}")
+
+
+# Selections wide enough that a query's ids split into 32 and 64 chunks, so
+# the merge of the chunk partials runs in several batches of 16 and (with the
+# growing rows and ascending ids) every later batch raises the running max.
+WIDE = [
+    W.Spec("wide4096", lengths=[9000, 12000], pads=[0, 5], kpool=4, index_heads=16,
+           index_dim=128, hidden=512, select_k=1024, out_width=4096, mla_heads=64),
+    W.Spec("wide8192_fp8", lengths=[20000], pads=[3], kpool=4, index_heads=16,
+           index_dim=128, hidden=512, select_k=2048, out_width=8192, mla_heads=64,
+           latent_fp8=True),
+]
+
+
+@pytest.mark.parametrize("paged", (False, True))
+@pytest.mark.parametrize("spec", WIDE, ids=[s.name for s in WIDE])
+def test_mla_wide_selection(spec, paged):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_attention_fp32_amd.pipeline import DsaStep
+    _say(f"sparse_mla wide selection {spec.name} paged={paged}")
+    x = W.make_inputs(spec, seed=12)
+    _growing_rows(x, spec)
+    tok = _ascending_selection(spec, seed=12)
+    xn = x.numpy()
+    xg = x.to("cuda")
+    st = DsaStep(xg)
+    st.tok.copy_(tok)
+    for t in (st.out, st.lse):
+        t.view(torch.uint8).fill_(0xFF)
+    if paged:
+        st.mla_paged(W.make_paged_cache(xg, 64, seed=12))
+    else:
+        st.mla()
+    want = O.sparse_mla_decode(xn["q_mla"], xn["ckv"], xn["ckv_scale"], xn["kv_off"], xn["q_req"],
+                               tok.numpy(), spec.sm_scale)
+    worst = PT.check_mla(_np(st.out), _np(st.lse), want["out_f64"], want["lse"])
+    _say(f"wide selection {spec.name} paged={paged}: worst rel err {worst:.3g}")
