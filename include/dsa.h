@@ -186,10 +186,16 @@ dsa_status dsa_index_scores(const uint16_t* qi, const float* w, const uint16_t* 
  * row_len [Q] i32 or NULL: only entries p < row_len[q] of row q count
  * (clamped to [0, pstride]; NULL means pstride), for rows shorter than the
  * batch's widest.
- * Any row length is taken: rows of up to 16384 entries stay in registers,
- * longer ones are read again from memory on each pass of the select (the
- * select is tiled over the row).
- * No workspace is needed at present (size 0; ws may be NULL).
+ * Any row length is taken: rows of up to 16384 entries stay in registers.
+ * A longer row is selected in two stages when ws holds
+ * dsa_topk_pools_workspace_size bytes: each 16384-entry block of the row
+ * keeps its own top select_k (the row's top select_k is among them), then one
+ * workgroup selects among those candidates; this needs at most 16384
+ * candidates per row (blocks x select_k).  Otherwise (ws NULL or smaller, or
+ * too many candidates) the row is read again from memory on each pass of a
+ * one-workgroup select.  Both give the same result.
+ * Workspace: Q x candidates x 4 bytes for rows longer than 16384 entries
+ * (0 otherwise); ws may be NULL.
  * Errors: INVALID_ARG for select_k < 1, pstride < 1, Q < 0, NULL pointers.
  * ------------------------------------------------------------------------- */
 size_t dsa_topk_pools_workspace_size(int Q, int pstride, int select_k);
@@ -428,8 +434,10 @@ dsa_status dsa_gate_compress_live(const float* hidden, const float* W, int M, in
  * arrays offset alike).
  *
  * dsa_topk_expand: dsa_topk_pools followed by dsa_expand_selection on the same
- * rows (arguments as there; sel and tok both written in full).  Errors: the
- * union of theirs.
+ * rows (arguments as there; sel and tok both written in full).  A row longer
+ * than 16384 entries whose first-stage candidates (blocks x select_k) fit its
+ * tok row keeps them there between the two stages (no workspace).  Errors:
+ * the union of theirs.
  * ------------------------------------------------------------------------- */
 int dsa_gate_split_count(int M, int K, int N);
 size_t dsa_gate_compress_workspace_size(int M, int K, int N);

@@ -56,6 +56,21 @@ struct ExpandArgs {
   int32_t* tok;
 };
 
+// Long rows in two stages.  Stage 1 (MODE 1): workgroup (row q, block b)
+// selects the block's own top select_k among ids [b*blk, (b+1)*blk) -- the
+// row's top select_k is among the union of the blocks' (every id that beats
+// it in the row's order beats it in its block's too) -- and writes their row
+// ids, ascending, -1-padded, to ids[q*stride + b*select_k ..].  Stage 2
+// (MODE 2): one workgroup per row selects among those ncand = nblk*select_k
+// candidates, keyed by the row's own scores, and emits their ids; positions
+// ascend with the ids, so ties still go to the lower id.
+struct TwoStage {
+  int32_t* ids;  // [Q, stride] candidate ids (stage 1 writes, stage 2 reads)
+  int stride;
+  int blk;       // block length (stage 1)
+  int ncand;     // candidates per row (stage 2)
+};
+
 // Exclusive prefix, in (e, wave) order, of the per-(e, wave) counts in cnt
 // (E * NW entries), written to off, plus `base`; returns the total (in every
 // lane).  Run by wave 0 alone.
@@ -97,12 +112,16 @@ __device__ __forceinline__ void hist_add(int* h, bool pred, uint32_t bin) {
   }
 }
 
-template <int NT, int E, bool STREAM, bool EXPAND>  // NT threads per row, E ids per thread per step
+// NT threads per row, E ids per thread per step; MODE 0: the row itself,
+// 1: a block of it (stage 1), 2: the candidates of stage 1 (stage 2)
+template <int NT, int E, bool STREAM, bool EXPAND, int MODE = 0>
 __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores,
                                                   const uint8_t* __restrict__ cand,
                                                   const int32_t* __restrict__ row_len,
                                                   int pstride, int select_k,
-                                                  int32_t* __restrict__ sel, ExpandArgs ex) {
+                                                  int32_t* __restrict__ sel, ExpandArgs ex,
+                                                  TwoStage ts) {
+  static_assert(MODE == 0 || (!STREAM && (MODE == 2 || !EXPAND)), "two-stage modes");
   constexpr int kWaves = NT / 64;
   constexpr int kStep = NT * E;
   constexpr int kBpt = kBins / NT;  // histogram bins per thread in the scan
@@ -118,9 +137,14 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   __shared__ int s_run[2];            // kept / equal keys of earlier steps (long rows)
   __shared__ int s_kid[kStage], s_kps[EXPAND ? kStage : 1];
   const int q = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const float* srow = scores + (int64_t)q * pstride;
-  const uint8_t* crow = cand + (int64_t)q * pstride;
-  int32_t* out = sel + (int64_t)q * select_k;
+  // stage 1: this workgroup's block is ids [id0, id0 + plen) of the row
+  const int id0 = MODE == 1 ? (int)blockIdx.y * ts.blk : 0;
+  const int plen = MODE == 1 ? min(ts.blk, pstride - id0) : (MODE == 2 ? ts.ncand : pstride);
+  const float* srow = scores + (int64_t)q * pstride + id0;
+  const uint8_t* crow = cand + (int64_t)q * pstride + id0;
+  const int32_t* cids = MODE == 2 ? ts.ids + (int64_t)q * ts.stride : nullptr;
+  int32_t* out = MODE == 1 ? ts.ids + (int64_t)q * ts.stride + (int64_t)blockIdx.y * select_k
+                           : sel + (int64_t)q * select_k;
   const int nstep = STREAM ? (pstride + kStep - 1) / kStep : 1;
 
   // fused expansion: the request's pool slots (a request with no slot reads
@@ -137,24 +161,31 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   }
   // the row's length loads beside the first scores (without row_len it reads a
   // score word and does not use it)
-  const int len_word = *(row_len ? row_len + q : (const int32_t*)srow);
+  const int len_word = *(row_len ? row_len + q : (const int32_t*)scores);
 
   // keys of pass step s (ids clamped into the row, then masked); with EXPAND
   // and `starts`, the start rows of those pools too
   uint32_t key[E];
   int32_t ps[EXPAND ? E : 1];
-  int lenq = pstride;
+  int32_t cid[MODE == 2 ? E : 1];  // stage 2: the row id of each candidate slot (-1: none)
+  int lenq = plen;
   auto load_step = [&](int s, bool starts) {
     float sv[E];
     uint8_t cv[E];
+    if (MODE == 2) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) cid[e] = cids[min(t + NT * e, plen - 1)];
+    }
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       // (unsigned, so the address is a 32-bit offset from the row's base when
       // the row fits one step)
-      const unsigned id = min((unsigned)(s * kStep + t + NT * e), (unsigned)(pstride - 1));
+      const unsigned id = MODE == 2 ? (unsigned)max(cid[e], 0)
+                                    : min((unsigned)(s * kStep + t + NT * e), (unsigned)(plen - 1));
       sv[e] = srow[id];
       cv[e] = crow[id];
-      if (EXPAND && starts) ps[e] = psrc[min((int)(s * kStep + t + NT * e), pslast)];
+      if (EXPAND && starts)
+        ps[e] = psrc[min(MODE == 2 ? (int)id : (int)(s * kStep + t + NT * e), pslast)];
     }
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -163,7 +194,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
       // (which would end in a wait for every outstanding load)
       uint32_t u = __float_as_uint(sv[e]), cb = cv[e];
       asm volatile("" : "+v"(u), "+v"(cb));
-      const bool c = (s * kStep + t + NT * e < lenq) & (cb != 0u);
+      const bool c = (s * kStep + t + NT * e < lenq) & (cb != 0u) & (MODE != 2 || cid[e] >= 0);
       key[e] = c ? float_order_key(__uint_as_float(u)) : 0u;
     }
   };
@@ -171,7 +202,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 #pragma unroll
   for (int j = 0; j < 2 * kBins / NT; ++j) (&hist[0][0])[t + j * NT] = 0;
   // (STREAM: the first pass loads its steps after the length is known)
-  lenq = row_len ? min(max(len_word, 0), pstride) : pstride;
+  if (MODE == 0) lenq = row_len ? min(max(len_word, 0), pstride) : pstride;
+  if (MODE == 1) lenq = row_len ? min(max(len_word - id0, 0), plen) : plen;
   if (!STREAM) {
     // the first load_step ran before the length was known: mask again
 #pragma unroll
@@ -301,7 +333,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int pos = s_eoff[e * kWaves + wv] + lanes_below(bk[e]);
-      const int id = s * kStep + t + NT * e;
+      const int id = MODE == 2 ? cid[e] : id0 + s * kStep + t + NT * e;
       if (keep[e] && pos < k_eff) {
         if (staged) {
           s_kid[pos] = id;
@@ -335,10 +367,48 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     for (int i = k_eff * ex.kpool + t; i < ex.out_width; i += NT) trow[i] = -1;
 }
 
+constexpr int kBlk = 16384;  // stage-1 block: 1024 threads x 16 ids in registers
+
+// Candidates per row of the two-stage select, or 0 where the row fits one
+// pass in registers or the candidates would not fit stage 2's registers.
+long long two_stage_cands(int pstride, int select_k) {
+  if (pstride <= kBlk) return 0;
+  const long long nblk = (pstride + kBlk - 1) / kBlk;
+  const long long n = nblk * select_k;
+  return n <= kBlk ? n : 0;
+}
+
 template <bool EXPAND>
 dsa_status launch_topk(const float* scores, const uint8_t* cand, const int32_t* row_len, int Q,
                        int pstride, int select_k, int32_t* sel, const ExpandArgs& ex,
-                       hipStream_t stream) {
+                       int32_t* cbuf, int cstride, hipStream_t stream) {
+  const char* who = EXPAND ? "dsa_topk_expand" : "dsa_topk_pools";
+  const long long ncand = two_stage_cands(pstride, select_k);
+  if (ncand > 0 && cbuf && ncand <= cstride) {
+    // long row in two stages: the blocks' own top-k, then one select over them
+    const int nblk = (pstride + kBlk - 1) / kBlk;
+    DSA_REQUIRE(nblk <= 65535, DSA_ERR_UNSUPPORTED, "%s: pstride=%d in %d blocks", who, pstride,
+                nblk);
+    if (dsa::trace_enabled())
+      fprintf(stderr, "[dsa] topk two-stage Q=%d pstride=%d select_k=%d blocks=%d cands=%lld\n",
+              Q, pstride, select_k, nblk, ncand);
+    const TwoStage ts{cbuf, cstride, kBlk, (int)ncand};
+    topk_kernel<1024, 16, false, false, 1><<<dim3(Q, nblk), 1024, 0, stream>>>(
+        scores, cand, row_len, pstride, select_k, sel, ExpandArgs{}, ts);
+    dsa_status st = dsa::check_launch(who);
+    if (st != DSA_OK) return st;
+    const int need = (int)((ncand + 1023) / 1024);
+#define DSA_LAUNCH_TK2(E) \
+  topk_kernel<1024, E, false, EXPAND, 2><<<Q, 1024, 0, stream>>>(scores, cand, row_len, pstride, \
+                                                                 select_k, sel, ex, ts)
+    if (need <= 1) DSA_LAUNCH_TK2(1);
+    else if (need <= 2) DSA_LAUNCH_TK2(2);
+    else if (need <= 4) DSA_LAUNCH_TK2(4);
+    else if (need <= 8) DSA_LAUNCH_TK2(8);
+    else DSA_LAUNCH_TK2(16);
+#undef DSA_LAUNCH_TK2
+    return dsa::check_launch(who);
+  }
   const int nt = pstride <= kShortRow ? 256 : 1024;
   const int need = (pstride + nt - 1) / nt;
   if (dsa::trace_enabled())
@@ -346,7 +416,7 @@ dsa_status launch_topk(const float* scores, const uint8_t* cand, const int32_t* 
             pstride, select_k, nt, need, (int)EXPAND);
 #define DSA_LAUNCH_TK(NT, E, S)                                                               \
   topk_kernel<NT, E, S, EXPAND><<<Q, NT, 0, stream>>>(scores, cand, row_len, pstride, select_k, \
-                                                      sel, ex)
+                                                      sel, ex, TwoStage{})
   if (nt == 256) {
     if (need <= 1) DSA_LAUNCH_TK(256, 1, false);
     else if (need <= 2) DSA_LAUNCH_TK(256, 2, false);
@@ -360,32 +430,31 @@ dsa_status launch_topk(const float* scores, const uint8_t* cand, const int32_t* 
     else DSA_LAUNCH_TK(1024, 16, true);
   }
 #undef DSA_LAUNCH_TK
-  return dsa::check_launch(EXPAND ? "dsa_topk_expand" : "dsa_topk_pools");
+  return dsa::check_launch(who);
 }
 
 }  // namespace
 
 DSA_EXPORT size_t dsa_topk_pools_workspace_size(int Q, int pstride, int select_k) {
-  (void)Q;
-  (void)pstride;
-  (void)select_k;
-  return 0;
+  if (Q <= 0 || pstride < 1 || select_k < 1) return 0;
+  return (size_t)Q * (size_t)two_stage_cands(pstride, select_k) * sizeof(int32_t);
 }
 
 DSA_EXPORT dsa_status dsa_topk_pools(const float* scores, const uint8_t* cand,
                                      const int32_t* row_len, int Q, int pstride, int select_k,
                                      int32_t* sel, void* ws, size_t ws_bytes,
                                      hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   DSA_REQUIRE(select_k >= 1, DSA_ERR_INVALID_ARG, "dsa_topk_pools: select_k=%d < 1", select_k);
   DSA_REQUIRE(pstride >= 1, DSA_ERR_INVALID_ARG, "dsa_topk_pools: pstride=%d < 1", pstride);
   DSA_REQUIRE(Q >= 0, DSA_ERR_INVALID_ARG, "dsa_topk_pools: Q=%d < 0", Q);
   if (Q == 0) return DSA_OK;
   DSA_REQUIRE(scores && cand && sel, DSA_ERR_INVALID_ARG, "dsa_topk_pools: NULL tensor pointer");
   DSA_REQUIRE_ALIGNED("dsa_topk_pools", scores, cand, row_len, sel, ws);
+  // the two-stage select of long rows when the workspace holds its candidates
+  const long long nc = two_stage_cands(pstride, select_k);
+  const bool two = nc > 0 && ws && ws_bytes >= (size_t)Q * (size_t)nc * sizeof(int32_t);
   return launch_topk<false>(scores, cand, row_len, Q, pstride, select_k, sel, ExpandArgs{},
-                            stream);
+                            two ? (int32_t*)ws : nullptr, (int)nc, stream);
 }
 
 DSA_EXPORT dsa_status dsa_topk_expand(const float* scores, const uint8_t* cand,
@@ -411,6 +480,9 @@ DSA_EXPORT dsa_status dsa_topk_expand(const float* scores, const uint8_t* cand,
               DSA_ERR_INVALID_ARG, "dsa_topk_expand: NULL tensor pointer");
   DSA_REQUIRE_ALIGNED("dsa_topk_expand", scores, cand, row_len, pool_start, pool_off, q_req, sel,
                       tok);
+  // (a long row's stage-1 candidates go to its tok row when they fit it; the
+  // second stage reads them all before it writes the row)
   return launch_topk<true>(scores, cand, row_len, Q, pstride, select_k, sel,
-                           ExpandArgs{pool_start, pool_off, q_req, kpool, out_width, tok}, stream);
+                           ExpandArgs{pool_start, pool_off, q_req, kpool, out_width, tok}, tok,
+                           out_width, stream);
 }

@@ -42,6 +42,8 @@ class DsaStep:
         self.scores = torch.empty(Q, self.pstride, dtype=torch.float32, device=dev)
         self.cand = torch.empty(Q, self.pstride, dtype=torch.uint8, device=dev)
         self.sel = torch.empty(Q, s.select_k, **i32)
+        ntk = dsa.topk_pools_workspace_size(Q, self.pstride, s.select_k)
+        self.ws_topk = torch.empty(ntk, dtype=torch.uint8, device=dev) if ntk else None
         self.tok = torch.empty(Q, s.out_width, **i32)
         self.out = torch.empty(Q, s.mla_heads, s.latent, dtype=torch.int16, device=dev)
         self.lse = torch.empty(Q, s.mla_heads, dtype=torch.float32, device=dev)
@@ -74,7 +76,7 @@ class DsaStep:
                              self.cand, stream=self.stream)
 
     def topk(self):
-        dsa.dsa_topk_pools(self.scores, self.cand, self.sel, stream=self.stream)
+        dsa.dsa_topk_pools(self.scores, self.cand, self.sel, ws=self.ws_topk, stream=self.stream)
 
     def expand(self):
         dsa.dsa_expand_selection(self.sel, self.pool_start, self.x.pool_off, self.x.q_req,

@@ -103,6 +103,9 @@ def test_topk_errors():
     assert _misaligned(L.dsa_topk_pools(FAKE, MIS, NUL, 4, 100, 8, FAKE, NUL, 0, NUL))
     assert _misaligned(L.dsa_topk_pools(FAKE, FAKE, MIS, 4, 100, 8, FAKE, NUL, 0, NUL))
     assert dsa.topk_pools_workspace_size(16, 8192, 512) == 0
+    # rows past one pass in registers: room for each row's first-stage candidates
+    assert dsa.topk_pools_workspace_size(2, 65536, 512) == 2 * 4 * 512 * 4
+    assert dsa.topk_pools_workspace_size(2, 65536, 8192) == 0   # candidates past stage 2's reach
 
 
 def test_expand_errors():

@@ -64,16 +64,17 @@ def _case_rows(P, k, kind):
     return rng, s, c
 
 
+@pytest.mark.parametrize("kpool", [3, 8])
 @pytest.mark.parametrize("P,k,kind", CASES)
-def test_topk_expand_exact(P, k, kind):
+def test_topk_expand_exact(P, k, kind, kpool):
     """The fused top-k + expansion: sel as the oracle's top-k, tok as the
     oracle's expansion of it (one request per row, pool starts spaced by
-    kpool from a random first row, a -1 tail)."""
+    kpool from a random first row, a -1 tail).  With kpool 8 the token row
+    holds the first stage's candidates of a long row (two-stage select)."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     rng, s, c = _case_rows(P, k, kind)
     Q = s.shape[0]
-    kpool = 3
     out_width = k * kpool + 5
     pool_off = np.arange(Q + 1, dtype=np.int32) * P
     first = rng.integers(0, 50, size=Q)
@@ -91,8 +92,11 @@ def test_topk_expand_exact(P, k, kind):
     assert np.array_equal(tok.cpu().numpy(), ref_tok)
 
 
+@pytest.mark.parametrize("with_ws", [False, True])
 @pytest.mark.parametrize("P,k,kind", CASES)
-def test_topk_exact(P, k, kind):
+def test_topk_exact(P, k, kind, with_ws):
+    """dsa_topk_pools against the oracle; with its workspace, rows longer than
+    one pass in registers take the two-stage select."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     rng = np.random.default_rng(_seed(P, k, kind))
@@ -106,7 +110,13 @@ def test_topk_exact(P, k, kind):
     ref = O.topk_pools(s, c, k)
     sg, cg = torch.from_numpy(s).cuda(), torch.from_numpy(c).cuda()
     out = torch.full((Q, k), 12345, dtype=torch.int32, device="cuda")
-    dsa.dsa_topk_pools(sg, cg, out)
+    ws = None
+    if with_ws:
+        n = dsa.topk_pools_workspace_size(Q, P, k)
+        if n == 0:
+            pytest.skip("no workspace at this shape")
+        ws = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")
+    dsa.dsa_topk_pools(sg, cg, out, ws=ws)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), ref)
 
@@ -130,21 +140,27 @@ def test_topk_row_len(P, k, kind, fused):
     ref_sel = O.topk_pools(s, c, k, row_len=lens)
     sg, cg = torch.from_numpy(s).cuda(), torch.from_numpy(c).cuda()
     lg = torch.from_numpy(lens).cuda()
-    sel = torch.full((Q, k), 12345, dtype=torch.int32, device="cuda")
     if not fused:
-        dsa.dsa_topk_pools(sg, cg, sel, row_len=lg)
+        # without and with the workspace (two stages for rows past one pass)
+        n = dsa.topk_pools_workspace_size(Q, P, k)
+        for ws in (None, torch.zeros(n, dtype=torch.uint8, device="cuda") if n else None):
+            sel = torch.full((Q, k), 12345, dtype=torch.int32, device="cuda")
+            dsa.dsa_topk_pools(sg, cg, sel, ws=ws, row_len=lg)
+            torch.cuda.synchronize()
+            assert np.array_equal(sel.cpu().numpy(), ref_sel)
+        return
+    # kpool 8: the token row holds a long row's first-stage candidates
+    for kpool in (2, 8):
+        out_width = k * kpool + 1
+        pool_off = np.arange(Q + 1, dtype=np.int32) * P
+        pool_start = np.concatenate([7 + kpool * np.arange(P)] * Q).astype(np.int32)
+        q_req = np.arange(Q, dtype=np.int32)
+        ref_tok = O.expand_selection(ref_sel, pool_start, pool_off, q_req, kpool, out_width)
+        sel = torch.full((Q, k), 12345, dtype=torch.int32, device="cuda")
+        tok = torch.full((Q, out_width), 12345, dtype=torch.int32, device="cuda")
+        dsa.dsa_topk_expand(sg, cg, torch.from_numpy(pool_start).cuda(),
+                            torch.from_numpy(pool_off).cuda(), torch.from_numpy(q_req).cuda(),
+                            kpool, sel, tok, row_len=lg)
         torch.cuda.synchronize()
         assert np.array_equal(sel.cpu().numpy(), ref_sel)
-        return
-    kpool = 2
-    out_width = k * kpool + 1
-    pool_off = np.arange(Q + 1, dtype=np.int32) * P
-    pool_start = np.concatenate([7 + kpool * np.arange(P)] * Q).astype(np.int32)
-    q_req = np.arange(Q, dtype=np.int32)
-    ref_tok = O.expand_selection(ref_sel, pool_start, pool_off, q_req, kpool, out_width)
-    tok = torch.full((Q, out_width), 12345, dtype=torch.int32, device="cuda")
-    dsa.dsa_topk_expand(sg, cg, torch.from_numpy(pool_start).cuda(), torch.from_numpy(pool_off).cuda(),
-                        torch.from_numpy(q_req).cuda(), kpool, sel, tok, row_len=lg)
-    torch.cuda.synchronize()
-    assert np.array_equal(sel.cpu().numpy(), ref_sel)
-    assert np.array_equal(tok.cpu().numpy(), ref_tok)
+        assert np.array_equal(tok.cpu().numpy(), ref_tok)
