@@ -3,9 +3,11 @@
 // One workgroup per score row (1024 threads, or 256 for rows of at most 1024
 // pools).  Thread t holds ids t + NT*e of a pass step of NT*E ids, so every
 // load instruction is fully coalesced and the order (step, e, t) is ascending
-// id order.  A row that does not fit one step (more than 16384 pools) is read
-// again from memory (L2) on every pass instead of staying in registers; there
-// is no cap on the row length.
+// id order.  A row that does not fit one step (more than 16384 pools) is
+// selected in two launches when there is room for the candidates (each block
+// of the row keeps its own top-k, then one workgroup selects among them; see
+// TwoStage), else read again from memory (L2) on every pass instead of staying
+// in registers; there is no cap on the row length.
 //
 // Scores become order-preserving integer keys (a finite float maps to a
 // nonzero unsigned key that sorts like the float; -0 like +0; non-candidates
