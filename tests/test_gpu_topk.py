@@ -92,13 +92,7 @@ def test_topk_expand_exact(P, k, kind, kpool):
     assert np.array_equal(tok.cpu().numpy(), ref_tok)
 
 
-@pytest.mark.parametrize("with_ws", [False, True])
-@pytest.mark.parametrize("P,k,kind", CASES)
-def test_topk_exact(P, k, kind, with_ws):
-    """dsa_topk_pools against the oracle; with its workspace, rows longer than
-    one pass in registers take the two-stage select."""
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU")
+def _exact_pools(P, k, kind, with_ws):
     rng = np.random.default_rng(_seed(P, k, kind))
     Q = 6
     s = _rows(rng, Q, P, kind)
@@ -113,12 +107,31 @@ def test_topk_exact(P, k, kind, with_ws):
     ws = None
     if with_ws:
         n = dsa.topk_pools_workspace_size(Q, P, k)
-        if n == 0:
-            pytest.skip("no workspace at this shape")
+        assert n > 0
         ws = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")
     dsa.dsa_topk_pools(sg, cg, out, ws=ws)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("P,k,kind", CASES)
+def test_topk_exact(P, k, kind):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _exact_pools(P, k, kind, with_ws=False)
+
+
+# long rows whose first-stage candidates fit stage 2 (blocks x k <= 16384)
+TWO_STAGE_CASES = [c for c in CASES if c[0] > 16384 and -(-c[0] // 16384) * c[1] <= 16384]
+
+
+@pytest.mark.parametrize("P,k,kind", TWO_STAGE_CASES)
+def test_topk_exact_two_stage(P, k, kind):
+    """dsa_topk_pools with its workspace: rows longer than one pass in
+    registers take the two-stage select."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _exact_pools(P, k, kind, with_ws=True)
 
 
 ROW_LEN_CASES = [(P, k, kind) for P in (30, 2047, 8192, 16384, 65536) for k in (1, 64, 512)
