@@ -107,6 +107,8 @@ __device__ __forceinline__ uint4 widen_fp8x8(uint2 v) {
                     __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 // Read as the scale of a slot with no id (zero; global memory, so the load
 // stays a plain global load).
 __device__ float kNoScale;
@@ -451,12 +453,15 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
         uint32_t pk[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) pk[e >> 1] = pack_bf16x2(o[ht][e][i], o[ht][e + 1][i]);
-        *(uint4*)(part_o + (pbase + h) * L + dim0 + col * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        // (non-temporal: the combine reads the partials once, from another
+        // launch, so they need not stay in this XCD's L2)
+        const u32x4_t v = {pk[0], pk[1], pk[2], pk[3]};
+        __builtin_nontemporal_store(v, (u32x4_t*)(part_o + (pbase + h) * L + dim0 + col * 8));
       }
     const int hq = hb * kHeadsWG + w * 16 + col;
     if (w < kHT && grp == 0 && hq < Hm) {
-      part_ml[(pbase + hq) * 2] = m_run;
-      part_ml[(pbase + hq) * 2 + 1] = l_run;
+      __builtin_nontemporal_store(m_run, part_ml + (pbase + hq) * 2);
+      __builtin_nontemporal_store(l_run, part_ml + (pbase + hq) * 2 + 1);
     }
   }
 }
