@@ -109,9 +109,9 @@ def source_sha(stage: str) -> str:
 CALL_KERNELS = {
     "sparse_mla_decode": (r"sparse_mla_kernel<(true|false), false>", r"mla_combine_kernel"),
     "index_scores_gated": (r"index_scores(_qblock)?_kernel<\d+, true",),
-    "topk_expand": (r"topk_kernel<\d+, \d+, (true|false), true>",),
+    "topk_expand": (r"topk_kernel<\d+, \d+, (true|false), true(, 0)?>",),
     "index_scores": (r"index_scores(_qblock)?_kernel<\d+, false",),
-    "topk_pools": (r"topk_kernel<\d+, \d+, (true|false), false>",),
+    "topk_pools": (r"topk_kernel<\d+, \d+, (true|false), false(, 0)?>",),
 }
 
 
