@@ -181,7 +181,14 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
     const int h = min(hb * kHeadsWG + ht * 16 + col, Hm - 1);
     const uint16_t* qrow = q + ((int64_t)qx * Hm + h) * L + dim0 + grp * 8;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qb[ht][kk] = as_bf16x8(*(const uint4*)(qrow + kk * 32));
+    for (int kk = 0; kk < 4; ++kk) {
+      // With one chunk per query every Q row is read once: a non-temporal load
+      // keeps the stream of Q (and of O below) from evicting the latent rows,
+      // which every query of a prefill batch gathers, from L2.
+      const u32x4_t* src = (const u32x4_t*)(qrow + kk * 32);
+      const u32x4_t v = nchunks == 1 ? __builtin_nontemporal_load(src) : *src;
+      qb[ht][kk] = __builtin_bit_cast(bf16x8_t, v);
+    }
   }
   int64_t rowbase = 0;
   constexpr int kBtPerThread = PAGED ? kMaxBt / 256 : 1;
@@ -437,7 +444,8 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
         uint32_t pk[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) pk[e >> 1] = pack_bf16x2(o[ht][e][i] * inv, o[ht][e + 1][i] * inv);
-        *(uint4*)(out + ((int64_t)qx * Hm + h) * L + dim0 + col * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        const u32x4_t v = {pk[0], pk[1], pk[2], pk[3]};
+        __builtin_nontemporal_store(v, (u32x4_t*)(out + ((int64_t)qx * Hm + h) * L + dim0 + col * 8));
       }
     const int hq = hb * kHeadsWG + w * 16 + col;
     if (lse && w < kHT && grp == 0 && hq < Hm)
