@@ -203,8 +203,18 @@ __global__ __launch_bounds__(256) void index_scores_qblock_kernel(
   __shared__ uint4 s_qi[kQB * 16 * kRowChunks];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int qb0 = blockIdx.y * kQB, nq = min(kQB, Q - qb0);
-  const int wg0 = blockIdx.x * kPoolsPerWG;
+  // Workgroup -> (pool block, query block), XCD-aware: workgroups go to the
+  // eight XCDs in turn, so the pool blocks of one query block are given ids
+  // eight apart -- the same XCD, dispatched together -- and its qi rows are
+  // fetched into that XCD's L2 once.  The grid's query blocks are padded to
+  // a multiple of 8; the padding workgroups leave at once.
+  const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+  const int pblk = (lin >> 3) % gridDim.x;
+  const int qblk = ((lin >> 3) / gridDim.x) * 8 + (lin & 7);
+  const int qb0 = qblk * kQB;
+  if (qb0 >= Q) return;
+  const int nq = min(kQB, Q - qb0);
+  const int wg0 = pblk * kPoolsPerWG;
   const int tile0 = wg0 + wave * (kTiles * 16);
   // thread (query j, head h) of the weight table
   // (with fewer than 16 queries per block the upper threads repeat the lower)
@@ -284,7 +294,7 @@ __global__ __launch_bounds__(256) void index_scores_qblock_kernel(
     rcur = r0;
     // nothing of this block's pools exists for the request: sentinels only
     // (unless this workgroup stores w)
-    if (wg0 >= P && !(GATED && w_out && blockIdx.x == 0)) {
+    if (wg0 >= P && !(GATED && w_out && pblk == 0)) {
       const int p = wg0 + t;  // kPoolsPerWG == blockDim.x
       if (p < pstride)
         for (int j = 0; j < nq; ++j) {
@@ -311,7 +321,7 @@ __global__ __launch_bounds__(256) void index_scores_qblock_kernel(
           if (g + 16 * i < NS) acc += g + 16 * i < nslices ? gp[g + 16 * i] : 0.f;
         sum += acc;
       }
-      if (w_out && blockIdx.x == 0 && wown && wj < nq && wh < H)
+      if (w_out && pblk == 0 && wown && wj < nq && wh < H)
         w_out[(int64_t)(qb0 + wj) * H + wh] = sum;
     } else {
       sum = gp[0];
@@ -423,7 +433,8 @@ dsa_status launch_scores(const uint16_t* qi, const float* w, int nslices, float*
   const int pblocks = (pstride + kPoolsPerWG - 1) / kPoolsPerWG;
   const int qblocks = (Q + kQB - 1) / kQB;
   const bool qblock = Q >= kQBlockMinQ && (long long)pblocks * qblocks >= kQBlockMinWG;
-  const dim3 grid(pblocks, qblock ? qblocks : Q);
+  // (query blocks padded to a multiple of 8 for the XCD-aware order)
+  const dim3 grid(pblocks, qblock ? (qblocks + 7) / 8 * 8 : Q);
   if (dsa::trace_enabled())
     fprintf(stderr, "[dsa] %s Q=%d H=%d D=%d pstride=%d slices=%d grid=(%d,%d)%s\n", who, Q, H, D,
             pstride, nslices, grid.x, grid.y, qblock ? " query-block" : "");
