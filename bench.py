@@ -107,7 +107,8 @@ def source_sha(stage: str) -> str:
 
 # kernels behind each call, by name (counters of a call add up over its kernels)
 CALL_KERNELS = {
-    "sparse_mla_decode": (r"sparse_mla_kernel<(true|false), false>", r"mla_combine_kernel"),
+    "sparse_mla_decode": (r"sparse_mla_kernel<(true|false), false, (true|false)>",
+                          r"mla_combine_kernel"),
     "index_scores_gated": (r"index_scores(_qblock)?_kernel<\d+, true",),
     "topk_expand": (r"topk_kernel<\d+, \d+, (true|false), true(, 0)?>",),
     "index_scores": (r"index_scores(_qblock)?_kernel<\d+, false",),

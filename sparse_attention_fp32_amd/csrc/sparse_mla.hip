@@ -132,7 +132,11 @@ struct CacheMap {
   int32_t* kvidx;              // paged, optional: [Q, out_width] physical rows
 };
 
-template <bool FP8, bool PAGED>
+// ONE: the launch gives every query one chunk (the output is written here,
+// no partials): only these instances carry the XCD-aware order and the
+// non-temporal output stores, so the split launches' code stays as short
+// as it was without them.
+template <bool FP8, bool PAGED, bool ONE>
 __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ ckv_v,
     const float* __restrict__ ckv_scale, const CacheMap cm,
@@ -153,7 +157,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
 
   const int nchunks = gridDim.x;
   int chunk = blockIdx.x, hb = blockIdx.y, qx = blockIdx.z;
-  if (xcd_order) {
+  if (ONE && xcd_order) {
     // XCD-aware order (the grid's queries padded to a multiple of 8):
     // workgroups go to the eight XCDs in turn, so ids eight apart share one;
     // every workgroup of query q takes an id on XCD q mod 8, so the second
@@ -196,14 +200,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
     const int h = min(hb * kHeadsWG + ht * 16 + col, Hm - 1);
     const uint16_t* qrow = q + ((int64_t)qx * Hm + h) * L + dim0 + grp * 8;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      // With one chunk per query every Q row is read once: a non-temporal load
-      // keeps the stream of Q (and of O below) from evicting the latent rows,
-      // which every query of a prefill batch gathers, from L2.
-      const u32x4_t* src = (const u32x4_t*)(qrow + kk * 32);
-      const u32x4_t v = nchunks == 1 ? __builtin_nontemporal_load(src) : *src;
-      qb[ht][kk] = __builtin_bit_cast(bf16x8_t, v);
-    }
+    for (int kk = 0; kk < 4; ++kk) qb[ht][kk] = as_bf16x8(*(const uint4*)(qrow + kk * 32));
   }
   int64_t rowbase = 0;
   constexpr int kBtPerThread = PAGED ? kMaxBt / 256 : 1;
@@ -459,8 +456,16 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
         uint32_t pk[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) pk[e >> 1] = pack_bf16x2(o[ht][e][i] * inv, o[ht][e + 1][i] * inv);
-        const u32x4_t v = {pk[0], pk[1], pk[2], pk[3]};
-        __builtin_nontemporal_store(v, (u32x4_t*)(out + ((int64_t)qx * Hm + h) * L + dim0 + col * 8));
+        uint16_t* dst = out + ((int64_t)qx * Hm + h) * L + dim0 + col * 8;
+        if constexpr (ONE) {
+          // each output row is written once and read by no later workgroup:
+          // a non-temporal store keeps it from evicting the latent rows, which
+          // every query of a prefill batch gathers, from L2
+          const u32x4_t v = {pk[0], pk[1], pk[2], pk[3]};
+          __builtin_nontemporal_store(v, (u32x4_t*)dst);
+        } else {
+          *(uint4*)dst = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        }
       }
     const int hq = hb * kHeadsWG + w * 16 + col;
     if (lse && w < kHT && grp == 0 && hq < Hm)
@@ -655,10 +660,17 @@ dsa_status launch_mla(const uint16_t* q, const void* ckv, const float* ckv_scale
   if (dsa::trace_enabled())
     fprintf(stderr, "[dsa] %s Q=%d Hm=%d out_width=%d fp8=%d paged=%d chunks=%d tch=%d\n", who, Q,
             Hm, out_width, latent_dtype, (int)paged, ch.nchunks, ch.tch);
-#define DSA_LAUNCH_MLA(F, P)                                                              \
-  sparse_mla_kernel<F, P><<<grid, 256, 0, stream>>>(q, ckv, ckv_scale, cm, q_req, tok, Hm, \
-                                                    out_width, ch.tch, sm_log2, out, lse,  \
-                                                    part_o, part_ml, Q, xcd_order)
+#define DSA_LAUNCH_MLA(F, P)                                                                 \
+  if (ch.nchunks == 1)                                                                        \
+    sparse_mla_kernel<F, P, true><<<grid, 256, 0, stream>>>(q, ckv, ckv_scale, cm, q_req, tok, \
+                                                            Hm, out_width, ch.tch, sm_log2,   \
+                                                            out, lse, part_o, part_ml, Q,     \
+                                                            xcd_order);                       \
+  else                                                                                        \
+    sparse_mla_kernel<F, P, false><<<grid, 256, 0, stream>>>(q, ckv, ckv_scale, cm, q_req,    \
+                                                             tok, Hm, out_width, ch.tch,      \
+                                                             sm_log2, out, lse, part_o,       \
+                                                             part_ml, Q, xcd_order)
   const bool fp8 = latent_dtype == DSA_LATENT_FP8_E4M3;
   if (paged) {
     if (fp8) DSA_LAUNCH_MLA(true, true);
