@@ -9,12 +9,15 @@ calls (gate+compress, gated index scores, top-k+expand, sparse MLA) over one bat
 resident synthetic input: the 32K-context decode batch (16 requests x 32768
 cached rows, one query each) by default.  Eight input sets (each larger than
 the 256 MB last-level cache together with its outputs) are rotated so that
-every step streams its keys and latent rows from HBM.  Each set's step is
-captured in a HIP graph of its own, and the timed region launches one graph
-per step, K steps in all (five equal segments give the median per-step time
-too).  Beside it: the eight sets' steps captured in sequence in one graph (as
-a serving loop captures consecutive decode steps, which spreads the host's
-graph-launch cost), the single-step graphs replayed with two and with four
+every step streams its keys and latent rows from HBM.  The timed region makes
+one dsa_decode_step call per step (the library's step executor: one host call
+that enqueues the fused calls on the stream; each set's arguments are
+marshalled once, before timing), K steps in all (five equal segments give the
+median per-step time too).  Beside it: each set's step captured in a HIP
+graph of its own and replayed once per step, the eight sets' steps captured in
+sequence in one graph (as a serving loop captures consecutive decode steps,
+which spreads the host's graph-launch cost), the single-step graphs replayed
+with two and with four
 batches in flight (two or four streams, showing how much of the step is
 fixed latency rather than throughput), the same step through the six separate calls, the step with
 the attention reading a paged copy of the latent cache (64-row pages in
@@ -351,14 +354,40 @@ def main():
                      for j in range(nseg) if bounds[j + 1] > bounds[j])
         return ev[0].elapsed_time(ev[-1]), time.perf_counter() - t0, seg[len(seg) // 2]
 
-    # the step: the fused decode calls over cached pools, one graph launch per
-    # step (the timed figure); the same steps replayed as graphs of eight
-    # consecutive steps are reported beside it
-    graphs = capture(lambda st: st.run_fused(incremental=True))
-    gseq = capture_seq(lambda st: st.run_fused(incremental=True))
-    ms, wall, seg_med_us = timed(graphs, a.steps, a.warmup, segments=5)
+    def timed_native(argsets, n, warm, segments=5):
+        """n steps, one dsa_decode_step call each (the sets in rotation) on the
+        current stream; events split them into `segments` runs of equal
+        length.  Returns the total time (ms), the wall time and the median
+        per-step time of the segments (us)."""
+        cur = torch.cuda.current_stream()
+        k = len(argsets)
+        for i in range(warm):
+            dsa.dsa_decode_step(argsets[i % k], stream=cur)
+        torch.cuda.synchronize()
+        nseg = max(1, min(segments, n))
+        bounds = [n * i // nseg for i in range(nseg + 1)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(nseg + 1)]
+        t0 = time.perf_counter()
+        ev[0].record()
+        for i in range(n):
+            dsa.dsa_decode_step(argsets[i % k], stream=cur)
+            if i + 1 in bounds[1:]:
+                ev[bounds.index(i + 1)].record()
+        torch.cuda.synchronize()
+        seg = sorted(ev[j].elapsed_time(ev[j + 1]) / (bounds[j + 1] - bounds[j]) * 1e3
+                     for j in range(nseg) if bounds[j + 1] > bounds[j])
+        return ev[0].elapsed_time(ev[-1]), time.perf_counter() - t0, seg[len(seg) // 2]
+
+    # the step: the fused decode calls over cached pools, one dsa_decode_step
+    # call per step (the timed figure); beside it, the same steps as one graph
+    # replay per step and as graphs of eight consecutive steps
+    argsets = [st.step_args(incremental=True) for st in steps]
+    ms, wall, seg_med_us = timed_native(argsets, a.steps, a.warmup)
     ms_per_step = ms / a.steps
     qps = spec.Q * a.steps / (ms / 1e3)
+    graphs = capture(lambda st: st.run_fused(incremental=True))
+    gseq = capture_seq(lambda st: st.run_fused(incremental=True))
+    msg, _, seg_med_g_us = timed(graphs, a.steps, a.warmup, segments=5)
     ms8, _, seg_med8_us = timed_seq(gseq, graphs, a.steps, a.warmup)
     # the same step graphs with two (four) batches in flight: set i replays on
     # side stream i mod 2 (4), default priority, bracketed by events on the
@@ -537,10 +566,17 @@ def main():
                    "latent_dtype": "fp8_e4m3" if spec.latent_fp8 else "bf16",
                    "pools": "cached; the step recompresses the pool of its newest row",
                    "input_sets": a.sets,
-                   "graph": "one HIP graph per step (the input sets in rotation), each "
-                            "the fused decode calls (gate+compress, gated index scores, "
-                            "top-k+expand, sparse MLA)"},
+                   "launch": "one dsa_decode_step call per step (the input sets in "
+                             "rotation): the fused decode calls (gate+compress, gated index "
+                             "scores, top-k+expand, sparse MLA) enqueued on the stream by "
+                             "the library's step executor"},
         "median_of_5_segments_us": round(seg_med_us, 2),
+        "single_step_graph": {"us_per_step": round(msg / a.steps * 1e3, 2),
+                              "value": round(spec.Q * a.steps / (msg / 1e3), 1),
+                              "unit": "queries/s",
+                              "median_of_5_segments_us": round(seg_med_g_us, 2),
+                              "graph": "each input set's step captured in a HIP graph of its "
+                                       "own, one replay per step"},
         "eight_step_graph": {"us_per_step": round(ms8 / a.steps * 1e3, 2),
                              "value": round(spec.Q * a.steps / (ms8 / 1e3), 1),
                              "unit": "queries/s",

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 3
+#define DSA_ABI_VERSION 4
 
 typedef int dsa_status;
 #define DSA_OK 0
@@ -461,6 +461,87 @@ dsa_status dsa_topk_expand(const float* scores, const uint8_t* cand, const int32
                            const int32_t* pool_off, const int32_t* q_req, int kpool,
                            int out_width, int flags, int32_t* sel, int32_t* tok,
                            hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * One decode step from one host call   [Atlas page, "Shape of the pipeline"
+ *     (the stages and their order); stkernel pull request #227 (the fp32
+ *     head-gate whose weights the index scores take)]
+ *
+ * dsa_decode_step(a, stream) enqueues on `stream`, in this order:
+ *   dsa_gate_compress       (N = H, M = Q)
+ *   dsa_index_scores_gated  (nslices = dsa_gate_split_count(Q, K, H))
+ *   dsa_topk_expand
+ *   dsa_select_tail         only when select_tail is nonzero
+ *   dsa_sparse_mla_decode   or dsa_sparse_mla_decode_paged when block_table
+ *                           is not NULL (kv_off is then unused)
+ * with the arguments held in *a, which lives in host memory and is read
+ * during the call only (its tensor pointers are device pointers, as in every
+ * call).  The results are those of the same calls made one by one, bit for
+ * bit.  The step costs one host call instead of four or five, so a host
+ * thread keeps the stream's queue ahead of the kernels without a graph.
+ * Every argument of every call is checked before anything is launched (each
+ * call first runs as a dry run): an error from any of them returns with
+ * nothing enqueued, and dsa_last_error() names the call.
+ * struct_bytes must be sizeof(dsa_decode_step_args), which
+ * dsa_decode_step_args_size() reports, so a binding that lays the struct out
+ * itself can check its layout.  Errors: INVALID_ARG for a NULL a, a
+ * struct_bytes that differs, or M != Q; then those of the calls.
+ * ------------------------------------------------------------------------- */
+typedef struct dsa_decode_step_args {
+  size_t struct_bytes;
+  /* dsa_gate_compress */
+  const float* hidden;
+  const float* W;
+  int M, K, H;
+  float* gate_part;
+  size_t gate_part_bytes;
+  const uint16_t* k;
+  const uint16_t* gate;
+  const uint16_t* ape;
+  const uint8_t* valid;
+  const int32_t* tok_off;
+  const int32_t* pool_off;
+  const int32_t* seq_len;
+  const float* ln_w;
+  const float* ln_b;
+  float eps;
+  int B, D, kpool, max_cap;
+  const int32_t* new_from;
+  int max_new;
+  uint16_t* keys;
+  int32_t* pool_start;
+  uint8_t* pool_valid;
+  int32_t* n_pools;
+  /* dsa_index_scores_gated */
+  const uint16_t* qi;
+  float* w;
+  const int32_t* q_req;
+  const int32_t* q_pos;
+  int Q, pstride;
+  float* scores;
+  uint8_t* cand;
+  /* dsa_topk_expand, then dsa_select_tail when select_tail != 0 */
+  const int32_t* row_len;
+  int select_k, out_width, topk_flags, select_tail;
+  int32_t* sel;
+  int32_t* tok;
+  /* dsa_sparse_mla_decode, or dsa_sparse_mla_decode_paged */
+  const uint16_t* q_mla;
+  const void* ckv;
+  const float* ckv_scale;
+  int latent_dtype, Hm, L;
+  float sm_scale;
+  const int32_t* kv_off;
+  uint16_t* out;
+  float* lse;
+  void* mla_ws;
+  size_t mla_ws_bytes;
+  const int32_t* block_table;
+  int bt_stride, page_rows, n_pages;
+  int32_t* kvidx;
+} dsa_decode_step_args;
+size_t dsa_decode_step_args_size(void);
+dsa_status dsa_decode_step(const dsa_decode_step_args* a, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Measurement: the HBM read lane   [stkernel pull request #290, its

@@ -7,6 +7,11 @@
 namespace dsa {
 
 static thread_local char g_err[512] = "";
+static thread_local bool g_dry = false;
+
+bool dry_run() { return g_dry; }
+DryRun::DryRun() { g_dry = true; }
+DryRun::~DryRun() { g_dry = false; }
 
 dsa_status set_error(dsa_status code, const char* fmt, ...) {
   va_list ap;
@@ -19,6 +24,7 @@ dsa_status set_error(dsa_status code, const char* fmt, ...) {
 void clear_error() { g_err[0] = '\0'; }
 
 dsa_status check_launch(const char* what) {
+  if (g_dry) return DSA_OK;  // nothing was launched
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
     return set_error(DSA_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));

@@ -18,6 +18,19 @@ void clear_error();
 dsa_status check_launch(const char* what);
 bool trace_enabled();
 
+// Validation pass of a composite call (dsa_decode_step): while a DryRun is in
+// scope on this thread, every entry point runs all of its argument checks and
+// returns at the point where it would launch, with nothing enqueued.  Each
+// launch site begins with `if (dsa::dry_run()) return DSA_OK;` after the last
+// check of its call.
+bool dry_run();
+struct DryRun {
+  DryRun();
+  ~DryRun();
+  DryRun(const DryRun&) = delete;
+  DryRun& operator=(const DryRun&) = delete;
+};
+
 // True when every non-NULL pointer is 16-byte aligned (the kernels' vector
 // loads and stores need it).
 inline bool aligned16() { return true; }

@@ -51,6 +51,7 @@ DSA_EXPORT dsa_status dsa_expand_selection(const int32_t* sel, const int32_t* po
   DSA_REQUIRE_ALIGNED("dsa_expand_selection", sel, pool_start, pool_off, q_req, tok);
   DSA_REQUIRE(Q <= 65535, DSA_ERR_UNSUPPORTED, "dsa_expand_selection: Q=%d above 65535", Q);
   dim3 grid((out_width + 255) / 256, Q);
+  if (dsa::dry_run()) return DSA_OK;
   expand_kernel<<<grid, 256, 0, stream>>>(sel, pool_start, pool_off, q_req, select_k, kpool,
                                           out_width, tok);
   return dsa::check_launch("dsa_expand_selection");
@@ -114,6 +115,7 @@ DSA_EXPORT dsa_status dsa_select_tail(const uint8_t* valid, const int32_t* tok_o
               DSA_ERR_INVALID_ARG, "dsa_select_tail: NULL tensor pointer");
   DSA_REQUIRE_ALIGNED("dsa_select_tail", valid, tok_off, pool_start, pool_off, n_pools, q_req,
                       q_pos, tok);
+  if (dsa::dry_run()) return DSA_OK;
   tail_kernel<<<(Q + 63) / 64, 64, 0, stream>>>(valid, tok_off, pool_start, pool_off, n_pools,
                                                 q_req, q_pos, Q, kpool, select_k, out_width, tok);
   return dsa::check_launch("dsa_select_tail");

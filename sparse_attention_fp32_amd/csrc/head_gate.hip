@@ -232,6 +232,7 @@ DSA_EXPORT dsa_status dsa_head_gate(const float* hidden, const float* W, float* 
   DSA_REQUIRE(hidden && W && w, DSA_ERR_INVALID_ARG, "dsa_head_gate: NULL tensor pointer");
   DSA_REQUIRE_ALIGNED("dsa_head_gate", hidden, W, w, ws);
   if (dsa::trace_enabled()) fprintf(stderr, "[dsa] head_gate M=%d K=%d N=%d\n", M, K, N);
+  if (dsa::dry_run()) return DSA_OK;
   if (M <= kRows)
     if (N == 16)
       head_gate_row_kernel<true><<<M, kRowThreads, 0, stream>>>(hidden, W, w, K, N);

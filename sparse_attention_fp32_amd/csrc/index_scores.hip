@@ -469,6 +469,7 @@ dsa_status launch_scores(const uint16_t* qi, const float* w, int nslices, float*
     case 4: LAUNCH(4); break;       \
     default: LAUNCH(8); break;      \
   }
+  if (dsa::dry_run()) return DSA_OK;
   if (qblock) {
     DSA_SWITCH_D(DSA_LAUNCH_QB_NS)
   } else {

@@ -477,6 +477,7 @@ dsa_status launch_compress(const uint16_t* k, const uint16_t* gate, const uint16
     case 16: DSA_LAUNCH_KP(16, KP); break; \
     default: DSA_LAUNCH_KP(32, KP); break; \
   }
+  if (dsa::dry_run()) return DSA_OK;
   switch (kpool) {
     case 1: DSA_LAUNCH_KP_D(1); break;
     case 2: DSA_LAUNCH_KP_D(2); break;

@@ -672,6 +672,7 @@ dsa_status launch_mla(const uint16_t* q, const void* ckv, const float* ckv_scale
                                                              sm_log2, out, lse, part_o,       \
                                                              part_ml, Q, xcd_order)
   const bool fp8 = latent_dtype == DSA_LATENT_FP8_E4M3;
+  if (dsa::dry_run()) return DSA_OK;
   if (paged) {
     if (fp8) DSA_LAUNCH_MLA(true, true);
     else DSA_LAUNCH_MLA(false, true);

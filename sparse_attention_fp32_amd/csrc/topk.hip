@@ -395,6 +395,7 @@ dsa_status launch_topk(const float* scores, const uint8_t* cand, const int32_t* 
       fprintf(stderr, "[dsa] topk two-stage Q=%d pstride=%d select_k=%d blocks=%d cands=%lld\n",
               Q, pstride, select_k, nblk, ncand);
     const TwoStage ts{cbuf, cstride, kBlk, (int)ncand};
+    if (dsa::dry_run()) return DSA_OK;
     topk_kernel<1024, 16, false, false, 1><<<dim3(Q, nblk), 1024, 0, stream>>>(
         scores, cand, row_len, pstride, select_k, sel, ExpandArgs{}, ts);
     dsa_status st = dsa::check_launch(who);
@@ -416,6 +417,7 @@ dsa_status launch_topk(const float* scores, const uint8_t* cand, const int32_t* 
   if (dsa::trace_enabled())
     fprintf(stderr, "[dsa] topk_pools Q=%d pstride=%d select_k=%d threads=%d E=%d expand=%d\n", Q,
             pstride, select_k, nt, need, (int)EXPAND);
+  if (dsa::dry_run()) return DSA_OK;
 #define DSA_LAUNCH_TK(NT, E, S)                                                               \
   topk_kernel<NT, E, S, EXPAND><<<Q, NT, 0, stream>>>(scores, cand, row_len, pstride, select_k, \
                                                       sel, ex, TwoStage{})

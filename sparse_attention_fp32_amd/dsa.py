@@ -63,6 +63,8 @@ _SIGS = {
                                     _I, _P, _P, _P]),
     "dsa_topk_expand": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _I, _I, _I, _P, _P, _P]),
     "dsa_select_tail": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
+    "dsa_decode_step_args_size": (_Z, []),
+    "dsa_decode_step": (_I, [_P, _P]),
 }
 
 
@@ -301,6 +303,123 @@ def dsa_gate_compress(hidden, W, gate_part, k, gate, ape, valid, tok_off, pool_o
         kpool, max_cap, _dev(new_from, _I32, "new_from", allow_none=True), int(max_new),
         _dev(keys, _BF, "keys"), _dev(pool_start, _I32, "pool_start"),
         _dev(pool_valid, _U8, "pool_valid"), _dev(n_pools, _I32, "n_pools"), _stream(stream)))
+
+
+class DecodeStepArgs(ctypes.Structure):
+    """The C struct dsa_decode_step_args (include/dsa.h), field for field;
+    ctypes lays it out by the same C rules, and dsa_decode_step_args_size()
+    checks that it did."""
+    _fields_ = [
+        ("struct_bytes", _Z),
+        ("hidden", _P), ("W", _P), ("M", _I), ("K", _I), ("H", _I),
+        ("gate_part", _P), ("gate_part_bytes", _Z),
+        ("k", _P), ("gate", _P), ("ape", _P), ("valid", _P), ("tok_off", _P), ("pool_off", _P),
+        ("seq_len", _P), ("ln_w", _P), ("ln_b", _P), ("eps", _F),
+        ("B", _I), ("D", _I), ("kpool", _I), ("max_cap", _I),
+        ("new_from", _P), ("max_new", _I),
+        ("keys", _P), ("pool_start", _P), ("pool_valid", _P), ("n_pools", _P),
+        ("qi", _P), ("w", _P), ("q_req", _P), ("q_pos", _P), ("Q", _I), ("pstride", _I),
+        ("scores", _P), ("cand", _P),
+        ("row_len", _P), ("select_k", _I), ("out_width", _I), ("topk_flags", _I),
+        ("select_tail", _I), ("sel", _P), ("tok", _P),
+        ("q_mla", _P), ("ckv", _P), ("ckv_scale", _P), ("latent_dtype", _I), ("Hm", _I),
+        ("L", _I), ("sm_scale", _F), ("kv_off", _P), ("out", _P), ("lse", _P),
+        ("mla_ws", _P), ("mla_ws_bytes", _Z),
+        ("block_table", _P), ("bt_stride", _I), ("page_rows", _I), ("n_pages", _I),
+        ("kvidx", _P),
+    ]
+
+
+class DecodeStep:
+    """A filled dsa_decode_step_args and the tensors its pointers point into
+    (held here, so they outlive every call made with it)."""
+
+    def __init__(self, args: DecodeStepArgs, tensors: list):
+        self.args = args
+        self.tensors = tensors
+
+
+def decode_step_args(hidden, W, gate_part, k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b,
+                     eps: float, kpool: int, max_cap: int, keys, pool_start, pool_valid, n_pools,
+                     qi, w, q_req, q_pos, scores, cand, sel, tok, q_mla, ckv, ckv_scale,
+                     sm_scale: float, out, lse, mla_ws, kv_off=None, new_from=None,
+                     max_new: int = 0, seq_len=None, row_len=None, topk_flags: int = 0,
+                     select_tail: bool = False, block_table=None, page_rows: int = 0,
+                     kvidx=None) -> DecodeStep:
+    """Marshals the arguments of one dsa_decode_step: those of
+    dsa_gate_compress, dsa_index_scores_gated, dsa_topk_expand,
+    dsa_select_tail (when select_tail) and dsa_sparse_mla_decode (or its paged
+    form when block_table is given), checked as those wrappers check them."""
+    M, K = hidden.shape
+    Q, H, D = qi.shape
+    if W.shape[1] != H or k.shape[1] != D:
+        raise ValueError(f"head-gate width {W.shape[1]} / key width {k.shape[1]} differ from "
+                         f"qi's {H} heads of {D}")
+    if gate_part.dtype != torch.float32:
+        raise ValueError("gate_part must be float32")
+    Qm, Hm, L = q_mla.shape
+    if Qm != Q or scores.shape[0] != Q:
+        raise ValueError("q_mla, qi and scores must hold the same queries")
+    if row_len is not None and row_len.numel() < Q:
+        raise ValueError(f"row_len holds {row_len.numel()} entries, need {Q}")
+    fp8 = ckv.dtype in (torch.uint8, torch.float8_e4m3fn)
+    gp, gb = _ws(gate_part)
+    wp, wb = _ws(mla_ws)
+    a = DecodeStepArgs()
+    a.struct_bytes = ctypes.sizeof(DecodeStepArgs)
+    a.hidden, a.W = _dev(hidden, torch.float32, "hidden"), _dev(W, torch.float32, "W")
+    a.M, a.K, a.H = M, K, H
+    a.gate_part, a.gate_part_bytes = gp, gb
+    a.k, a.gate, a.ape = _dev(k, _BF, "k"), _dev(gate, _BF, "gate"), _dev(ape, _BF, "ape")
+    a.valid = _dev(valid, _U8, "valid")
+    a.tok_off, a.pool_off = _dev(tok_off, _I32, "tok_off"), _dev(pool_off, _I32, "pool_off")
+    a.seq_len = _dev(seq_len, _I32, "seq_len", allow_none=True)
+    a.ln_w = _dev(ln_w, torch.float32, "ln_w", allow_none=True)
+    a.ln_b = _dev(ln_b, torch.float32, "ln_b", allow_none=True)
+    a.eps, a.B, a.D, a.kpool, a.max_cap = float(eps), tok_off.numel() - 1, D, kpool, max_cap
+    a.new_from, a.max_new = _dev(new_from, _I32, "new_from", allow_none=True), int(max_new)
+    a.keys, a.pool_start = _dev(keys, _BF, "keys"), _dev(pool_start, _I32, "pool_start")
+    a.pool_valid, a.n_pools = _dev(pool_valid, _U8, "pool_valid"), _dev(n_pools, _I32, "n_pools")
+    a.qi, a.w = _dev(qi, _BF, "qi"), _dev(w, torch.float32, "w", allow_none=True)
+    a.q_req, a.q_pos = _dev(q_req, _I32, "q_req"), _dev(q_pos, _I32, "q_pos")
+    a.Q, a.pstride = Q, scores.shape[1]
+    a.scores, a.cand = _dev(scores, torch.float32, "scores"), _dev(cand, _U8, "cand")
+    a.row_len = _dev(row_len, _I32, "row_len", allow_none=True)
+    a.select_k, a.out_width = sel.shape[1], tok.shape[1]
+    a.topk_flags, a.select_tail = int(topk_flags), int(bool(select_tail))
+    a.sel, a.tok = _dev(sel, _I32, "sel"), _dev(tok, _I32, "tok")
+    a.q_mla = _dev(q_mla, _BF, "q_mla")
+    a.ckv = _dev(ckv, (torch.uint8, torch.float8_e4m3fn) if fp8 else _BF, "ckv")
+    a.ckv_scale = _dev(ckv_scale, torch.float32, "ckv_scale", allow_none=not fp8)
+    a.latent_dtype = LATENT_FP8_E4M3 if fp8 else LATENT_BF16
+    a.Hm, a.L, a.sm_scale = Hm, L, float(sm_scale)
+    a.out, a.lse = _dev(out, _BF, "out"), _dev(lse, torch.float32, "lse", allow_none=True)
+    a.mla_ws, a.mla_ws_bytes = wp, wb
+    if block_table is None:
+        a.kv_off = _dev(kv_off, _I32, "kv_off")
+        a.block_table = _P(None)
+    else:
+        if page_rows < 1 or ckv.shape[0] % page_rows:
+            raise ValueError(f"cache of {ckv.shape[0]} rows is not a whole number of "
+                             f"{page_rows}-row pages")
+        if fp8 and (ckv_scale is None or ckv_scale.numel() < ckv.shape[0]):
+            raise ValueError("fp8 cache needs one scale per cache row")
+        a.kv_off = _dev(kv_off, _I32, "kv_off", allow_none=True)
+        a.block_table = _dev(block_table, _I32, "block_table")
+        a.bt_stride, a.page_rows = block_table.shape[1], int(page_rows)
+        a.n_pages = ckv.shape[0] // page_rows
+        a.kvidx = _dev(kvidx, _I32, "kvidx", allow_none=True)
+    keep = [t for t in (hidden, W, gate_part, k, gate, ape, valid, tok_off, pool_off, ln_w, ln_b,
+                        keys, pool_start, pool_valid, n_pools, qi, w, q_req, q_pos, scores, cand,
+                        sel, tok, q_mla, ckv, ckv_scale, out, lse, mla_ws, kv_off, new_from,
+                        seq_len, row_len, block_table, kvidx) if t is not None]
+    return DecodeStep(a, keep)
+
+
+def dsa_decode_step(step: DecodeStep, stream=None) -> None:
+    """One decode step (include/dsa.h, dsa_decode_step) from arguments that
+    decode_step_args marshalled."""
+    _check(lib().dsa_decode_step(ctypes.byref(step.args), _stream(stream)))
 
 
 # --- the cache-write side --------------------------------------------------

@@ -143,6 +143,32 @@ class DsaStep:
         else:
             self.mla_paged(paged)
 
+    # -- the whole fused step from one host call -------------------------------
+    def step_args(self, incremental: bool = False, paged=None, kvidx: bool = False):
+        """The arguments of dsa_decode_step for this set: the fused calls of
+        run_fused (with the tail when the shape asks for it), marshalled once;
+        pass the result to run_step."""
+        x, s = self.x, self.spec
+        lw, lb = (x.ln_w, x.ln_b) if self.post_ln else (None, None)
+        if kvidx and getattr(self, "kvidx", None) is None:
+            self.kvidx = torch.empty(s.Q, s.out_width, dtype=torch.int32, device=x.k.device)
+        return dsa.decode_step_args(
+            x.hidden, x.W, self.gate_part, x.k, x.gate, x.ape, x.valid, x.tok_off, x.pool_off,
+            lw, lb, s.eps, s.kpool, self.max_cap, self.keys, self.pool_start, self.pool_valid,
+            self.n_pools, x.qi, self.w, x.q_req, x.q_pos, self.scores, self.cand, self.sel,
+            self.tok, x.q_mla, x.ckv if paged is None else paged.ckv,
+            x.ckv_scale if paged is None else paged.ckv_scale, s.sm_scale, self.out, self.lse,
+            self.ws_mla, kv_off=x.kv_off, new_from=x.new_from if incremental else None,
+            max_new=1 if incremental else 0, seq_len=self.seq_len,
+            select_tail=s.always_select_tail,
+            block_table=None if paged is None else paged.block_table,
+            page_rows=0 if paged is None else paged.page_rows,
+            kvidx=self.kvidx if kvidx else None)
+
+    def run_step(self, args):
+        """One dsa_decode_step call with arguments from step_args."""
+        dsa.dsa_decode_step(args, stream=self.stream)
+
     # -- the cache-write side of a decode step --------------------------------
     def write_geom(self, paged=None, slot=None):
         """q_req, q_pos and new_from of the inputs (one query per request)

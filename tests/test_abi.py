@@ -22,14 +22,14 @@ def _misaligned(code):
 
 def test_exports_every_declared_function():
     names = dsa.header_functions()
-    assert len(names) == 23
+    assert len(names) == 25
     import subprocess
     out = subprocess.run(["nm", "-D", "--defined-only", dsa.LIB_PATH], capture_output=True, text=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
     for n in names:
         assert n in exported, n
         getattr(dsa.lib(), n)
-    assert dsa.abi_version() == 3
+    assert dsa.abi_version() == 4
 
 
 def _code(fn, *args):
@@ -285,3 +285,60 @@ def test_mla_noalloc_errors():
     assert f(FAKE, FAKE, NUL, 0, FAKE, FAKE, FAKE, 4, 0, 512, 2048, 1.0, FAKE, NUL, NUL) == INV
     assert f(FAKE, FAKE, NUL, 1, FAKE, FAKE, FAKE, 4, 64, 512, 2048, 1.0, FAKE, NUL, NUL) == INV
     assert f(FAKE, FAKE, NUL, 0, FAKE, FAKE, FAKE, 0, 64, 512, 2048, 1.0, FAKE, NUL, NUL) == dsa.DSA_OK
+
+
+def _step_args(**kw):
+    """A dsa_decode_step_args for the 32K decode shape (16 queries, 8192 pools
+    per row, 64 attention heads) with fake device pointers; fields in kw
+    override."""
+    a = dsa.DecodeStepArgs()
+    a.struct_bytes = dsa.lib().dsa_decode_step_args_size()
+    Q, K, H, D, kpool = 16, 4096, 16, 128, 4
+    ns = dsa.gate_split_count(Q, K, H)
+    for name, kind in dsa.DecodeStepArgs._fields_:
+        if kind is ctypes.c_void_p:
+            setattr(a, name, FAKE)
+    a.M, a.K, a.H = Q, K, H
+    a.gate_part_bytes = dsa.gate_compress_workspace_size(Q, K, H)
+    a.seq_len = a.row_len = a.kvidx = a.block_table = NUL
+    a.eps, a.B, a.D, a.kpool, a.max_cap, a.max_new = 1e-5, 16, D, kpool, 8192, 1
+    a.Q, a.pstride, a.select_k, a.out_width = Q, 8192, 512, 2048
+    a.ckv_scale = NUL
+    a.latent_dtype, a.Hm, a.L, a.sm_scale = dsa.LATENT_BF16, 64, 512, 0.04
+    a.mla_ws_bytes = dsa.sparse_mla_decode_workspace_size(Q, 64, 512, 2048, 0)
+    assert ns > 1 and a.gate_part_bytes > 0 and a.mla_ws_bytes > 0
+    for k_, v in kw.items():
+        setattr(a, k_, v)
+    return a
+
+
+def _step(a):
+    return dsa.lib().dsa_decode_step(ctypes.byref(a) if a is not None else NUL, NUL)
+
+
+def test_decode_step_errors():
+    """The step executor checks the arguments of every call it makes before it
+    launches any: a bad argument of its last call (the attention) is reported
+    as that call's error, not as a failed launch of its first call (the
+    arguments of the first calls here are valid, and this host has no GPU)."""
+    assert ctypes.sizeof(dsa.DecodeStepArgs) == dsa.lib().dsa_decode_step_args_size()
+    assert _step(None) == INV
+    assert _step(_step_args(struct_bytes=8)) == INV
+    assert "struct_bytes" in dsa.last_error()
+    assert _step(_step_args(M=8)) == INV                       # the gate's rows are the queries
+    assert _step(_step_args(kpool=9)) == INV                   # the compression's validate()
+    assert "kpool=9" in dsa.last_error()
+    assert _step(_step_args(gate_part_bytes=4)) == INV
+    assert _step(_step_args(qi=MIS)) == INV                    # the gated scores
+    assert "dsa_index_scores_gated" in dsa.last_error()
+    assert _step(_step_args(select_k=0)) == INV                # top-k + expansion
+    assert "dsa_topk_expand" in dsa.last_error()
+    assert _step(_step_args(select_tail=1, out_width=2048)) == INV   # no room for the tail slots
+    assert "dsa_select_tail" in dsa.last_error()
+    assert _step(_step_args(L=576)) == UNS                     # the attention, last
+    assert "dsa_sparse_mla_decode" in dsa.last_error()
+    assert _step(_step_args(mla_ws_bytes=16)) == INV
+    assert _step(_step_args(latent_dtype=dsa.LATENT_FP8_E4M3)) == INV   # fp8 without row scales
+    # the paged attention when a block table is given
+    assert _step(_step_args(block_table=FAKE, bt_stride=0, page_rows=64, n_pages=8)) == INV
+    assert "dsa_sparse_mla_decode_paged" in dsa.last_error()
