@@ -91,6 +91,30 @@ def test_step_equals_fused_calls(case):
     _say(f"decode step executor {spec.name}: equal to the calls, boundary swaps {nd}")
 
 
+@pytest.mark.parametrize("post_ln", (True, False))
+def test_step_live_lengths(post_ln):
+    """Live lengths inside the requests' regions (seq_len) and rows stored
+    normalised (post_ln False): the executor passes both to the compression."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_attention_fp32_amd.pipeline import DsaStep
+    spec = W.spec_by_name("medium_live")
+    _say(f"decode step executor live lengths post_ln={post_ln}")
+    xg = W.make_inputs(spec, seed=5).to("cuda")
+    st = DsaStep(xg)
+    st.seq_len = torch.tensor(spec.live_lengths(), dtype=torch.int32, device="cuda")
+    st.post_ln = post_ln
+    for incremental in (False, True):
+        names = STEP_OUTS if incremental else OUTS
+        args = st.step_args(incremental=incremental)
+        _poison(st, names)
+        _fused(st, incremental, None)
+        a = _snap(st)
+        _poison(st, names)
+        st.run_step(args)
+        _same(a, _snap(st), f"live step incremental={incremental}")
+
+
 @pytest.mark.parametrize("page_rows", (7, 64))
 def test_step_paged_equals_fused_calls(case, page_rows):
     spec, xn, ref, xg = case
