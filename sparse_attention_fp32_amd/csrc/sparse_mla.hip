@@ -498,6 +498,9 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_kernel(
 // head, 8 dims per lane, four heads per workgroup.  All chunks' loads of a
 // batch are issued before any is used; the batch is the smallest of 4, 8, 16
 // that holds every chunk (up to 16), so no load repeats a chunk needlessly.
+// The partials are read, and the output written, non-temporally (each is
+// touched once here; measured about a microsecond faster per decode step than
+// plain accesses).
 template <int kBatch>
 __global__ __launch_bounds__(256) void mla_combine_kernel(const uint16_t* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
@@ -518,7 +521,8 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const uint16_t* __rest
     for (int k = 0; k < kBatch; ++k) {
       const int c = min(c0 + k, nchunks - 1);
       const int64_t pc = b0 + (int64_t)c * Hm;
-      v[k] = *(const uint4*)(part_o + pc * L + lane * 8);
+      v[k] = __builtin_bit_cast(
+          uint4, __builtin_nontemporal_load((const u32x4_t*)(part_o + pc * L + lane * 8)));
       ml[k] = *(const float2*)(part_ml + pc * 2);
     }
     float Mb = M;
@@ -546,7 +550,8 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const uint16_t* __rest
   uint32_t pk[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) pk[k] = pack_bf16x2(acc[2 * k] * inv, acc[2 * k + 1] * inv);
-  *(uint4*)(out + ((int64_t)qx * Hm + h) * L + lane * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  const u32x4_t ov = {pk[0], pk[1], pk[2], pk[3]};
+  __builtin_nontemporal_store(ov, (u32x4_t*)(out + ((int64_t)qx * Hm + h) * L + lane * 8));
   if (lse && lane == 0)
     lse[(int64_t)qx * Hm + h] = lsum > 0.f ? (M + log2f(lsum)) * kLn2 : -INFINITY;
 }
