@@ -515,15 +515,23 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const uint16_t* __rest
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
   for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+    // lane k holds the (max, sum) pair of chunk c0 + k; the wave reads them
+    // back one by one (one load per lane instead of one per chunk)
+    const int cl = min(c0 + (lane & (kBatch - 1)), nchunks - 1);
+    const float2 mlv = *(const float2*)(part_ml + (b0 + (int64_t)cl * Hm) * 2);
     uint4 v[kBatch];
-    float2 ml[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int c = min(c0 + k, nchunks - 1);
       const int64_t pc = b0 + (int64_t)c * Hm;
       v[k] = __builtin_bit_cast(
           uint4, __builtin_nontemporal_load((const u32x4_t*)(part_o + pc * L + lane * 8)));
-      ml[k] = *(const float2*)(part_ml + pc * 2);
+    }
+    float2 ml[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      ml[k].x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv.x), k));
+      ml[k].y = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv.y), k));
     }
     float Mb = M;
 #pragma unroll

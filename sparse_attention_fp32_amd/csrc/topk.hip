@@ -241,13 +241,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     const int incl = wave_incl_scan(sum);
     if (lane == 63) s_wsum[wv] = incl;
     __syncthreads();
-    int above = incl - sum, total = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const int x = s_wsum[w];
-      total += x;
-      above += w < wv ? x : 0;
-    }
+    // the waves' totals in one read: lane w holds wave w's, and their
+    // inclusive scan gives the row's total and this wave's exclusive prefix
+    const int wx = wave_incl_scan(lane < kWaves ? s_wsum[lane] : 0);
+    const int total = __builtin_amdgcn_readlane(wx, kWaves - 1);
+    int above = incl - sum + (wv > 0 ? __builtin_amdgcn_readlane(wx, wv > 0 ? wv - 1 : 0) : 0);
     if (level == 0) {
       k_eff = min(select_k, total);  // total: the row's candidates
       need = k_eff;
@@ -302,39 +300,47 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     } else {
       bool gt[E], eq[E];
       uint64_t beq[E];
+      int qc = 0;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         gt[e] = key[e] != 0u && key[e] > prefix;  // mask is all ones here
         eq[e] = key[e] != 0u && key[e] == prefix;
         beq[e] = ballot(eq[e]);
-        if (lane == 0) s_ecnt[e * kWaves + wv] = __popcll(beq[e]);
+        qc = lane == e ? (int)__popcll(beq[e]) : qc;
       }
+      if (lane < E) s_ecnt[lane * kWaves + wv] = qc;
       __syncthreads();
       if (wv == 0) {
         const int n = wave0_offsets<E, kWaves>(s_ecnt, s_eoff, lane, s_run[1]);
         if (lane == 0) s_run[1] += n;  // (wave 0 alone reads and writes s_run)
       }
       __syncthreads();
+      const int qo = lane < E ? s_eoff[lane * kWaves + wv] : 0;
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        keep[e] = gt[e] || (eq[e] && s_eoff[e * kWaves + wv] + lanes_below(beq[e]) < need);
+        keep[e] = gt[e] || (eq[e] && __builtin_amdgcn_readlane(qo, e) + lanes_below(beq[e]) < need);
       __syncthreads();  // s_ecnt / s_eoff are reused below
     }
+    // the wave's E counts go out in one store (lane e holds count e), and
+    // their offsets come back in one read
     uint64_t bk[E];
+    int kc = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       bk[e] = ballot(keep[e]);
-      if (lane == 0) s_ecnt[e * kWaves + wv] = __popcll(bk[e]);
+      kc = lane == e ? (int)__popcll(bk[e]) : kc;
     }
+    if (lane < E) s_ecnt[lane * kWaves + wv] = kc;
     __syncthreads();
     if (wv == 0) {
       const int n = wave0_offsets<E, kWaves>(s_ecnt, s_eoff, lane, s_run[0]);
       if (lane == 0) s_run[0] += n;  // (read by wave 0 alone, before the next step's barrier)
     }
     __syncthreads();
+    const int ko = lane < E ? s_eoff[lane * kWaves + wv] : 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int pos = s_eoff[e * kWaves + wv] + lanes_below(bk[e]);
+      const int pos = __builtin_amdgcn_readlane(ko, e) + lanes_below(bk[e]);
       const int id = MODE == 2 ? cid[e] : id0 + s * kStep + t + NT * e;
       if (keep[e] && pos < k_eff) {
         if (staged) {
@@ -358,7 +364,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     if (EXPAND) {
       const int kp = ex.kpool;
       for (int i = t; i < ex.out_width; i += NT) {
-        const int j = i / kp;
+        const int j = kp == 4 ? i >> 2 : i / kp;
         trow[i] = j < k_eff ? s_kps[j] + (i - j * kp) : -1;
       }
     }
