@@ -193,9 +193,11 @@ dsa_status dsa_index_scores(const uint16_t* qi, const float* w, const uint16_t* 
  * workgroup selects among those candidates; this needs at most 16384
  * candidates per row (blocks x select_k).  Otherwise (ws NULL or smaller, or
  * too many candidates) the row is read again from memory on each pass of a
- * one-workgroup select.  Both give the same result.
- * Workspace: Q x candidates x 4 bytes for rows longer than 16384 entries
- * (0 otherwise); ws may be NULL.
+ * one-workgroup select.  A row of 4096 to 16384 entries with
+ * 8 * select_k <= 2048 takes the two stages too, in 2048-entry blocks, when
+ * ws is large enough (else one pass).  All give the same result.
+ * Workspace: Q x candidates x 4 bytes for rows that take two stages (0
+ * otherwise); ws may be NULL.
  * Errors: INVALID_ARG for select_k < 1, pstride < 1, Q < 0, NULL pointers.
  * ------------------------------------------------------------------------- */
 size_t dsa_topk_pools_workspace_size(int Q, int pstride, int select_k);
@@ -434,9 +436,10 @@ dsa_status dsa_gate_compress_live(const float* hidden, const float* W, int M, in
  * arrays offset alike).
  *
  * dsa_topk_expand: dsa_topk_pools followed by dsa_expand_selection on the same
- * rows (arguments as there; sel and tok both written in full).  A row longer
- * than 16384 entries whose first-stage candidates (blocks x select_k) fit its
- * tok row keeps them there between the two stages (no workspace).  Errors:
+ * rows (arguments as there; sel and tok both written in full).  A row that
+ * takes two stages (as there) and whose first-stage candidates (blocks x
+ * select_k) fit its tok row keeps them there between the stages (no
+ * workspace).  Errors:
  * the union of theirs.
  * ------------------------------------------------------------------------- */
 int dsa_gate_split_count(int M, int K, int N);

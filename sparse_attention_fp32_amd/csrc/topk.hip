@@ -7,7 +7,9 @@
 // selected in two launches when there is room for the candidates (each block
 // of the row keeps its own top-k, then one workgroup selects among them; see
 // TwoStage), else read again from memory (L2) on every pass instead of staying
-// in registers; there is no cap on the row length.
+// in registers; there is no cap on the row length.  A row that fits one step
+// but keeps at most an eighth of each 2048-pool block takes the two launches
+// as well (stage_blk).
 //
 // Scores become order-preserving integer keys (a finite float maps to a
 // nonzero unsigned key that sorts like the float; -0 like +0; non-candidates
@@ -376,12 +378,25 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 }
 
 constexpr int kBlk = 16384;  // stage-1 block: 1024 threads x 16 ids in registers
+constexpr int kBlkSmall = 2048;  // stage-1 block of rows that fit one pass: 2 ids per thread
 
-// Candidates per row of the two-stage select, or 0 where the row fits one
-// pass in registers or the candidates would not fit stage 2's registers.
+// Stage-1 block length of the two-stage select, or 0 for one pass.  Rows past
+// one register pass always take it; a row that fits one pass takes it in
+// 2048-pool blocks when each block keeps at most an eighth of its pools (the
+// second launch then costs less than the first pass saves: measured on
+// 16384-pool rows keeping 256; a block keeping a quarter was slower).
+int stage_blk(int pstride, int select_k) {
+  if (pstride > kBlk) return kBlk;
+  if (pstride >= 2 * kBlkSmall && 8LL * select_k <= kBlkSmall) return kBlkSmall;
+  return 0;
+}
+
+// Candidates per row of the two-stage select, or 0 where the row takes one
+// pass or the candidates would not fit stage 2's registers.
 long long two_stage_cands(int pstride, int select_k) {
-  if (pstride <= kBlk) return 0;
-  const long long nblk = (pstride + kBlk - 1) / kBlk;
+  const int blk = stage_blk(pstride, select_k);
+  if (blk == 0) return 0;
+  const long long nblk = (pstride + blk - 1) / blk;
   const long long n = nblk * select_k;
   return n <= kBlk ? n : 0;
 }
@@ -394,16 +409,21 @@ dsa_status launch_topk(const float* scores, const uint8_t* cand, const int32_t* 
   const long long ncand = two_stage_cands(pstride, select_k);
   if (ncand > 0 && cbuf && ncand <= cstride) {
     // long row in two stages: the blocks' own top-k, then one select over them
-    const int nblk = (pstride + kBlk - 1) / kBlk;
+    const int blk = stage_blk(pstride, select_k);
+    const int nblk = (pstride + blk - 1) / blk;
     DSA_REQUIRE(nblk <= 65535, DSA_ERR_UNSUPPORTED, "%s: pstride=%d in %d blocks", who, pstride,
                 nblk);
     if (dsa::trace_enabled())
       fprintf(stderr, "[dsa] topk two-stage Q=%d pstride=%d select_k=%d blocks=%d cands=%lld\n",
               Q, pstride, select_k, nblk, ncand);
-    const TwoStage ts{cbuf, cstride, kBlk, (int)ncand};
+    const TwoStage ts{cbuf, cstride, blk, (int)ncand};
     if (dsa::dry_run()) return DSA_OK;
-    topk_kernel<1024, 16, false, false, 1><<<dim3(Q, nblk), 1024, 0, stream>>>(
-        scores, cand, row_len, pstride, select_k, sel, ExpandArgs{}, ts);
+    if (blk == kBlk)
+      topk_kernel<1024, 16, false, false, 1><<<dim3(Q, nblk), 1024, 0, stream>>>(
+          scores, cand, row_len, pstride, select_k, sel, ExpandArgs{}, ts);
+    else
+      topk_kernel<1024, kBlkSmall / 1024, false, false, 1><<<dim3(Q, nblk), 1024, 0, stream>>>(
+          scores, cand, row_len, pstride, select_k, sel, ExpandArgs{}, ts);
     dsa_status st = dsa::check_launch(who);
     if (st != DSA_OK) return st;
     const int need = (int)((ncand + 1023) / 1024);

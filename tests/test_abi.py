@@ -106,6 +106,13 @@ def test_topk_errors():
     # rows past one pass in registers: room for each row's first-stage candidates
     assert dsa.topk_pools_workspace_size(2, 65536, 512) == 2 * 4 * 512 * 4
     assert dsa.topk_pools_workspace_size(2, 65536, 8192) == 0   # candidates past stage 2's reach
+    # rows of one pass that keep at most an eighth of each 2048-pool block:
+    # two stages in 2048-pool blocks (ceil(P / 2048) blocks of k candidates)
+    assert dsa.topk_pools_workspace_size(4, 16384, 256) == 4 * 8 * 256 * 4
+    assert dsa.topk_pools_workspace_size(4, 4096, 256) == 4 * 2 * 256 * 4
+    assert dsa.topk_pools_workspace_size(3, 6000, 200) == 3 * 3 * 200 * 4
+    assert dsa.topk_pools_workspace_size(4, 4095, 256) == 0     # below 4096 pools
+    assert dsa.topk_pools_workspace_size(4, 8192, 257) == 0     # a block keeps more than 1/8
 
 
 def test_expand_errors():

@@ -45,6 +45,9 @@ CASES += [(P, k, kind) for P in (16385, 32768, 65536) for k in (1, 512)
           for kind in ("normal", "ties", "wide")]
 CASES += [(65536, 512, "equal"), (65536, 512, "negative"), (40000, 100, "zeros"),
           (65536, 2048, "normal"), (65536, 4000, "ties"), (32768, 20000, "wide")]
+# rows of one pass that take two stages in 2048-pool blocks (the fused call
+# keeps the candidates in its token row when they fit)
+CASES += [(6000, 200, "wide"), (16384, 256, "ties"), (12289, 255, "zeros")]
 
 
 def _seed(*parts):
@@ -107,8 +110,10 @@ def _exact_pools(P, k, kind, with_ws):
     ws = None
     if with_ws:
         n = dsa.topk_pools_workspace_size(Q, P, k)
-        assert n > 0
-        ws = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")
+        blk = 16384 if P > 16384 else (2048 if P >= 4096 and 8 * k <= 2048 else 0)
+        assert (n > 0) == (blk > 0 and -(-P // blk) * k <= 16384), n
+        if n:
+            ws = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")
     dsa.dsa_topk_pools(sg, cg, out, ws=ws)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), ref)
@@ -123,12 +128,22 @@ def test_topk_exact(P, k, kind):
 
 # long rows whose first-stage candidates fit stage 2 (blocks x k <= 16384)
 TWO_STAGE_CASES = [c for c in CASES if c[0] > 16384 and -(-c[0] // 16384) * c[1] <= 16384]
+# rows of one register pass that keep at most an eighth of each 2048-pool block
+# take two stages in 2048-pool blocks: exact cases at and past the thresholds
+# (4096 pools, 8 * k == 2048), a ragged last block, and rows just outside the
+# rule (one pass)
+SMALL_BLOCK_CASES = [c for c in CASES if 4096 <= c[0] <= 16384 and 8 * c[1] <= 2048]
+SMALL_BLOCK_CASES += [(4096, 256, "ties"), (4095, 256, "normal"), (6000, 200, "wide"),
+                      (16384, 256, "equal"), (16384, 256, "ties"), (12289, 255, "zeros"),
+                      (8192, 257, "normal")]
+TWO_STAGE_CASES += SMALL_BLOCK_CASES
 
 
 @pytest.mark.parametrize("P,k,kind", TWO_STAGE_CASES)
 def test_topk_exact_two_stage(P, k, kind):
     """dsa_topk_pools with its workspace: rows longer than one pass in
-    registers take the two-stage select."""
+    registers, and rows that keep at most an eighth of each 2048-pool block,
+    take the two-stage select."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     _exact_pools(P, k, kind, with_ws=True)
