@@ -113,9 +113,15 @@ CALL_KERNELS = {
     "sparse_mla_decode": (r"sparse_mla_kernel<(true|false), false, (true|false)>",
                           r"mla_combine_kernel"),
     "index_scores_gated": (r"index_scores(_qblock)?_kernel<\d+, true",),
-    "topk_expand": (r"topk_kernel<\d+, \d+, (true|false), true(, 0)?>",),
+    # (a row selected in two stages runs the stage-1 kernel, shared by both
+    # top-k calls, then the call's stage-2 kernel)
+    "topk_expand": (r"topk_kernel<\d+, \d+, (true|false), true(, 0)?>",
+                    r"topk_kernel<\d+, \d+, false, false, 1>",
+                    r"topk_kernel<\d+, \d+, false, true, 2>"),
     "index_scores": (r"index_scores(_qblock)?_kernel<\d+, false",),
-    "topk_pools": (r"topk_kernel<\d+, \d+, (true|false), false(, 0)?>",),
+    "topk_pools": (r"topk_kernel<\d+, \d+, (true|false), false(, 0)?>",
+                   r"topk_kernel<\d+, \d+, false, false, 1>",
+                   r"topk_kernel<\d+, \d+, false, false, 2>"),
 }
 
 
