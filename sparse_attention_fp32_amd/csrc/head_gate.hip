@@ -161,8 +161,11 @@ constexpr int kGateWaves = 16;  // waves over K per workgroup (MFMA path)
 // A[l % 16][l / 16] = hidden[m0 + l % 16][k], B[l / 16][l % 16] = W[k][l % 16],
 // and D[4 (l / 16) + r][l % 16] in acc[r].  A float4 of a hidden row feeds four
 // MFMAs: for c < 4 the K index of lane group j is k0 + 4 j + c.  Wave wv takes
-// the 16-wide K steps [s0, s1).
-template <int U>  // K steps per loop pass, all loads of a pass in flight
+// the 16-wide K steps [s0, s1) in passes of U steps, two register sets in
+// turn: the loads of the next pass are issued before the MFMAs of the current
+// one, so the MFMAs run while the next rows stream in.  The MFMAs still take
+// the steps in ascending order.
+template <int U>  // K steps per pass
 __global__ __launch_bounds__(kGateWaves * 64) void head_gate_mfma_kernel(
     const float* __restrict__ hidden, const float* __restrict__ W, float* __restrict__ w, int M,
     int K, int N) {
@@ -176,17 +179,17 @@ __global__ __launch_bounds__(kGateWaves * 64) void head_gate_mfma_kernel(
   const int ncol = i < N ? i : N - 1;
   const float bmask = i < N ? 1.f : 0.f;
   f32x4_v acc = {0.f, 0.f, 0.f, 0.f};
-  for (int sb = s0; sb < s1; sb += U) {
-    float4 h[U];
-    float b[U][4];
+  // (steps past s1 are loaded, clamped to s1 - 1, and not used)
+  auto load = [&](float4 (&h)[U], float (&b)[U][4], int sb) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int st = min(sb + u, s1 - 1);  // (steps past s1 are loaded and not used)
-      const int k0 = st * 16;
+      const int k0 = min(sb + u, s1 - 1) * 16;
       h[u] = *(const float4*)(hrow + k0 + 4 * j);
 #pragma unroll
       for (int c = 0; c < 4; ++c) b[u][c] = W[(size_t)(k0 + 4 * j + c) * N + ncol];
     }
+  };
+  auto mma = [&](const float4 (&h)[U], const float (&b)[U][4], int sb) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (sb + u < s1) {
@@ -196,6 +199,16 @@ __global__ __launch_bounds__(kGateWaves * 64) void head_gate_mfma_kernel(
           acc = __builtin_amdgcn_mfma_f32_16x16x4f32(hv[c], b[u][c] * bmask, acc, 0, 0, 0);
       }
     }
+  };
+  float4 ha[U], hb[U];
+  float ba[U][4], bb[U][4];
+  if (s0 < s1) load(ha, ba, s0);
+  for (int sb = s0; sb < s1; sb += 2 * U) {
+    if (sb + U < s1) load(hb, bb, sb + U);
+    mma(ha, ba, sb);
+    if (sb + U >= s1) break;
+    if (sb + 2 * U < s1) load(ha, ba, sb + 2 * U);
+    mma(hb, bb, sb + U);
   }
   s_red[wv][lane] = acc;
   __syncthreads();
@@ -239,7 +252,7 @@ DSA_EXPORT dsa_status dsa_head_gate(const float* hidden, const float* W, float* 
     else
       head_gate_row_kernel<false><<<M, kRowThreads, 0, stream>>>(hidden, W, w, K, N);
   else if (K % 16 == 0)
-    head_gate_mfma_kernel<8><<<(M + kRows - 1) / kRows, kGateWaves * 64, 0, stream>>>(hidden, W, w,
+    head_gate_mfma_kernel<4><<<(M + kRows - 1) / kRows, kGateWaves * 64, 0, stream>>>(hidden, W, w,
                                                                                    M, K, N);
   else
     head_gate_rows_kernel<<<(M + kRows - 1) / kRows, 256, 0, stream>>>(hidden, W, w, M, K, N);
