@@ -37,6 +37,14 @@ def case(request):
     return spec, xn, ref, x.to("cuda")
 
 
+# shapes a case applies to (the case fixture is parametrized over them
+# directly, so no case is collected where it cannot run)
+TAIL_SHAPES = [n for n in W.PARITY_SHAPES if W.spec_by_name(n).always_select_tail]
+MULTI_QUERY_SHAPES = [n for n in W.PARITY_SHAPES if W.spec_by_name(n).Q >= 2]
+SUBRANGE_Q0 = 4
+SUBRANGE_SHAPES = [n for n in W.PARITY_SHAPES if W.spec_by_name(n).Q > SUBRANGE_Q0]
+
+
 def _step(xg):
     from sparse_attention_fp32_amd.pipeline import DsaStep
     return DsaStep(xg)
@@ -257,12 +265,11 @@ def test_expand_isolated(case):
     assert np.array_equal(_np(st.tok), ref["tok"])
 
 
+@pytest.mark.parametrize("case", TAIL_SHAPES, indirect=True)
 def test_select_tail_isolated(case):
     """The tail alone, on the oracle's expansion without it."""
     from sparse_attention_fp32_amd import dsa
     spec, xn, ref, xg = case
-    if not spec.always_select_tail:
-        pytest.skip("shape without always_select_tail")
     _say(f"select_tail {spec.name}")
     st = _step(xg)
     _load_oracle_front(st, ref)
@@ -326,12 +333,11 @@ def test_chain(case):
     _say(f"chain {spec.name}: boundary swaps {nd}")
 
 
+@pytest.mark.parametrize("case", MULTI_QUERY_SHAPES, indirect=True)
 def test_determinism_and_duplicate_rows(case):
     spec, xn, ref, xg = case
     _say(f"determinism {spec.name}")
     # make query 1 an exact copy of query 0 (same request, position, vectors)
-    if spec.Q < 2:
-        pytest.skip("needs two queries")
     d = dict(xg.__dict__)
     for name in ("hidden", "qi", "q_mla", "q_req", "q_pos"):
         t = d[name].clone()
@@ -421,14 +427,13 @@ def test_gated_scores_slice_counts(case, ns):
     PT.check_scores(_np(st.scores), _np(st.cand), ref["scores"], ref["cand"])
 
 
+@pytest.mark.parametrize("case", SUBRANGE_SHAPES, indirect=True)
 def test_gated_scores_query_subrange(case):
     """The gated scores on a run of queries q0.. of the batch (the per-query
     arrays, the query-major head-gate partials among them, passed from q0 on)
     give those queries' rows of the whole call."""
     spec, xn, ref, xg = case
-    q0 = 4
-    if spec.Q <= q0:
-        pytest.skip("needs more than four queries")
+    q0 = SUBRANGE_Q0
     _say(f"index_scores_gated {spec.name} on queries {q0}..{spec.Q - 1}")
     from sparse_attention_fp32_amd import dsa
     st = _step(xg)
