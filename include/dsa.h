@@ -77,12 +77,13 @@ const char* dsa_last_error(void);
  *   w[m, n] = sum_k hidden[m, k] * W[k, n]        (fp32 in, fp32 accumulate)
  *
  * hidden [M, K] f32, W [K, N] f32, w [M, N] f32.  1 <= N <= 16, K >= 1,
- * M >= 0 (M = 0 is a no-op).  For M <= 16 (decode) every row gets its own
- * workgroup that spreads K over 1024 threads and adds the partial sums in a
- * fixed order, so the result is deterministic and the same bits for a row
- * whatever the batch.  For M > 16 one workgroup per 16 rows splits K over
- * 16 waves (fp32 MFMA when K % 16 == 0) and adds the waves' partial sums in
- * a fixed order, so those rows are deterministic too.  No
+ * M >= 0 (M = 0 is a no-op).  For M <= 512 (decode, and small batches)
+ * every row gets its own workgroup that spreads K over 1024 threads and adds
+ * the partial sums in a fixed order, so the result is deterministic and the
+ * same bits for a row whatever the batch (up to 512 rows).  For M > 512 one
+ * workgroup per 16 rows splits K over 16 waves (fp32 MFMA when K % 16 == 0)
+ * and adds the waves' partial sums in a fixed order, so those rows are
+ * deterministic too.  No
  * workspace is needed at present (dsa_head_gate_workspace_size returns 0; ws
  * may be NULL).
  * Errors: INVALID_ARG for N outside [1,16], K < 1, M < 0, or a NULL or

@@ -3,14 +3,14 @@
 // The product of stkernel PR #227 ("indexer fp32 head-gate split-K").  At
 // decode (M <= 16) a plain GEMM leaves almost every compute unit idle and the
 // PR splits K over programs that add their partials with float atomics.  Here
-// each of the M rows gets a 1024-thread workgroup that issues all of its loads
-// at once (four 16-float rows of W and four hidden values per thread), keeps 16
+// each of the M rows (up to kRowMaxM of them) gets a 1024-thread workgroup
+// that issues all of its loads at once (four 16-float rows of W and four hidden values per thread), keeps 16
 // running sums per thread, and reduces them in a fixed order: a
 // reduce-scatter over the wave (17 ALU-latency lane exchanges leave lane l with
 // output j(l)),
 // then the 16 waves' sums added in wave order.  Deterministic, and the same
-// bits for a row whatever the batch.  Above 16 rows (prefill) each workgroup
-// owns 16 rows: a [16,K] x [K,16] product on fp32 MFMA (v_mfma_f32_16x16x4_f32,
+// bits for a row whatever the batch.  Above kRowMaxM rows (prefill) each
+// workgroup owns 16 rows: a [16,K] x [K,16] product on fp32 MFMA (v_mfma_f32_16x16x4_f32,
 // fp32 products and sums) with the 16 waves splitting K and their 16x16
 // partials added in wave order; K not a multiple of 16 takes a plain LDS-tiled
 // loop.
@@ -29,9 +29,15 @@ using namespace dsa;
 constexpr int kSlice = 128;  // K rows per LDS tile (rows path)
 constexpr int kRows = 16;    // output rows per workgroup (rows path)
 constexpr int kRowThreads = 1024;
+// Most rows taken one workgroup per row.  Each of those workgroups reads all
+// of W (from L2), so the per-row form stops paying once the rows' W reads
+// outweigh the 16-row MFMA form's single pass: measured per launch at K 4096,
+// N 16, per-row against MFMA form, 6.1 vs 11.6 us at 17 rows, 6.4 vs 12.6 at
+// 256, 10.3 vs 12.6 at 512, 17.4 vs 12.9 at 1024, 68 vs 15.8 at 4096.
+constexpr int kRowMaxM = 512;
 constexpr int kPerThread = 4;  // K elements per thread per pass (row path)
 
-// One workgroup per output row m (M <= 16).  Thread t takes k = t + 1024*i.
+// One workgroup per output row m (M <= kRowMaxM).  Thread t takes k = t + 1024*i.
 // N16: W rows are exactly 16 floats (four 16-byte loads per row).
 template <bool N16>
 __global__ __launch_bounds__(kRowThreads) void head_gate_row_kernel(const float* __restrict__ hidden,
@@ -120,7 +126,7 @@ __global__ __launch_bounds__(kRowThreads) void head_gate_row_kernel(const float*
   }
 }
 
-// 16 rows per workgroup, all of K through LDS tiles (M > 16).  Thread t owns
+// 16 rows per workgroup, all of K through LDS tiles (M > kRowMaxM).  Thread t owns
 // output (m = t / 16, n = t % 16).
 __global__ __launch_bounds__(256) void head_gate_rows_kernel(const float* __restrict__ hidden,
                                                              const float* __restrict__ W,
@@ -157,7 +163,7 @@ typedef float f32x4_v __attribute__((ext_vector_type(4)));
 
 constexpr int kGateWaves = 16;  // waves over K per workgroup (MFMA path)
 
-// 16 rows per workgroup (M > 16, K % 16 == 0).  MFMA 16x16x4 f32: lane l holds
+// 16 rows per workgroup (M > kRowMaxM, K % 16 == 0).  MFMA 16x16x4 f32: lane l holds
 // A[l % 16][l / 16] = hidden[m0 + l % 16][k], B[l / 16][l % 16] = W[k][l % 16],
 // and D[4 (l / 16) + r][l % 16] in acc[r].  A float4 of a hidden row feeds four
 // MFMAs: for c < 4 the K index of lane group j is k0 + 4 j + c.  Wave wv takes
@@ -246,7 +252,7 @@ DSA_EXPORT dsa_status dsa_head_gate(const float* hidden, const float* W, float* 
   DSA_REQUIRE_ALIGNED("dsa_head_gate", hidden, W, w, ws);
   if (dsa::trace_enabled()) fprintf(stderr, "[dsa] head_gate M=%d K=%d N=%d\n", M, K, N);
   if (dsa::dry_run()) return DSA_OK;
-  if (M <= kRows)
+  if (M <= kRowMaxM)
     if (N == 16)
       head_gate_row_kernel<true><<<M, kRowThreads, 0, stream>>>(hidden, W, w, K, N);
     else

@@ -80,8 +80,11 @@ def test_head_gate_repeat_keeps_workspace_clean(case):
 
 # (M, K, N): row path at its upper bound, MFMA path with ragged row tiles, waves
 # left without K steps, N < 16 and N = 1, and the LDS path (K % 16 != 0)
+# up to 512 rows one workgroup per row; above, 16 rows per workgroup on fp32
+# MFMA (K % 16 == 0) or the LDS-tiled loop
 GATE_SHAPES = [(16, 4096, 16), (17, 16, 16), (33, 48, 7), (100, 4096, 16), (63, 2064, 1),
-               (40, 1000, 16), (20, 4104, 5)]
+               (40, 1000, 16), (20, 4104, 5), (512, 4096, 16), (513, 2064, 16),
+               (600, 4096, 5), (530, 1000, 7), (1041, 48, 16)]
 
 
 @pytest.mark.parametrize("M,K,N", GATE_SHAPES)
