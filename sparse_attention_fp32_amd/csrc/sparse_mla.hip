@@ -62,7 +62,9 @@ constexpr int kSliceRow = kSlice * 2 + 16;  // LDS bytes per token row of a slic
 constexpr int kHT = 2;                    // 16-head tiles per workgroup
 constexpr int kHeadsWG = 16 * kHT;        // heads per workgroup
 constexpr int kTargetWG = 512;            // aim for two workgroups per CU
-constexpr int kMinSubPerChunk = 4;        // >= 128 ids per chunk keeps partials small
+// >= 64 ids per chunk: batches of few queries (one to four long-context
+// requests) get up to twice as many workgroups with half the chain each
+constexpr int kMinSubPerChunk = 2;
 constexpr int kMaxTch = 2048;             // most ids per chunk
 constexpr int kPF = 1;                    // sub-chunks of rows loading ahead of the one computed
 constexpr int kMaxBt = 2048;              // block-table entries staged in LDS
